@@ -1,0 +1,183 @@
+/*
+ * moe_mi355x.h -- C ABI of the MI355X routed-expert (MoE) layer library.
+ *
+ * One MoE layer call is four entry points enqueued on one HIP stream:
+ *
+ *   moe_route_topk   router logits -> top-k expert ids, gate weights, load histogram
+ *   moe_permute      ids -> per-expert route lists (offsets, sorted pairs, inverse)
+ *   moe_grouped_ffn  every expert's SwiGLU FFN over its route list
+ *   moe_combine      per-token gate-weighted sum of its k expert outputs
+ *
+ * What is computed, and where the pages say so:
+ *   - routed experts per MoE layer (384 in the served model) and per-token
+ *     routing: dsv41-flash-offload wiki, opening paragraph;
+ *   - per-expert route lists with positive counts, and splitting large lists
+ *     into batches that share one read of the expert's weights: wiki,
+ *     repository file table, entries for the staged cold-expert prefill and
+ *     segment patches;
+ *   - busy experts (at least the "fat threshold" of 32 tokens) as GEMMs on
+ *     reconstructed weights: wiki opening paragraph and file table (busy-expert
+ *     GEMM entry); threshold value 32: recipe page "DeepSeek-V4.1-Flash /
+ *     RTX 3090", step 3 environment block;
+ *   - split of routed work and combine of the results on the GPU: wiki file
+ *     table, CPU-tier entry;
+ *   - failing loudly instead of falling back silently, and keeping host work
+ *     out of graph-captured regions: "dsv41-flash-engram-disk-prestage",
+ *     section "The prestage, per decode step", point 4.
+ * The pages do not write down the gate function, the expert's form or the
+ * 3-bit format; the readings implemented are stated at each function.
+ *
+ * Conventions shared by every entry point
+ *   - Pointers are device pointers unless stated; the caller owns every
+ *     buffer (inputs, outputs and the workspace).  The library allocates no
+ *     device or host memory.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     All work is enqueued on it; no call synchronises the host with the
+ *     device, so every call may be captured into a HIP graph.
+ *   - Outputs are overwritten, never accumulated into.
+ *   - The return value reports only what the host can check: argument
+ *     validity (MOE_ERR_INVALID_ARG), shapes the kernels do not support
+ *     (MOE_ERR_UNSUPPORTED -- there is no slower fallback), a workspace that
+ *     is too small (MOE_ERR_WORKSPACE) and launch failures (MOE_ERR_HIP).  On
+ *     any error nothing has been enqueued except, for MOE_ERR_HIP, the
+ *     launches before the failing one.
+ *   - Calls that share a workspace must be ordered on one stream.
+ *   - Sizes: 1 <= T, 1 <= k <= min(E, 32), E <= 1024, T*k < 2^31.
+ *   - bf16 and fp16 values are passed as their 16-bit patterns (uint16_t).
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t moe_status;
+#define MOE_OK               0
+#define MOE_ERR_INVALID_ARG  1
+#define MOE_ERR_UNSUPPORTED  2
+#define MOE_ERR_WORKSPACE    3
+#define MOE_ERR_HIP          4
+
+/* Expert weight storage formats accepted by moe_grouped_ffn. */
+#define MOE_WFMT_BF16   0   /* bf16 matrices [E, out, in]                       */
+#define MOE_WFMT_Q3G128 1   /* 3-bit codes, groups of 128 along `in`, fp16 scale */
+
+#define MOE_MAX_TOPK    32
+#define MOE_MAX_EXPERTS 1024
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* moe_status_string(moe_status s);
+
+/* Library version as "major.minor.patch" (static string). */
+const char* moe_version(void);
+
+/*
+ * Bytes of workspace needed by moe_permute and moe_grouped_ffn for a layer
+ * of T tokens, E experts, top-k, hidden H, expert intermediate I and the
+ * weight format `wfmt`.  One buffer of this size serves both calls (they
+ * use it in stream order).  Returns 0 for arguments that are invalid or
+ * unsupported.  Alignment: 256 bytes (any hipMalloc pointer).
+ */
+size_t moe_workspace_size(int T, int E, int k, int H, int I, int wfmt);
+
+/*
+ * moe_route_topk -- top-k gate over the layer's experts.
+ *
+ * For each token t (row of `logits`, fp32 [T, E], row-major):
+ *   topk_ids[t, 0..k-1]  int32  the k experts with the largest logits, in
+ *                        descending logit order; equal logits are ordered
+ *                        by expert index ascending and -0.0 equals +0.0;
+ *   topk_w[t, j]         fp32   softmax over the k selected logits,
+ *                        exp(l_j - l_0) / sum_i exp(l_i - l_0);
+ *   expert_counts[e]     int32  number of (token, slot) pairs routed to e
+ *                        (the router's load histogram, E entries).
+ * Reading of the pages (the gate is not written there): softmax over the
+ * selected logits, no scaling factor, no shared expert.  Logits must be
+ * finite; NaN/Inf give unspecified ids.  Errors: NULL pointers, T < 1,
+ * E < 1 or E > 1024, k outside [1, min(E, 32)], T*k >= 2^31 ->
+ * MOE_ERR_INVALID_ARG.
+ */
+moe_status moe_route_topk(const float* logits, int T, int E, int k,
+                          int32_t* topk_ids, float* topk_w, int32_t* expert_counts,
+                          void* stream);
+
+/*
+ * moe_permute -- per-expert route lists (a stable counting sort of the
+ * T*k pairs p = t*k + j by expert id).
+ *
+ * Inputs:  topk_ids int32 [T, k], every id in [0, E) and distinct within a
+ *          token (ids outside [0, E) are undefined behaviour).
+ * Outputs: expert_offsets int32 [E+1]  exclusive prefix sum of the per-expert
+ *                                      counts; expert_offsets[E] = T*k;
+ *          sorted_pair    int32 [T*k]  pair stored at sorted row i: rows
+ *                                      [offsets[e], offsets[e+1]) hold the
+ *                                      pairs routed to e, ascending pair index;
+ *          pair_to_sorted int32 [T*k]  inverse of sorted_pair.
+ * The result is unique and bit-exact (no order depends on scheduling).
+ * Workspace: >= moe_workspace_size(T, E, k, ...) bytes (only the permute
+ * part is used here), else MOE_ERR_WORKSPACE.
+ */
+moe_status moe_permute(const int32_t* topk_ids, int T, int E, int k,
+                       int32_t* expert_offsets, int32_t* sorted_pair, int32_t* pair_to_sorted,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * moe_grouped_ffn -- run each expert's SwiGLU FFN over its route list.
+ *
+ * For every sorted row i in [offsets[e], offsets[e+1]), token t =
+ * sorted_pair[i] / k:
+ *     g = x[t] . W_gate[e]^T,  u = x[t] . W_up[e]^T        (length I)
+ *     a = silu(g) * u,         silu(g) = g / (1 + exp(-g))
+ *     y_sorted[i] = a . W_down[e]^T                        (length H)
+ * Reading of the pages (the expert's form is not written there): the SwiGLU
+ * expert; matrices stored [out, in] with the reduction index contiguous.
+ *
+ * x          bf16 [T, H]
+ * w_gate     MOE_WFMT_BF16: bf16 [E, I, H];   MOE_WFMT_Q3G128: uint32 [E, I, H/128, 13]
+ * w_up       same as w_gate
+ * w_down     MOE_WFMT_BF16: bf16 [E, H, I];   MOE_WFMT_Q3G128: uint32 [E, H, I/128, 13]
+ * s_gate, s_up, s_down   fp16 scales [E, I, H/128] / [E, H, I/128] for
+ *            MOE_WFMT_Q3G128 (must be NULL for MOE_WFMT_BF16).  3-bit group
+ *            layout: 13 words per 128 weights; field j of a word at bits
+ *            [3j, 3j+3), 10 fields in words 0..11, 8 in word 12; weight =
+ *            scale * (field - 4).
+ * expert_offsets, sorted_pair   as produced by moe_permute.
+ * fat_threshold  experts with at least this many rows run as MFMA tiles of
+ *            128 rows with weight tiles staged in LDS; smaller experts stream
+ *            their weights once through a 32-row tile.  Both paths compute the
+ *            same function (rounding differs only in summation order).
+ *            Must be >= 1.
+ * y_sorted   fp16 [T*k, H] output in sorted-row order.
+ * Precision: products accumulate in fp32; a is stored as fp16 and the down
+ * projection multiplies fp16 a by W_down converted to fp16 (exact for
+ * |w| in [2^-14, 65504]; smaller magnitudes lose at most 2^-24 absolute).
+ * Shapes: H % 256 == 0 and I % 128 == 0, else MOE_ERR_UNSUPPORTED.
+ * Workspace: >= moe_workspace_size(T, E, k, H, I, wfmt) bytes.
+ */
+moe_status moe_grouped_ffn(const uint16_t* x, int wfmt,
+                           const void* w_gate, const void* w_up, const void* w_down,
+                           const uint16_t* s_gate, const uint16_t* s_up, const uint16_t* s_down,
+                           const int32_t* expert_offsets, const int32_t* sorted_pair,
+                           int T, int E, int k, int H, int I, int fat_threshold,
+                           uint16_t* y_sorted, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
+/*
+ * moe_combine -- out[t, :] = sum_{j=0..k-1} topk_w[t, j] * y_sorted[pair_to_sorted[t*k+j], :]
+ *
+ * fp32 accumulation in ascending j, no atomics: bit-identical across runs.
+ * y_sorted fp16 [T*k, H], topk_w fp32 [T, k], pair_to_sorted int32 [T*k],
+ * out fp32 [T, H].  H % 8 == 0 else MOE_ERR_UNSUPPORTED.
+ */
+moe_status moe_combine(const uint16_t* y_sorted, const float* topk_w, const int32_t* pair_to_sorted,
+                       int T, int k, int H, float* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

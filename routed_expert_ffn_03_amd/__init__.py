@@ -1,0 +1,15 @@
+"""MI355X-native routed-expert (MoE) layer: a C-ABI HIP library
+(``libmoe_mi355x.so``) with a thin ctypes binding.
+
+    moe_route_topk   top-k gate, gate weights, load histogram
+    moe_permute      per-expert route lists
+    moe_grouped_ffn  every expert's SwiGLU FFN (MFMA tiles for busy experts,
+                     HBM-streaming tiles for the rest)
+    moe_combine      gate-weighted sum per token
+"""
+from .binding import (  # noqa: F401
+    MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP,
+    MOE_WFMT_BF16, MOE_WFMT_Q3G128, DEFAULT_FAT_THRESHOLD, EXPORTS, MoEError, lib,
+    moe_workspace_size, moe_route_topk, moe_permute, moe_grouped_ffn, moe_combine,
+)
+from .layer import MoELayerBuffers  # noqa: F401

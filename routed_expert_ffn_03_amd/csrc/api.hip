@@ -1,0 +1,108 @@
+// C ABI of the routed-expert layer library: argument checks, workspace
+// layout, and the launches.  Every check here happens on the host before
+// anything is enqueued; nothing here synchronises with the device.
+// Failing loudly instead of falling back: "dsv41-flash-engram-disk-prestage",
+// section "The prestage, per decode step", point 4.
+#include "../../include/moe_mi355x.h"
+#include "kernels.h"
+
+namespace {
+
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+bool bad_tek(int T, int E, int k) {
+    if (T < 1 || E < 1 || E > moe::MAX_EXPERTS || k < 1) return true;
+    if (k > moe::MAX_TOPK || k > E) return true;
+    if ((long long)T * (long long)k >= (1LL << 31)) return true;
+    return false;
+}
+
+bool ffn_shape_ok(int H, int I) { return H >= 256 && I >= 128 && H % 256 == 0 && I % 128 == 0; }
+
+moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(moe_status s) {
+    switch (s) {
+        case MOE_OK: return "MOE_OK";
+        case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG: invalid argument";
+        case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED: shape or format not supported by the kernels";
+        case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE: workspace missing or too small";
+        case MOE_ERR_HIP: return "MOE_ERR_HIP: HIP launch or runtime error";
+        default: return "MOE_ERR_UNKNOWN";
+    }
+}
+
+const char* moe_version(void) { return "0.1.0"; }
+
+size_t moe_workspace_size(int T, int E, int k, int H, int I, int wfmt) {
+    if (bad_tek(T, E, k) || !ffn_shape_ok(H, I)) return 0;
+    if (wfmt != MOE_WFMT_BF16 && wfmt != MOE_WFMT_Q3G128) return 0;
+    return align256(moe::permute_ws_bytes(T, E)) + moe::ffn_ws_bytes(T, E, k, H, I);
+}
+
+moe_status moe_route_topk(const float* logits, int T, int E, int k, int32_t* topk_ids, float* topk_w,
+                          int32_t* expert_counts, void* stream) {
+    if (!logits || !topk_ids || !topk_w || !expert_counts) return MOE_ERR_INVALID_ARG;
+    if (bad_tek(T, E, k)) return MOE_ERR_INVALID_ARG;
+    return hip_status(moe::launch_route_topk(logits, T, E, k, topk_ids, topk_w, expert_counts,
+                                             reinterpret_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_permute(const int32_t* topk_ids, int T, int E, int k, int32_t* expert_offsets,
+                       int32_t* sorted_pair, int32_t* pair_to_sorted, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+    if (!topk_ids || !expert_offsets || !sorted_pair || !pair_to_sorted) return MOE_ERR_INVALID_ARG;
+    if (bad_tek(T, E, k)) return MOE_ERR_INVALID_ARG;
+    if (!workspace || workspace_bytes < moe::permute_ws_bytes(T, E)) return MOE_ERR_WORKSPACE;
+    return hip_status(moe::launch_permute(topk_ids, T, E, k, expert_offsets, sorted_pair, pair_to_sorted,
+                                          reinterpret_cast<int32_t*>(workspace),
+                                          reinterpret_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_grouped_ffn(const uint16_t* x, int wfmt, const void* w_gate, const void* w_up, const void* w_down,
+                           const uint16_t* s_gate, const uint16_t* s_up, const uint16_t* s_down,
+                           const int32_t* expert_offsets, const int32_t* sorted_pair, int T, int E, int k, int H,
+                           int I, int fat_threshold, uint16_t* y_sorted, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+    if (!x || !w_gate || !w_up || !w_down || !expert_offsets || !sorted_pair || !y_sorted)
+        return MOE_ERR_INVALID_ARG;
+    if (bad_tek(T, E, k) || fat_threshold < 1 || H < 1 || I < 1) return MOE_ERR_INVALID_ARG;
+    if (wfmt == MOE_WFMT_BF16) {
+        if (s_gate || s_up || s_down) return MOE_ERR_INVALID_ARG;
+    } else if (wfmt == MOE_WFMT_Q3G128) {
+        if (!s_gate || !s_up || !s_down) return MOE_ERR_INVALID_ARG;
+    } else {
+        return MOE_ERR_UNSUPPORTED;
+    }
+    if (!ffn_shape_ok(H, I)) return MOE_ERR_UNSUPPORTED;
+    const size_t need = moe_workspace_size(T, E, k, H, I, wfmt);
+    if (!workspace || workspace_bytes < need) return MOE_ERR_WORKSPACE;
+    moe::FfnLaunch a;
+    a.x = x;
+    a.wfmt = wfmt;
+    a.wg = w_gate; a.wu = w_up; a.wd = w_down;
+    a.sg = s_gate; a.su = s_up; a.sd = s_down;
+    a.offsets = expert_offsets;
+    a.sorted_pair = sorted_pair;
+    a.T = T; a.E = E; a.k = k; a.H = H; a.I = I;
+    a.fat_threshold = fat_threshold;
+    a.y = y_sorted;
+    a.ws = reinterpret_cast<char*>(workspace) + align256(moe::permute_ws_bytes(T, E));
+    return hip_status(moe::launch_grouped_ffn(a, reinterpret_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_combine(const uint16_t* y_sorted, const float* topk_w, const int32_t* pair_to_sorted, int T, int k,
+                       int H, float* out, void* stream) {
+    if (!y_sorted || !topk_w || !pair_to_sorted || !out) return MOE_ERR_INVALID_ARG;
+    if (T < 1 || k < 1 || k > moe::MAX_TOPK || H < 1 || (long long)T * k >= (1LL << 31))
+        return MOE_ERR_INVALID_ARG;
+    if (H % 8) return MOE_ERR_UNSUPPORTED;
+    return hip_status(moe::launch_combine(y_sorted, topk_w, pair_to_sorted, T, k, H, out,
+                                          reinterpret_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

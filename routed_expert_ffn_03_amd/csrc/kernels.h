@@ -1,0 +1,43 @@
+// Host-side launchers of the library's kernels (internal, C++ linkage).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int MAX_EXPERTS = 1024;
+constexpr int MAX_TOPK = 32;
+
+hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* topk_ids,
+                             float* topk_w, int32_t* counts, hipStream_t s);
+
+size_t permute_ws_bytes(int T, int E);
+hipError_t launch_permute(const int32_t* ids, int T, int E, int k, int32_t* offsets,
+                          int32_t* sorted_pair, int32_t* pair_to_sorted, int32_t* block_hist,
+                          hipStream_t s);
+
+struct FfnLaunch {
+    const uint16_t* x;
+    int wfmt;                       // 0 = bf16, 1 = 3-bit groups of 128
+    const void* wg;
+    const void* wu;
+    const void* wd;
+    const uint16_t* sg;
+    const uint16_t* su;
+    const uint16_t* sd;
+    const int32_t* offsets;
+    const int32_t* sorted_pair;
+    int T, E, k, H, I, fat_threshold;
+    uint16_t* y;
+    void* ws;                       // FFN part of the workspace
+};
+
+size_t ffn_ws_bytes(int T, int E, int k, int H, int I);
+hipError_t launch_grouped_ffn(const FfnLaunch& a, hipStream_t s);
+
+hipError_t launch_combine(const uint16_t* y, const float* w, const int32_t* p2s, int T, int k, int H,
+                          float* out, hipStream_t s);
+
+}  // namespace moe

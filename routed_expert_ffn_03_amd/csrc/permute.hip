@@ -1,0 +1,105 @@
+// Permute: per-expert route lists as a stable counting sort of the pairs
+// p = t*k + j by expert id.
+//
+// One route list per expert, only experts with a positive count run:
+// dsv41-flash-offload wiki, repository file table, entry for the staged
+// cold-expert prefill patch.  Reading for a unique order: lists in expert
+// order, ascending pair index inside a list.
+//
+// Three passes, no global atomics, every position a pure function of the ids:
+//   1. block histogram: block b (256 consecutive tokens) counts its pairs per
+//      expert in LDS and writes hist[b][e];
+//   2. scan (one block): per expert, totals -> offsets (exclusive scan over
+//      experts) and hist[b][e] -> offsets[e] + sum_{b'<b} hist[b'][e];
+//   3. scatter: inside block b the rank of pair (t, j) among the block's
+//      pairs of the same expert is (pairs of lower waves) + (lower lanes of
+//      its own wave), read off 64-bit lane masks built with LDS atomic OR.
+//      Since a token picks an expert at most once, lane order = pair order.
+#include "common.h"
+#include "kernels.h"
+
+namespace moe {
+namespace {
+
+constexpr int PB_TOKENS = 256;            // tokens (= threads) per block
+constexpr int PB_WAVES = PB_TOKENS / WAVE;
+
+__global__ __launch_bounds__(PB_TOKENS)
+void permute_hist_kernel(const int32_t* __restrict__ ids, int T, int E, int k,
+                         int32_t* __restrict__ block_hist) {
+    __shared__ int hist[MAX_EXPERTS];
+    for (int e = threadIdx.x; e < E; e += PB_TOKENS) hist[e] = 0;
+    __syncthreads();
+    const int t = blockIdx.x * PB_TOKENS + threadIdx.x;
+    if (t < T)
+        for (int j = 0; j < k; ++j) atomicAdd(&hist[ids[(size_t)t * k + j]], 1);
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += PB_TOKENS) block_hist[(size_t)blockIdx.x * E + e] = hist[e];
+}
+
+__global__ __launch_bounds__(1024)
+void permute_scan_kernel(int32_t* __restrict__ block_hist, int nblocks, int E, int P,
+                         int32_t* __restrict__ offsets) {
+    __shared__ int scratch[16];
+    const int e = threadIdx.x;
+    int total = 0;
+    if (e < E)
+        for (int b = 0; b < nblocks; ++b) total += block_hist[(size_t)b * E + e];
+    const int incl = block_inclusive_scan(total, scratch);
+    if (e < E) {
+        int base = incl - total;
+        offsets[e] = base;
+        for (int b = 0; b < nblocks; ++b) {
+            const size_t i = (size_t)b * E + e;
+            const int c = block_hist[i];
+            block_hist[i] = base;
+            base += c;
+        }
+    }
+    if (e == 0) offsets[E] = P;
+}
+
+__global__ __launch_bounds__(PB_TOKENS)
+void permute_scatter_kernel(const int32_t* __restrict__ ids, int T, int E, int k,
+                            const int32_t* __restrict__ block_base, int32_t* __restrict__ sorted_pair,
+                            int32_t* __restrict__ pair_to_sorted) {
+    __shared__ unsigned long long mask[PB_WAVES][MAX_EXPERTS];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    for (int i = threadIdx.x; i < PB_WAVES * E; i += PB_TOKENS) mask[i / E][i % E] = 0ull;
+    __syncthreads();
+    const int t = blockIdx.x * PB_TOKENS + threadIdx.x;
+    const unsigned long long bit = 1ull << lane;
+    if (t < T)
+        for (int j = 0; j < k; ++j) atomicOr(&mask[wave][ids[(size_t)t * k + j]], bit);
+    __syncthreads();
+    if (t < T) {
+        const int32_t* base = block_base + (size_t)blockIdx.x * E;
+        for (int j = 0; j < k; ++j) {
+            const int p = t * k + j;
+            const int e = ids[p];
+            int pos = base[e] + __popcll(mask[wave][e] & (bit - 1ull));
+            for (int w = 0; w < wave; ++w) pos += __popcll(mask[w][e]);
+            sorted_pair[pos] = p;
+            pair_to_sorted[p] = pos;
+        }
+    }
+}
+
+}  // namespace
+
+size_t permute_ws_bytes(int T, int E) {
+    const size_t nb = (size_t)(T + PB_TOKENS - 1) / PB_TOKENS;
+    return nb * (size_t)E * sizeof(int32_t);
+}
+
+hipError_t launch_permute(const int32_t* ids, int T, int E, int k, int32_t* offsets,
+                          int32_t* sorted_pair, int32_t* pair_to_sorted, int32_t* block_hist,
+                          hipStream_t s) {
+    const int nb = (T + PB_TOKENS - 1) / PB_TOKENS;
+    permute_hist_kernel<<<nb, PB_TOKENS, 0, s>>>(ids, T, E, k, block_hist);
+    permute_scan_kernel<<<1, 1024, 0, s>>>(block_hist, nb, E, T * k, offsets);
+    permute_scatter_kernel<<<nb, PB_TOKENS, 0, s>>>(ids, T, E, k, block_hist, sorted_pair, pair_to_sorted);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,104 @@
+"""C-ABI boundary checks that need no GPU: the library loads, exports every
+entry point its header declares, and rejects every invalid argument with the
+documented status before touching the device.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import routed_expert_ffn_03_amd as moe
+from routed_expert_ffn_03_amd.build import LIB
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "moe_mi355x.h")
+FAKE = 0x10000        # never dereferenced: every call below fails validation first
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return re.findall(r"^\s*(?:const\s+char\s*\*|size_t|moe_status)\s*(\w+)\s*\(", src, flags=re.M)
+
+
+def test_library_exports_every_declared_symbol():
+    if not os.path.exists(LIB):
+        pytest.skip("library not built")
+    names = declared_functions()
+    assert set(names) == set(moe.EXPORTS)
+    raw = ctypes.CDLL(LIB)
+    for n in names:
+        assert hasattr(raw, n), n
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(LIB):
+        pytest.skip("library not built")
+    return moe.lib()
+
+
+def test_status_strings(L):
+    for s in range(5):
+        assert L.moe_status_string(s).startswith(b"MOE_")
+    assert L.moe_status_string(99) == b"MOE_ERR_UNKNOWN"
+    assert L.moe_version() == b"0.1.0"
+
+
+def test_workspace_size(L):
+    ws = L.moe_workspace_size(16384, 384, 8, 4096, 2048, 0)
+    assert ws >= 16384 * 8 * 2048 * 2             # the fp16 activation dominates
+    assert L.moe_workspace_size(16384, 384, 8, 4096, 2048, 1) == ws
+    assert L.moe_workspace_size(4, 384, 8, 4096, 2048, 0) > 0
+    for bad in [(0, 384, 8, 4096, 2048, 0), (4, 2000, 8, 4096, 2048, 0), (4, 384, 0, 4096, 2048, 0),
+                (4, 384, 33, 4096, 2048, 0), (4, 4, 5, 4096, 2048, 0), (4, 384, 8, 4000, 2048, 0),
+                (4, 384, 8, 4096, 2000, 0), (4, 384, 8, 4096, 2048, 5), (1 << 28, 384, 8, 4096, 2048, 0)]:
+        assert L.moe_workspace_size(*bad) == 0, bad
+
+
+def test_route_rejects(L):
+    ok = (FAKE, 64, 16, 2, FAKE, FAKE, FAKE, None)
+    for i in (0, 4, 5, 6):
+        args = list(ok)
+        args[i] = None
+        assert L.moe_route_topk(*args) == moe.MOE_ERR_INVALID_ARG
+    for T, E, k in [(0, 16, 2), (64, 0, 1), (64, 1025, 2), (64, 16, 0), (64, 16, 17), (64, 64, 33),
+                    (1 << 30, 16, 2)]:
+        assert L.moe_route_topk(FAKE, T, E, k, FAKE, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+
+
+def test_permute_rejects(L):
+    assert L.moe_permute(None, 64, 16, 2, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_permute(FAKE, 64, 16, 0, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_permute(FAKE, 64, 16, 2, FAKE, FAKE, FAKE, None, 1 << 20, None) == moe.MOE_ERR_WORKSPACE
+    assert L.moe_permute(FAKE, 4096, 384, 8, FAKE, FAKE, FAKE, FAKE, 100, None) == moe.MOE_ERR_WORKSPACE
+
+
+def _ffn(L, **kw):
+    a = dict(x=FAKE, wfmt=0, wg=FAKE, wu=FAKE, wd=FAKE, sg=None, su=None, sd=None, off=FAKE, sp=FAKE,
+             T=64, E=16, k=2, H=256, I=128, thr=32, y=FAKE, ws=FAKE, wsb=1 << 40, s=None)
+    a.update(kw)
+    return L.moe_grouped_ffn(a["x"], a["wfmt"], a["wg"], a["wu"], a["wd"], a["sg"], a["su"], a["sd"], a["off"],
+                             a["sp"], a["T"], a["E"], a["k"], a["H"], a["I"], a["thr"], a["y"], a["ws"], a["wsb"],
+                             a["s"])
+
+
+def test_grouped_ffn_rejects(L):
+    for key in ("x", "wg", "wu", "wd", "off", "sp", "y"):
+        assert _ffn(L, **{key: None}) == moe.MOE_ERR_INVALID_ARG, key
+    assert _ffn(L, thr=0) == moe.MOE_ERR_INVALID_ARG
+    assert _ffn(L, sg=FAKE) == moe.MOE_ERR_INVALID_ARG                 # bf16 takes no scales
+    assert _ffn(L, wfmt=1) == moe.MOE_ERR_INVALID_ARG                  # 3-bit needs scales
+    assert _ffn(L, wfmt=2) == moe.MOE_ERR_UNSUPPORTED
+    assert _ffn(L, H=384) == moe.MOE_ERR_UNSUPPORTED
+    assert _ffn(L, I=192) == moe.MOE_ERR_UNSUPPORTED
+    assert _ffn(L, k=17) == moe.MOE_ERR_INVALID_ARG
+    assert _ffn(L, ws=None) == moe.MOE_ERR_WORKSPACE
+    assert _ffn(L, wsb=1024) == moe.MOE_ERR_WORKSPACE
+
+
+def test_combine_rejects(L):
+    assert L.moe_combine(None, FAKE, FAKE, 4, 2, 64, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_combine(FAKE, FAKE, FAKE, 0, 2, 64, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_combine(FAKE, FAKE, FAKE, 4, 33, 64, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_combine(FAKE, FAKE, FAKE, 4, 2, 60, FAKE, None) == moe.MOE_ERR_UNSUPPORTED

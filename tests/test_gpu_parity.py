@@ -1,0 +1,212 @@
+"""GPU parity: the HIP path (through the C ABI) against the float64 oracle.
+
+Integer outputs (top-k ids, histogram, offsets, sorted pairs, inverse) must
+be bit-exact; gate weights within 2e-6; expert outputs and the layer output
+within max|err| / rms(ref) <= 1e-2 (bf16 weights) or 3e-2 (3-bit weights).
+Small layers are compared element by element over every output; the full
+layer shapes compare every index and a seeded sample of tokens.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import routed_expert_ffn_03_amd as moe
+from moe_inputs import SHAPES, LayerShape, expert_weights, for_each_expert, layer_weights, routing_inputs
+from moe_inputs.device import upload_weights
+from tests.gpu_util import (TOL_BF16, TOL_Q3, check_indices, host_raw, run_layer, say, to_dev_weights,
+                            wfmt_id)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    moe.lib()
+    yield
+
+
+def tol(shape):
+    return TOL_BF16 if shape.wfmt == "bf16" else TOL_Q3
+
+
+SMALL = [
+    (LayerShape("tiny", 64, 256, 128, 16, 2, "normal", "bf16"), [1, 8, 32, 10**6]),
+    (LayerShape("mid", 700, 512, 384, 6, 2, "normal", "bf16"), [1, 32, 10**6]),
+    (LayerShape("skew", 333, 256, 256, 40, 4, "zipf", "bf16"), [32]),
+    (LayerShape("e100", 50, 256, 128, 100, 3, "normal", "bf16"), [1, 32]),
+    (LayerShape("t1", 1, 256, 128, 16, 2, "normal", "bf16"), [1, 32]),
+    (LayerShape("kE", 8, 256, 128, 16, 16, "normal", "bf16"), [1, 32]),
+    (LayerShape("k1", 100, 256, 128, 8, 1, "normal", "bf16"), [1, 32]),
+    (LayerShape("tiny_q3", 64, 256, 128, 16, 2, "normal", "q3"), [1, 32, 10**6]),
+    (LayerShape("mid_q3", 700, 512, 384, 6, 2, "normal", "q3"), [1, 10**6]),
+]
+
+
+@pytest.mark.parametrize("shape,thresholds", SMALL, ids=[s.name for s, _ in SMALL])
+def test_layer_small(shape, thresholds):
+    seed = 0
+    logits, x = routing_inputs(shape, seed)
+    W = layer_weights(shape, seed)
+    ref = oracle.moe_layer(logits, x, host_raw(W), shape.k)
+    dw = to_dev_weights(W)
+    bufs = moe.MoELayerBuffers(shape.T, shape.E, shape.k, shape.H, shape.I, wfmt_id(shape))
+    outs = []
+    for thr in thresholds:
+        say(f"[layer {shape.name}] T={shape.T} E={shape.E} k={shape.k} H={shape.H} I={shape.I} "
+            f"wfmt={shape.wfmt} fat_threshold={thr}")
+        got = run_layer(bufs, logits, x, dw, fat_threshold=thr)
+        check_indices(got, ref)
+        ey = oracle.rel_max_err(got["Y"], ref["Y"])
+        eo = oracle.rel_max_err(got["out"], ref["out"])
+        say(f"   Y err {ey:.3e}  out err {eo:.3e}")
+        assert ey <= tol(shape) and eo <= tol(shape)
+        outs.append(got["out"])
+    # same thresholds run again: bit-identical (no atomics in any float path)
+    got = run_layer(bufs, logits, x, dw, fat_threshold=thresholds[-1])
+    assert np.array_equal(got["out"], outs[-1])
+
+
+def _tie_logits(T, E, seed):
+    rng = np.random.default_rng(seed)
+    lg = (np.round(rng.standard_normal((T, E)) * 2) / 2).astype(np.float32)
+    lg[rng.random((T, E)) < 0.15] = np.float32(-0.0)
+    lg[rng.random((T, E)) < 0.15] = np.float32(0.0)
+    return lg
+
+
+@pytest.mark.parametrize("T,E,k", [(10, 40, 6), (200, 40, 6), (65, 1024, 32), (300, 100, 1), (7, 16, 16),
+                                   (129, 384, 8)])
+def test_route_ties_and_shapes(T, E, k):
+    say(f"[route] T={T} E={E} k={k} (ties, signed zeros)")
+    lg = _tie_logits(T, E, T + E + k)
+    ids_ref, w_ref = oracle.route_topk(lg, k)
+    d = torch.from_numpy(lg).cuda()
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    cnt = torch.full((E,), 12345, dtype=torch.int32, device="cuda")
+    moe.moe_route_topk(d, k, ids, w, cnt)
+    torch.cuda.synchronize()
+    assert np.array_equal(ids.cpu().numpy(), ids_ref)
+    assert np.array_equal(cnt.cpu().numpy(), oracle.expert_histogram(ids_ref, E))
+    np.testing.assert_allclose(w.cpu().numpy(), w_ref, rtol=0, atol=2e-6)
+
+
+@pytest.mark.parametrize("name", ["decode", "prefill1k", "prefill16k", "prefill16k_q3"])
+def test_route_and_permute_full_batch(name):
+    shape = SHAPES[name]
+    for seed in (0, 1, 2):
+        say(f"[route+permute] {name} seed={seed}")
+        logits, _ = routing_inputs(shape, seed)
+        ids_ref, w_ref = oracle.route_topk(logits, shape.k)
+        counts, offsets, sp, p2s = oracle.permute(ids_ref, shape.E)
+        bufs = moe.MoELayerBuffers(shape.T, shape.E, shape.k, shape.H, shape.I, wfmt_id(shape))
+        moe.moe_route_topk(torch.from_numpy(logits).cuda(), shape.k, bufs.topk_ids, bufs.topk_w,
+                           bufs.expert_counts)
+        moe.moe_permute(bufs.topk_ids, shape.E, bufs.expert_offsets, bufs.sorted_pair, bufs.pair_to_sorted,
+                        bufs.workspace)
+        torch.cuda.synchronize()
+        assert np.array_equal(bufs.topk_ids.cpu().numpy(), ids_ref)
+        assert np.array_equal(bufs.expert_counts.cpu().numpy(), counts)
+        assert np.array_equal(bufs.expert_offsets.cpu().numpy(), offsets)
+        assert np.array_equal(bufs.sorted_pair.cpu().numpy(), sp)
+        assert np.array_equal(bufs.pair_to_sorted.cpu().numpy(), p2s)
+        np.testing.assert_allclose(bufs.topk_w.cpu().numpy(), w_ref, rtol=0, atol=2e-6)
+
+
+def test_permute_skewed_extremes():
+    # every token on the same k experts (maximum skew) and a permutation of
+    # a single expert per token
+    for T, E, k, kind in [(5000, 64, 4, "same"), (20000, 300, 1, "mod"), (3, 1024, 32, "same")]:
+        say(f"[permute] T={T} E={E} k={k} {kind}")
+        if kind == "same":
+            ids = np.tile(np.arange(E - k, E, dtype=np.int32)[::-1], (T, 1))
+        else:
+            ids = (np.arange(T, dtype=np.int32) * 7 % E)[:, None]
+        counts, offsets, sp, p2s = oracle.permute(ids, E)
+        d = torch.from_numpy(np.ascontiguousarray(ids)).cuda()
+        off = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+        gsp = torch.empty(T * k, dtype=torch.int32, device="cuda")
+        gp2s = torch.empty(T * k, dtype=torch.int32, device="cuda")
+        ws = torch.empty(moe.moe_workspace_size(T, E, k, 256, 128), dtype=torch.uint8, device="cuda")
+        moe.moe_permute(d, E, off, gsp, gp2s, ws)
+        torch.cuda.synchronize()
+        assert np.array_equal(off.cpu().numpy(), offsets)
+        assert np.array_equal(gsp.cpu().numpy(), sp)
+        assert np.array_equal(gp2s.cpu().numpy(), p2s)
+
+
+def test_combine_alone():
+    rng = np.random.default_rng(3)
+    T, k, H = 37, 5, 264
+    y = rng.standard_normal((T * k, H)).astype(np.float16)
+    w = rng.random((T, k)).astype(np.float32)
+    p2s = rng.permutation(T * k).astype(np.int32)
+    ref = oracle.combine(y.astype(np.float64), w.astype(np.float64), p2s, k)
+    out = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    moe.moe_combine(torch.from_numpy(y).cuda(), torch.from_numpy(w).cuda(), torch.from_numpy(p2s).cuda(), out)
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(out.cpu().numpy(), ref, rtol=1e-6, atol=1e-6)
+
+
+# ------------------------------------------------------------ full layer shapes
+
+_DEV_W = {}
+
+
+def device_weights(shape, seed):
+    key = (shape.H, shape.I, shape.E, shape.wfmt, seed)
+    if key not in _DEV_W:
+        say(f"[weights] generating {shape.wfmt} layer H={shape.H} I={shape.I} E={shape.E} seed={seed}")
+        _DEV_W.clear()
+        _DEV_W[key] = upload_weights(shape, seed)
+        say("[weights] on device")
+    return _DEV_W[key]
+
+
+def full_layer_case(shape, seed, n_sample):
+    logits, x = routing_inputs(shape, seed)
+    dw = device_weights(shape, seed)
+    bufs = moe.MoELayerBuffers(shape.T, shape.E, shape.k, shape.H, shape.I, wfmt_id(shape))
+    dl = torch.from_numpy(logits).cuda()
+    dx = torch.from_numpy(x.view(np.int16)).cuda()
+    bufs.forward(dl, dx, dw, fat_threshold=32)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(1000 + seed)
+    if n_sample >= shape.T:
+        tokens = list(range(shape.T))
+    else:
+        tokens = sorted({0, shape.T - 1, *rng.choice(shape.T, n_sample - 2, replace=False).tolist()})
+    ids_ref, _ = oracle.route_topk(logits, shape.k)
+    need = sorted({int(e) for t in tokens for e in ids_ref[t]})
+    say(f"   sampled tokens {len(tokens)}, experts for the oracle {len(need)}")
+    cache = {}
+    for_each_expert(shape, seed, lambda e, a: cache.__setitem__(e, a), experts=need)
+    ref = oracle.moe_layer(logits, x, lambda e: cache.pop(e), shape.k, tokens=tokens)
+    got = {
+        "ids": bufs.topk_ids.cpu().numpy(), "w": bufs.topk_w.cpu().numpy(),
+        "counts": bufs.expert_counts.cpu().numpy(), "offsets": bufs.expert_offsets.cpu().numpy(),
+        "sorted_pair": bufs.sorted_pair.cpu().numpy(), "pair_to_sorted": bufs.pair_to_sorted.cpu().numpy(),
+    }
+    check_indices(got, ref)
+    rows = sorted({int(ref["pair_to_sorted"][t * shape.k + j]) for t in tokens for j in range(shape.k)})
+    y = bufs.y_sorted[torch.tensor(rows, device="cuda")].float().cpu().numpy()
+    out = bufs.out[torch.tensor(tokens, device="cuda")].cpu().numpy()
+    ey = oracle.rel_max_err(y, ref["Y"][rows])
+    eo = oracle.rel_max_err(out, ref["out"])
+    say(f"   Y err {ey:.3e}  out err {eo:.3e}")
+    assert ey <= tol(shape) and eo <= tol(shape)
+    # fat/thin mix of this batch, for the record
+    n = np.diff(got["offsets"])
+    say(f"   experts touched {int((n > 0).sum())}, fat {int((n >= 32).sum())}, thin {int(((n > 0) & (n < 32)).sum())}")
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name,n_sample", [("decode", 4), ("prefill1k", 12), ("prefill16k", 10),
+                                           ("prefill16k_q3", 10)])
+def test_layer_full_shape(name, n_sample):
+    shape = SHAPES[name]
+    say(f"[full layer] {name} T={shape.T} wfmt={shape.wfmt}")
+    full_layer_case(shape, 0, n_sample)
