@@ -31,13 +31,9 @@ void combine_kernel(const uint16_t* __restrict__ y, const float* __restrict__ w,
         const size_t p = (size_t)t * k + j;
         const float wj = w[p];
         const size_t row = (size_t)p2s[p];
-        u32x4 v = ldg16(y + row * H + col);
+        const f16x8 h = __builtin_bit_cast(f16x8, ldg16(y + row * H + col));
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            f16x2 h = __builtin_bit_cast(f16x2, v[i]);
-            acc[2 * i] += wj * (float)h[0];
-            acc[2 * i + 1] += wj * (float)h[1];
-        }
+        for (int i = 0; i < 8; ++i) acc[i] += wj * (float)h[i];
     }
     float* o = out + (size_t)t * H + col;
     u32x4 a, b;
