@@ -167,6 +167,31 @@ moe_status moe_grouped_ffn(const uint16_t* x, int wfmt,
                            void* stream);
 
 /*
+ * The three steps of moe_grouped_ffn, callable one by one (same arguments,
+ * same workspace; moe_grouped_ffn == plan + gate_up + down on one stream).
+ * They communicate through the workspace: the plan writes the batch lists,
+ * gate_up writes the activation a (fp16 [T*k, I]) that down reads.
+ *
+ * moe_ffn_plan -- cut every non-empty route list into batches that share one
+ * read of the expert's weights (wiki file table, segment patch entry): lists
+ * of at least fat_threshold rows into 128-row MFMA batches, shorter lists
+ * into 32-row streaming batches.  Reads expert_offsets only.
+ */
+moe_status moe_ffn_plan(const int32_t* expert_offsets, int T, int E, int k, int H, int I, int wfmt,
+                        int fat_threshold, void* workspace, size_t workspace_bytes, void* stream);
+
+/* moe_ffn_gate_up -- a = silu(x W_gate^T) * (x W_up^T) for every planned batch,
+ * stored fp16 in the workspace (row i of a belongs to sorted row i). */
+moe_status moe_ffn_gate_up(const uint16_t* x, int wfmt, const void* w_gate, const void* w_up,
+                           const uint16_t* s_gate, const uint16_t* s_up, const int32_t* sorted_pair,
+                           int T, int E, int k, int H, int I, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
+/* moe_ffn_down -- y_sorted = a W_down^T for every planned batch. */
+moe_status moe_ffn_down(int wfmt, const void* w_down, const uint16_t* s_down, int T, int E, int k, int H, int I,
+                        uint16_t* y_sorted, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * moe_combine -- out[t, :] = sum_{j=0..k-1} topk_w[t, j] * y_sorted[pair_to_sorted[t*k+j], :]
  *
  * fp32 accumulation in ascending j, no atomics: bit-identical across runs.

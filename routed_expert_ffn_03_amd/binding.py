@@ -22,7 +22,8 @@ MOE_WFMT_Q3G128 = 1
 DEFAULT_FAT_THRESHOLD = 32
 
 EXPORTS = ("moe_status_string", "moe_version", "moe_workspace_size", "moe_route_topk",
-           "moe_permute", "moe_grouped_ffn", "moe_combine")
+           "moe_permute", "moe_grouped_ffn", "moe_ffn_plan", "moe_ffn_gate_up", "moe_ffn_down",
+           "moe_combine")
 
 _lib = None
 
@@ -54,6 +55,12 @@ def lib() -> ctypes.CDLL:
         L.moe_grouped_ffn.restype = i32
         L.moe_grouped_ffn.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp, vp, vp,
                                       i32, i32, i32, i32, i32, i32, vp, vp, sz, vp]
+        L.moe_ffn_plan.restype = i32
+        L.moe_ffn_plan.argtypes = [vp, i32, i32, i32, i32, i32, i32, i32, vp, sz, vp]
+        L.moe_ffn_gate_up.restype = i32
+        L.moe_ffn_gate_up.argtypes = [vp, i32, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, sz, vp]
+        L.moe_ffn_down.restype = i32
+        L.moe_ffn_down.argtypes = [i32, vp, vp, i32, i32, i32, i32, i32, vp, vp, sz, vp]
         L.moe_combine.restype = i32
         L.moe_combine.argtypes = [vp, vp, vp, i32, i32, i32, vp, vp]
         _lib = L
@@ -134,6 +141,30 @@ def moe_grouped_ffn(x, w_gate, w_up, w_down, expert_offsets, sorted_pair, k, y_s
                                  _ptr(s_up), _ptr(s_down), _ptr(expert_offsets), _ptr(sorted_pair), T, E, k, H, I,
                                  fat_threshold, _ptr(y_sorted), _ptr(workspace), workspace.numel(),
                                  _stream(stream)), "moe_grouped_ffn")
+
+
+def moe_ffn_plan(expert_offsets, T, k, H, I, workspace, fat_threshold=DEFAULT_FAT_THRESHOLD,
+                 wfmt=MOE_WFMT_BF16, stream=None):
+    E = expert_offsets.numel() - 1
+    _dev(expert_offsets, torch.int32, "expert_offsets")
+    _dev(workspace, torch.uint8, "workspace")
+    _check(lib().moe_ffn_plan(_ptr(expert_offsets), T, E, k, H, I, wfmt, fat_threshold, _ptr(workspace),
+                              workspace.numel(), _stream(stream)), "moe_ffn_plan")
+
+
+def moe_ffn_gate_up(x, w_gate, w_up, sorted_pair, E, k, workspace, s_gate=None, s_up=None,
+                    wfmt=MOE_WFMT_BF16, stream=None):
+    T, H = x.shape
+    I = w_gate.shape[1]
+    _check(lib().moe_ffn_gate_up(_ptr(x), wfmt, _ptr(w_gate), _ptr(w_up), _ptr(s_gate), _ptr(s_up),
+                                 _ptr(sorted_pair), T, E, k, H, I, _ptr(workspace), workspace.numel(),
+                                 _stream(stream)), "moe_ffn_gate_up")
+
+
+def moe_ffn_down(w_down, T, E, k, I, y_sorted, workspace, s_down=None, wfmt=MOE_WFMT_BF16, stream=None):
+    H = y_sorted.shape[1]
+    _check(lib().moe_ffn_down(wfmt, _ptr(w_down), _ptr(s_down), T, E, k, H, I, _ptr(y_sorted),
+                              _ptr(workspace), workspace.numel(), _stream(stream)), "moe_ffn_down")
 
 
 def moe_combine(y_sorted, topk_w, pair_to_sorted, out, stream=None):

@@ -63,6 +63,67 @@ moe_status moe_permute(const int32_t* topk_ids, int T, int E, int k, int32_t* ex
                                           reinterpret_cast<hipStream_t>(stream)));
 }
 
+// Shared checks of the FFN entry points; fills `a` on success.
+static moe_status ffn_prepare(moe::FfnLaunch& a, int wfmt, int T, int E, int k, int H, int I,
+                              void* workspace, size_t workspace_bytes) {
+    if (bad_tek(T, E, k) || H < 1 || I < 1) return MOE_ERR_INVALID_ARG;
+    if (wfmt != MOE_WFMT_BF16 && wfmt != MOE_WFMT_Q3G128) return MOE_ERR_UNSUPPORTED;
+    if (!ffn_shape_ok(H, I)) return MOE_ERR_UNSUPPORTED;
+    const size_t need = moe_workspace_size(T, E, k, H, I, wfmt);
+    if (!workspace || workspace_bytes < need) return MOE_ERR_WORKSPACE;
+    a = moe::FfnLaunch{};
+    a.wfmt = wfmt;
+    a.T = T; a.E = E; a.k = k; a.H = H; a.I = I;
+    a.ws = reinterpret_cast<char*>(workspace) + align256(moe::permute_ws_bytes(T, E));
+    return MOE_OK;
+}
+
+static bool scales_ok(int wfmt, const void* a, const void* b) {
+    return wfmt == MOE_WFMT_BF16 ? (!a && !b) : (a && b);
+}
+
+moe_status moe_ffn_plan(const int32_t* expert_offsets, int T, int E, int k, int H, int I, int wfmt,
+                        int fat_threshold, void* workspace, size_t workspace_bytes, void* stream) {
+    if (!expert_offsets || fat_threshold < 1) return MOE_ERR_INVALID_ARG;
+    moe::FfnLaunch a;
+    moe_status st = ffn_prepare(a, wfmt, T, E, k, H, I, workspace, workspace_bytes);
+    if (st != MOE_OK) return st;
+    a.offsets = expert_offsets;
+    a.fat_threshold = fat_threshold;
+    return hip_status(moe::launch_ffn_plan(a, reinterpret_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_ffn_gate_up(const uint16_t* x, int wfmt, const void* w_gate, const void* w_up,
+                           const uint16_t* s_gate, const uint16_t* s_up, const int32_t* sorted_pair,
+                           int T, int E, int k, int H, int I, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+    if (!x || !w_gate || !w_up || !sorted_pair) return MOE_ERR_INVALID_ARG;
+    if ((wfmt == MOE_WFMT_BF16 || wfmt == MOE_WFMT_Q3G128) && !scales_ok(wfmt, s_gate, s_up))
+        return MOE_ERR_INVALID_ARG;
+    moe::FfnLaunch a;
+    moe_status st = ffn_prepare(a, wfmt, T, E, k, H, I, workspace, workspace_bytes);
+    if (st != MOE_OK) return st;
+    a.x = x;
+    a.wg = w_gate; a.wu = w_up;
+    a.sg = s_gate; a.su = s_up;
+    a.sorted_pair = sorted_pair;
+    return hip_status(moe::launch_ffn_phase(a, 1, reinterpret_cast<hipStream_t>(stream)));
+}
+
+moe_status moe_ffn_down(int wfmt, const void* w_down, const uint16_t* s_down, int T, int E, int k, int H, int I,
+                        uint16_t* y_sorted, void* workspace, size_t workspace_bytes, void* stream) {
+    if (!w_down || !y_sorted) return MOE_ERR_INVALID_ARG;
+    if ((wfmt == MOE_WFMT_BF16 || wfmt == MOE_WFMT_Q3G128) && !scales_ok(wfmt, s_down, s_down))
+        return MOE_ERR_INVALID_ARG;
+    moe::FfnLaunch a;
+    moe_status st = ffn_prepare(a, wfmt, T, E, k, H, I, workspace, workspace_bytes);
+    if (st != MOE_OK) return st;
+    a.wd = w_down;
+    a.sd = s_down;
+    a.y = y_sorted;
+    return hip_status(moe::launch_ffn_phase(a, 2, reinterpret_cast<hipStream_t>(stream)));
+}
+
 moe_status moe_grouped_ffn(const uint16_t* x, int wfmt, const void* w_gate, const void* w_up, const void* w_down,
                            const uint16_t* s_gate, const uint16_t* s_up, const uint16_t* s_down,
                            const int32_t* expert_offsets, const int32_t* sorted_pair, int T, int E, int k, int H,
@@ -70,29 +131,19 @@ moe_status moe_grouped_ffn(const uint16_t* x, int wfmt, const void* w_gate, cons
                            void* stream) {
     if (!x || !w_gate || !w_up || !w_down || !expert_offsets || !sorted_pair || !y_sorted)
         return MOE_ERR_INVALID_ARG;
-    if (bad_tek(T, E, k) || fat_threshold < 1 || H < 1 || I < 1) return MOE_ERR_INVALID_ARG;
-    if (wfmt == MOE_WFMT_BF16) {
-        if (s_gate || s_up || s_down) return MOE_ERR_INVALID_ARG;
-    } else if (wfmt == MOE_WFMT_Q3G128) {
-        if (!s_gate || !s_up || !s_down) return MOE_ERR_INVALID_ARG;
-    } else {
-        return MOE_ERR_UNSUPPORTED;
+    if (fat_threshold < 1) return MOE_ERR_INVALID_ARG;
+    if (wfmt == MOE_WFMT_BF16 || wfmt == MOE_WFMT_Q3G128) {
+        if (!scales_ok(wfmt, s_gate, s_up) || !scales_ok(wfmt, s_down, s_down)) return MOE_ERR_INVALID_ARG;
     }
-    if (!ffn_shape_ok(H, I)) return MOE_ERR_UNSUPPORTED;
-    const size_t need = moe_workspace_size(T, E, k, H, I, wfmt);
-    if (!workspace || workspace_bytes < need) return MOE_ERR_WORKSPACE;
     moe::FfnLaunch a;
-    a.x = x;
-    a.wfmt = wfmt;
-    a.wg = w_gate; a.wu = w_up; a.wd = w_down;
-    a.sg = s_gate; a.su = s_up; a.sd = s_down;
-    a.offsets = expert_offsets;
-    a.sorted_pair = sorted_pair;
-    a.T = T; a.E = E; a.k = k; a.H = H; a.I = I;
-    a.fat_threshold = fat_threshold;
-    a.y = y_sorted;
-    a.ws = reinterpret_cast<char*>(workspace) + align256(moe::permute_ws_bytes(T, E));
-    return hip_status(moe::launch_grouped_ffn(a, reinterpret_cast<hipStream_t>(stream)));
+    moe_status st = ffn_prepare(a, wfmt, T, E, k, H, I, workspace, workspace_bytes);
+    if (st != MOE_OK) return st;
+    st = moe_ffn_plan(expert_offsets, T, E, k, H, I, wfmt, fat_threshold, workspace, workspace_bytes, stream);
+    if (st != MOE_OK) return st;
+    st = moe_ffn_gate_up(x, wfmt, w_gate, w_up, s_gate, s_up, sorted_pair, T, E, k, H, I, workspace,
+                         workspace_bytes, stream);
+    if (st != MOE_OK) return st;
+    return moe_ffn_down(wfmt, w_down, s_down, T, E, k, H, I, y_sorted, workspace, workspace_bytes, stream);
 }
 
 moe_status moe_combine(const uint16_t* y_sorted, const float* topk_w, const int32_t* pair_to_sorted, int T, int k,

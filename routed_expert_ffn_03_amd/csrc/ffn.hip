@@ -127,7 +127,7 @@ __device__ __forceinline__ u32x4 q3_chunk(const uint32_t* __restrict__ wrow, con
     const int g = k >> 7, f0 = k & 127;
     const uint32_t* gw = wrow + g * Q3_WORDS;
     const int wlo = f0 / 10, n0 = f0 - wlo * 10;
-    uint32_t bits = gw[wlo] >> (3 * n0);
+    uint32_t bits = (gw[wlo] & 0x3FFFFFFFu) >> (3 * n0);   // bits 30-31 are not fields
     if (n0 > 2) bits |= gw[wlo + 1] << (30 - 3 * n0);
     const float s = (float)__builtin_bit_cast(_Float16, srow[g]);
     const float m4 = -4.0f * s;
@@ -502,23 +502,7 @@ hipError_t dev_info(DevInfo& out) {
     return hipSuccess;
 }
 
-template <int WFMT>
-void launch_phases(const FfnArgs& fa, const DevInfo& d, hipStream_t s) {
-    const int gfat = d.cus;
-    ffn_fat_kernel<1, WFMT><<<gfat, FAT_THREADS, 0, s>>>(fa);
-    ffn_thin_kernel<1, WFMT><<<d.cus * d.thin_blocks[WFMT][0], THIN_THREADS, 0, s>>>(fa);
-    ffn_fat_kernel<2, WFMT><<<gfat, FAT_THREADS, 0, s>>>(fa);
-    ffn_thin_kernel<2, WFMT><<<d.cus * d.thin_blocks[WFMT][1], THIN_THREADS, 0, s>>>(fa);
-}
-
-}  // namespace
-
-size_t ffn_ws_bytes(int T, int E, int k, int H, int I) { return ffn_layout(T, E, k, H, I).total; }
-
-hipError_t launch_grouped_ffn(const FfnLaunch& a, hipStream_t s) {
-    DevInfo d;
-    hipError_t err = dev_info(d);
-    if (err != hipSuccess) return err;
+FfnArgs make_args(const FfnLaunch& a) {
     const FfnLayout L = ffn_layout(a.T, a.E, a.k, a.H, a.I);
     char* ws = reinterpret_cast<char*>(a.ws);
     FfnArgs fa;
@@ -532,12 +516,41 @@ hipError_t launch_grouped_ffn(const FfnLaunch& a, hipStream_t s) {
     fa.hdr = reinterpret_cast<FfnHeader*>(ws + L.hdr);
     fa.fat = reinterpret_cast<MTile*>(ws + L.fat);
     fa.thin = reinterpret_cast<MTile*>(ws + L.thin);
+    return fa;
+}
+
+template <int PHASE, int WFMT>
+void launch_phase_t(const FfnArgs& fa, const DevInfo& d, hipStream_t s) {
+    ffn_fat_kernel<PHASE, WFMT><<<d.cus, FAT_THREADS, 0, s>>>(fa);
+    ffn_thin_kernel<PHASE, WFMT><<<d.cus * d.thin_blocks[WFMT][PHASE - 1], THIN_THREADS, 0, s>>>(fa);
+}
+
+}  // namespace
+
+size_t ffn_ws_bytes(int T, int E, int k, int H, int I) { return ffn_layout(T, E, k, H, I).total; }
+
+hipError_t launch_ffn_plan(const FfnLaunch& a, hipStream_t s) {
+    const FfnLayout L = ffn_layout(a.T, a.E, a.k, a.H, a.I);
+    char* ws = reinterpret_cast<char*>(a.ws);
     build_tiles_kernel<<<1, 1024, 0, s>>>(a.offsets, a.E, a.fat_threshold,
                                           reinterpret_cast<FfnHeader*>(ws + L.hdr),
                                           reinterpret_cast<MTile*>(ws + L.fat),
                                           reinterpret_cast<MTile*>(ws + L.thin));
-    if (a.wfmt == 0) launch_phases<0>(fa, d, s);
-    else launch_phases<1>(fa, d, s);
+    return hipGetLastError();
+}
+
+hipError_t launch_ffn_phase(const FfnLaunch& a, int phase, hipStream_t s) {
+    DevInfo d;
+    hipError_t err = dev_info(d);
+    if (err != hipSuccess) return err;
+    const FfnArgs fa = make_args(a);
+    if (phase == 1) {
+        if (a.wfmt == 0) launch_phase_t<1, 0>(fa, d, s);
+        else launch_phase_t<1, 1>(fa, d, s);
+    } else {
+        if (a.wfmt == 0) launch_phase_t<2, 0>(fa, d, s);
+        else launch_phase_t<2, 1>(fa, d, s);
+    }
     return hipGetLastError();
 }
 

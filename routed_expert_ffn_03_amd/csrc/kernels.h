@@ -35,7 +35,8 @@ struct FfnLaunch {
 };
 
 size_t ffn_ws_bytes(int T, int E, int k, int H, int I);
-hipError_t launch_grouped_ffn(const FfnLaunch& a, hipStream_t s);
+hipError_t launch_ffn_plan(const FfnLaunch& a, hipStream_t s);
+hipError_t launch_ffn_phase(const FfnLaunch& a, int phase, hipStream_t s);   // 1 = gate/up, 2 = down
 
 hipError_t launch_combine(const uint16_t* y, const float* w, const int32_t* p2s, int T, int k, int H,
                           float* out, hipStream_t s);
