@@ -41,6 +41,7 @@
 #include "kernels.h"
 
 #include <mutex>
+#include <type_traits>
 
 namespace moe {
 namespace {
@@ -54,11 +55,14 @@ struct FfnHeader {
     int32_t pad[62];
 };
 
-constexpr int FAT_BM = 128;
-constexpr int FAT_BN_ROWS = 256;          // weight rows per fat tile
-constexpr int FAT_BK = 64;
+constexpr int FAT_BM = 256;              // rows per fat M-tile
 constexpr int FAT_THREADS = 256;
-constexpr int FAT_STAGE = (FAT_BM + FAT_BN_ROWS) * 8;   // 16-byte chunks per stage
+constexpr int FAT_STAGE = (FAT_BM + 256) * 8;            // 16-byte chunks per LDS stage (A + B)
+constexpr size_t FAT_LDS_BYTES = 2 * FAT_STAGE * 16;     // 128 KB: double-buffered stages / epilogue
+constexpr int DMA_STAGES = 4;                            // LDS ring of the bf16 fat kernel
+constexpr uint32_t DMA_A_BYTES = 256 * 64;               // activations of one 32-k stage
+constexpr uint32_t DMA_STAGE_BYTES = 2 * DMA_A_BYTES;    // + the same for weights
+static_assert(DMA_STAGES * DMA_STAGE_BYTES <= FAT_LDS_BYTES, "LDS ring too large");
 constexpr int THIN_BM = 32;
 constexpr int THIN_THREADS = 256;
 constexpr int THIN_DEPTH = 4;             // chunks in flight per lane
@@ -74,7 +78,7 @@ struct FfnArgs {
     const uint16_t* su;
     const uint16_t* sd;
     const int32_t* sorted_pair;
-    int k, H, I;
+    int T, k, H, I;
     uint16_t* act;
     uint16_t* y;
     const FfnHeader* hdr;
@@ -121,15 +125,12 @@ void build_tiles_kernel(const int32_t* __restrict__ offsets, int E, int thr, Ffn
 // 3*(f%10).  Eight consecutive fields span at most two words; they are
 // gathered into one 24-bit run first.  weight = scale * (field - 4), computed
 // exactly in fp32 as fma(field, s, -4s) and rounded once to the MFMA type.
+// 8 consecutive 3-bit fields (bits 3q..3q+2 of `bits`, q = 0..7) to MFMA
+// operand values scale * (field - 4): exact in fp32 as fma(field, s, -4s),
+// rounded once to fp16 (TO_F16) or bf16 (nearest even).
 template <bool TO_F16>
-__device__ __forceinline__ u32x4 q3_chunk(const uint32_t* __restrict__ wrow, const uint16_t* __restrict__ srow,
-                                          int k) {
-    const int g = k >> 7, f0 = k & 127;
-    const uint32_t* gw = wrow + g * Q3_WORDS;
-    const int wlo = f0 / 10, n0 = f0 - wlo * 10;
-    uint32_t bits = (gw[wlo] & 0x3FFFFFFFu) >> (3 * n0);   // bits 30-31 are not fields
-    if (n0 > 2) bits |= gw[wlo + 1] << (30 - 3 * n0);
-    const float s = (float)__builtin_bit_cast(_Float16, srow[g]);
+__device__ __forceinline__ u32x4 q3_decode8(uint32_t bits, uint32_t scale_bits) {
+    const float s = (float)__builtin_bit_cast(_Float16, (uint16_t)scale_bits);
     const float m4 = -4.0f * s;
     u32x4 r;
 #pragma unroll
@@ -140,7 +141,6 @@ __device__ __forceinline__ u32x4 q3_chunk(const uint32_t* __restrict__ wrow, con
             const _Float16 h0 = (_Float16)v0, h1 = (_Float16)v1;
             r[i] = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
         } else {
-            // round to nearest even bf16 (values are finite)
             uint32_t u0 = __float_as_uint(v0), u1 = __float_as_uint(v1);
             u0 += 0x7FFFu + ((u0 >> 16) & 1u);
             u1 += 0x7FFFu + ((u1 >> 16) & 1u);
@@ -148,6 +148,21 @@ __device__ __forceinline__ u32x4 q3_chunk(const uint32_t* __restrict__ wrow, con
         }
     }
     return r;
+}
+
+// 3-bit group decode: the 8 weights k..k+7 (k % 8 == 0) of one output row.
+// A group of 128 weights is 13 words; field f sits in word f/10 at bits
+// 3*(f%10).  Eight consecutive fields span at most two words; they are
+// gathered into one 24-bit run first.
+template <bool TO_F16>
+__device__ __forceinline__ u32x4 q3_chunk(const uint32_t* __restrict__ wrow, const uint16_t* __restrict__ srow,
+                                          int k) {
+    const int g = k >> 7, f0 = k & 127;
+    const uint32_t* gw = wrow + g * Q3_WORDS;
+    const int wlo = f0 / 10, n0 = f0 - wlo * 10;
+    uint32_t bits = (gw[wlo] & 0x3FFFFFFFu) >> (3 * n0);   // bits 30-31 are not fields
+    if (n0 > 2) bits |= gw[wlo + 1] << (30 - 3 * n0);
+    return q3_decode8<TO_F16>(bits, srow[g]);
 }
 
 // One weight row as seen by a loader: bf16 row pointer, or 3-bit words + scales.
@@ -194,167 +209,418 @@ __device__ __forceinline__ int logical_block() {
 
 // ------------------------------------------------------------ fat kernel
 
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// One 16-byte staging chunk of a weight row (8 weights k..k+7) on its way
+// from memory to the LDS tile: raw bf16, or the 3-bit words it is decoded
+// from.  `row` is the row index inside one expert's matrix of K columns.
+template <int WFMT, int PHASE>
+struct WStage;
+
+template <int PHASE>
+struct WStage<0, PHASE> {
+    u32x4 raw;
+    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t w, __amdgpu_buffer_rsrc_t, uint32_t row, int K,
+                                         int k) {
+        raw = __builtin_amdgcn_raw_buffer_load_b128(w, (row * (uint32_t)K + k) * 2u, 0, 0);
+    }
+    __device__ __forceinline__ u32x4 value(int) const { return PHASE == 2 ? bf16x8_to_f16x8(raw) : raw; }
+};
+
+template <int PHASE>
+struct WStage<1, PHASE> {
+    uint32_t w0, w1, sc;
+    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t w, __amdgpu_buffer_rsrc_t s, uint32_t row, int K,
+                                         int k) {
+        const uint32_t grp = row * (uint32_t)(K >> 7) + (k >> 7);
+        const int wl = (k & 127) / 10;
+        const uint32_t base = grp * (Q3_WORDS * 4);
+        w0 = __builtin_amdgcn_raw_buffer_load_b32(w, base + wl * 4, 0, 0);
+        w1 = __builtin_amdgcn_raw_buffer_load_b32(w, base + (wl + 1 < Q3_WORDS ? wl + 1 : Q3_WORDS - 1) * 4, 0, 0);
+        sc = __builtin_amdgcn_raw_buffer_load_b32(s, (grp * 2) & ~3u, 0, 0) >> ((grp & 1) * 16);
+    }
+    __device__ __forceinline__ u32x4 value(int k) const {
+        const int f = k & 127;
+        const int n0 = f - (f / 10) * 10;
+        uint32_t bits = (w0 & 0x3FFFFFFFu) >> (3 * n0);
+        if (n0 > 2) bits |= w1 << (30 - 3 * n0);
+        return q3_decode8<PHASE == 2>(bits, sc & 0xFFFFu);
+    }
+};
+
+// Fat-tile epilogue: two passes of 64 rows per wave through LDS, 16-byte row
+// stores (MFMA 32x32 output: lane holds column n, rows 8(r>>2) + 4g + (r&3)).
+// Phase 1 stores silu(gate) * up as fp16 activations, phase 2 fp16 y rows.
+template <int PHASE>
+__device__ __forceinline__ void fat_epilogue(const FfnArgs& a, const f32x16 (&acc)[4][4], const MTile& t, int nt,
+                                             int rtw, u32x4* smem) {
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform (SGPR)
+    const int wm = wave >> 1, wn = wave & 1;
+    const int n = lane & 31, g = lane >> 5;
+    const int N = PHASE == 1 ? a.I : a.H;
+    constexpr int BN = PHASE == 1 ? 128 : 256;
+    constexpr int OC = PHASE == 1 ? 64 : 128;           // output columns per wave
+    constexpr int LD = OC + 8;                          // staged row length (halves)
+    uint16_t* sO = reinterpret_cast<uint16_t*>(smem) + wave * 64 * LD;
+    uint16_t* dst = PHASE == 1 ? a.act : a.y;
+    const int col0 = nt * BN + wn * OC;
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int ri = pass * 2 + h;
+            if (ri < rtw) {
+#pragma unroll
+                for (int cj = 0; cj < (PHASE == 1 ? 2 : 4); ++cj)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int m = h * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+                        const float v = PHASE == 1 ? silu_mul(acc[ri][cj][r], acc[ri][cj + 2][r]) : acc[ri][cj][r];
+                        sO[m * LD + cj * 32 + n] = f32_to_f16_bits(v);
+                    }
+            }
+        }
+        __syncthreads();
+        constexpr int LPR = OC / 8;                     // lanes per staged row
+#pragma unroll
+        for (int it = 0; it < 64 * LPR / 64; ++it) {
+            const int m = it * (64 / LPR) + lane / LPR, ch = lane % LPR;
+            const int row = wm * 128 + pass * 64 + m;
+            if (row < t.rows)
+                stg16(dst + (size_t)(t.row0 + row) * N + col0 + ch * 8,
+                      *reinterpret_cast<const u32x4*>(sO + m * LD + ch * 8));
+        }
+        __syncthreads();
+    }
+}
+
+// Fat tile: 256 rows x 256 weight rows x 64 k per stage, 4 waves as 2 x 2,
+// each wave 128 rows x 128 weight rows = 4 x 4 MFMA 32x32x16 accumulators
+// (256 accumulator registers).  Both operands are staged through LDS with
+// coalesced 128-byte row loads (8 lanes per row, buffer loads against one
+// resource per matrix so every per-thread address is a 32-bit offset); the
+// next stage's loads are in flight in registers while the current one is
+// computed, LDS is double-buffered (2 x 64 KB), one barrier per stage.
+// Phase 1's 256 weight rows are 128 gate rows followed by the matching 128 up
+// rows; wave column wn takes gate rows 64 wn.. and up rows 128 + 64 wn.., so
+// each wave applies SwiGLU to its own accumulators.
 template <int PHASE, int WFMT>
 __global__ __launch_bounds__(FAT_THREADS, 1)
 void ffn_fat_kernel(FfnArgs a) {
-    __shared__ u32x4 smem[2 * FAT_STAGE];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    extern __shared__ u32x4 smem[];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (SGPR)
     const int wm = wave >> 1, wn = wave & 1;
+    const int n = lane & 31, g = lane >> 5;
     const int K = PHASE == 1 ? a.H : a.I;
-    const int NT = PHASE == 1 ? a.I / 128 : a.H / 256;
+    const int N = PHASE == 1 ? a.I : a.H;                 // outputs per row
+    constexpr int BN = PHASE == 1 ? 128 : 256;            // outputs per tile
+    const int NT = N / BN;
     const int n_mt = a.hdr->n_fat;
     const int n_items = n_mt * NT;
+    const int KT = K / 64;
+    // staging: thread t moves chunk c = t % 8 of rows t/8 + 32 i
     const int c = tid & 7, rb = tid >> 3;
-    const int swz = (rb >> 1) & 7;          // rows rb + 32 i share it
-    const int KT = K / FAT_BK;
-    // weight-row groups of this wave (two 64-row groups of the 256 staged)
-    const int bgrp0 = PHASE == 1 ? wn * 64 : wn * 128;
-    const int bgrp1 = PHASE == 1 ? 128 + wn * 64 : wn * 128 + 64;
+    const int swz = (rb >> 1) & 7;                        // rows rb + 32 i share it
+    // this wave's 4 weight-row groups of 32 inside the tile
+    const int bg0 = PHASE == 1 ? wn * 64 : wn * 128;
+    const int bg1 = PHASE == 1 ? 128 + wn * 64 : wn * 128 + 64;
+    // activation source: x (gathered rows) or the fp16 activation
+    const __amdgpu_buffer_rsrc_t asrc = PHASE == 1
+        ? make_rsrc(a.x, (uint32_t)(a.T * a.H * 2))
+        : make_rsrc(a.act, (uint32_t)((size_t)a.T * a.k * a.I * 2));
+    const size_t wmat = (size_t)a.I * a.H;                // weights per matrix per expert
+    const size_t wbytes = WFMT == 0 ? wmat * 2 : wmat / 128 * Q3_WORDS * 4;
+    const size_t sbytes = wmat / 128 * 2;
 
     for (int item = logical_block(); item < n_items; item += gridDim.x) {
         const int nt = item / n_mt, mt = item % n_mt;
         const MTile t = a.fat[mt];
-        const uint16_t* arow[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = rb + 32 * i;
-            arow[i] = nullptr;
-            if (r < t.rows) {
-                if (PHASE == 1) {
-                    const int tok = a.sorted_pair[t.row0 + r] / a.k;
-                    arow[i] = a.x + (size_t)tok * a.H;
-                } else {
-                    arow[i] = a.act + (size_t)(t.row0 + r) * a.I;
-                }
-            }
-        }
-        WRow brow[8];
+        const int rtw = max(0, min(4, (t.rows - wm * 128 + 31) >> 5));   // this wave's row tiles with data
+
+        // activation rows: byte offsets of 8 rows (rows past the tile repeat its
+        // last row; their results are never stored)
+        uint32_t aoff[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const int r = rb + 32 * i;
-            if (PHASE == 1) {
-                const int n = nt * 128 + (r & 127);
-                brow[i] = r < 128 ? weight_row<WFMT>(a.wg, a.sg, (size_t)t.e * a.I + n, K)
-                                  : weight_row<WFMT>(a.wu, a.su, (size_t)t.e * a.I + n, K);
-            } else {
-                brow[i] = weight_row<WFMT>(a.wd, a.sd, (size_t)t.e * a.H + nt * 256 + r, K);
-            }
+            const int r = min(rb + 32 * i, t.rows - 1);
+            const uint32_t src_row = PHASE == 1 ? (uint32_t)(a.sorted_pair[t.row0 + r] / a.k) : (uint32_t)(t.row0 + r);
+            aoff[i] = src_row * (uint32_t)K * 2u + c * 16;
         }
-        const bool act0 = wm * 64 < t.rows;        // this wave has rows to compute
-        const bool act1 = wm * 64 + 32 < t.rows;
+        // weight matrices of this expert
+        __amdgpu_buffer_rsrc_t wr0, wr1, sr0, sr1;
+        if (PHASE == 1) {
+            wr0 = make_rsrc((const char*)a.wg + t.e * wbytes, (uint32_t)wbytes);
+            wr1 = make_rsrc((const char*)a.wu + t.e * wbytes, (uint32_t)wbytes);
+            sr0 = make_rsrc(a.sg ? (const char*)a.sg + t.e * sbytes : nullptr, a.sg ? (uint32_t)sbytes : 0u);
+            sr1 = make_rsrc(a.su ? (const char*)a.su + t.e * sbytes : nullptr, a.su ? (uint32_t)sbytes : 0u);
+        } else {
+            wr0 = wr1 = make_rsrc((const char*)a.wd + t.e * wbytes, (uint32_t)wbytes);
+            sr0 = sr1 = make_rsrc(a.sd ? (const char*)a.sd + t.e * sbytes : nullptr, a.sd ? (uint32_t)sbytes : 0u);
+        }
+        const uint32_t brow0 = PHASE == 1 ? (uint32_t)(nt * 128 + rb) : (uint32_t)(nt * 256 + rb);
 
-        u32x4 ar[4], br[8];
-        auto gload = [&](int kt) {
-            const int off = kt * FAT_BK + c * 8;
+        u32x4 ast[8];
+        WStage<WFMT, PHASE> bst[8];
+        f32x16 acc[4][4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                ar[i] = u32x4{0, 0, 0, 0};
-                if (arow[i]) ar[i] = ldg16(arow[i] + off);
-            }
-#pragma unroll
-            for (int i = 0; i < 8; ++i) br[i] = load_w8<WFMT, PHASE>(brow[i], off);
-        };
-        auto sstore = [&](int stage) {
-            u32x4* sA = smem + stage * FAT_STAGE;
-            u32x4* sB = sA + FAT_BM * 8;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) sA[(rb + 32 * i) * 8 + (c ^ swz)] = ar[i];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) sB[(rb + 32 * i) * 8 + (c ^ swz)] = br[i];
-        };
-
-        f32x16 acc[2][4];
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
 
-        auto compute = [&](int stage) {
-            const u32x4* sA = smem + stage * FAT_STAGE;
+        auto gload = [&](int kt) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) ast[i] = __builtin_amdgcn_raw_buffer_load_b128(asrc, aoff[i], kt * 128, 0);
+            const int k = kt * 64 + c * 8;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                // phase 1: i < 4 are gate rows, i >= 4 the matching up rows
+                const uint32_t row = PHASE == 1 ? brow0 + 32 * (i & 3) : brow0 + 32 * i;
+                if (PHASE == 1 && i >= 4) bst[i].load(wr1, sr1, row, K, k);
+                else bst[i].load(wr0, sr0, row, K, k);
+            }
+        };
+        auto sstore = [&](int kt, int slot) {
+            u32x4* sA = smem + slot * FAT_STAGE;
+            u32x4* sB = sA + FAT_BM * 8;
+            const int k = kt * 64 + c * 8;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) sA[(rb + 32 * i) * 8 + (c ^ swz)] = ast[i];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) sB[(rb + 32 * i) * 8 + (c ^ swz)] = bst[i].value(k);
+        };
+        auto compute = [&](int slot, auto rt_c) {
+            constexpr int RT = decltype(rt_c)::value;           // row tiles with data (1..4)
+            const u32x4* sA = smem + slot * FAT_STAGE;
             const u32x4* sB = sA + FAT_BM * 8;
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
-                const int ch = 2 * s + (lane >> 5);
-                u32x4 af[2], bfr[4];
+                const int ch = 2 * s + g;
+                u32x4 af[4], bf[4];
 #pragma unroll
-                for (int ri = 0; ri < 2; ++ri) {
-                    const int ra = wm * 64 + ri * 32 + (lane & 31);
-                    af[ri] = sA[ra * 8 + (ch ^ ((ra >> 1) & 7))];
+                for (int ri = 0; ri < 4; ++ri) {
+                    const int r = wm * 128 + ri * 32 + n;
+                    af[ri] = sA[r * 8 + (ch ^ ((r >> 1) & 7))];
                 }
 #pragma unroll
                 for (int cj = 0; cj < 4; ++cj) {
-                    const int rw = ((cj >> 1) ? bgrp1 : bgrp0) + (cj & 1) * 32 + (lane & 31);
-                    bfr[cj] = sB[rw * 8 + (ch ^ ((rw >> 1) & 7))];
+                    const int r = ((cj >> 1) ? bg1 : bg0) + (cj & 1) * 32 + n;
+                    bf[cj] = sB[r * 8 + (ch ^ ((r >> 1) & 7))];
                 }
 #pragma unroll
-                for (int cj = 0; cj < 4; ++cj) {
-                    acc[0][cj] = mma<PHASE>(af[0], bfr[cj], acc[0][cj]);
-                    if (act1) acc[1][cj] = mma<PHASE>(af[1], bfr[cj], acc[1][cj]);
-                }
+                for (int ri = 0; ri < RT; ++ri)
+#pragma unroll
+                    for (int cj = 0; cj < 4; ++cj) acc[ri][cj] = mma<PHASE>(af[ri], bf[cj], acc[ri][cj]);
             }
         };
 
+        // one stage in flight in registers while the other is computed from LDS
         gload(0);
-        sstore(0);
+        sstore(0, 0);
         __syncthreads();
-        for (int kt = 0; kt < KT; ++kt) {
-            if (kt + 1 < KT) gload(kt + 1);
-            if (act0) compute(kt & 1);
-            if (kt + 1 < KT) sstore((kt + 1) & 1);
-            __syncthreads();
+        auto kloop = [&](auto rt_c) {
+            for (int kt = 0; kt < KT; ++kt) {
+                if (kt + 1 < KT) gload(kt + 1);
+                if (decltype(rt_c)::value > 0) compute(kt & 1, rt_c);
+                if (kt + 1 < KT) sstore(kt + 1, (kt + 1) & 1);
+                __syncthreads();
+            }
+        };
+        switch (rtw) {
+            case 4: kloop(std::integral_constant<int, 4>{}); break;
+            case 3: kloop(std::integral_constant<int, 3>{}); break;
+            case 2: kloop(std::integral_constant<int, 2>{}); break;
+            case 1: kloop(std::integral_constant<int, 1>{}); break;
+            default: kloop(std::integral_constant<int, 0>{}); break;
         }
 
-        // epilogue: registers -> LDS (fp16) -> 16-byte row stores
-        // MFMA 32x32 output layout: lane holds column (lane & 31) and rows
-        // 8*(r>>2) + 4*(lane>>5) + (r&3) for r = 0..15.
+        fat_epilogue<PHASE>(a, acc, t, nt, rtw, smem);
+    }
+}
+
+// ------------------------------------------------------------ fat kernel, bf16 weights
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)p; }
+
+// 16-byte LDS read issued as inline asm: the operand reads of the fat tile
+// must not wait on the direct-to-LDS loads of later stages that are still in
+// flight (the compiler would make every LDS read wait for all of them).
+template <int OFF>
+__device__ __forceinline__ u32x4 ds_read16(uint32_t addr) {
+    u32x4 v;
+    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF));
+    return v;
+}
+
+// Wait for this wave's outstanding LDS reads; the fragments are tied to the
+// wait so no use of them can be scheduled before it.
+__device__ __forceinline__ void lds_wait(u32x4 (&a)[4], u32x4 (&b)[4]) {
+    asm volatile("s_waitcnt lgkmcnt(0)"
+                 : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(b[0]), "+v"(b[1]), "+v"(b[2]), "+v"(b[3])
+                 :
+                 : "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+    asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+
+// Fat tile for bf16 weights: 256 rows x 256 weight rows, 4 waves as 2 x 2,
+// each wave 128 rows x 128 weight rows = 4 x 4 MFMA 32x32x16 accumulators.
+// Both operands stream into a ring of DMA_STAGES LDS stages of 32 k (16 KB of
+// activations + 16 KB of weights each) with direct-to-LDS buffer loads issued
+// DMA_STAGES - 1 stages ahead, so ~3 stages of loads are in flight without
+// holding any registers.  LDS rows are 64 bytes; the 16-byte chunk c of row r
+// sits at position c ^ ((r >> 2) & 3), which keeps each 16-lane phase of a
+// 16-byte fragment read on distinct banks.  A DMA instruction fills 1 KB of
+// consecutive LDS (lane L -> bytes 16 L), so lane L of block b loads row
+// 16 b + L / 4, chunk (L % 4) ^ swizzle.  One barrier per stage.
+template <int PHASE>
+__global__ __launch_bounds__(FAT_THREADS, 1)
+void ffn_fat_dma_kernel(FfnArgs a) {
+    extern __shared__ u32x4 smem[];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (SGPR)
+    const int wm = wave >> 1, wn = wave & 1;
+    const int n = lane & 31, g = lane >> 5;
+    const int K = PHASE == 1 ? a.H : a.I;
+    const int N = PHASE == 1 ? a.I : a.H;
+    constexpr int BN = PHASE == 1 ? 128 : 256;
+    const int NT = N / BN;
+    const int n_mt = a.hdr->n_fat;
+    const int n_items = n_mt * NT;
+    const int KT = K / 32;
+    const __amdgpu_buffer_rsrc_t asrc = PHASE == 1
+        ? make_rsrc(a.x, (uint32_t)(a.T * a.H * 2))
+        : make_rsrc(a.act, (uint32_t)((size_t)a.T * a.k * a.I * 2));
+    const size_t wbytes = (size_t)a.I * a.H * 2;
+    // DMA roles of this lane: LDS block b = 4 wave + q (q = 0..3) of each operand
+    // holds rows 16 b .. 16 b + 15; lane L writes row 16 b + L/4, position L%4
+    int dma_row[4], dma_ch[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        dma_row[q] = (wave * 4 + q) * 16 + (lane >> 2);
+        dma_ch[q] = (lane & 3) ^ ((dma_row[q] >> 2) & 3);
+    }
+    // fragment read addresses (bytes inside a stage): A row wm*128 + ri*32 + n,
+    // B rows of this wave's four 32-row groups; chunk 2s + g, swizzled by (n>>2)&3
+    const uint32_t sbase = lds_addr(smem);
+    const int sw = (n >> 2) & 3;
+    uint32_t aoffs[2], boffs[2][2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+        const uint32_t cpos = (uint32_t)(((2 * s + g) ^ sw) * 16);
+        aoffs[s] = (uint32_t)(wm * 128 + n) * 64 + cpos;
+        const int bg0 = PHASE == 1 ? wn * 64 : wn * 128;
+        const int bg1 = PHASE == 1 ? 128 + wn * 64 : wn * 128 + 64;
+        boffs[s][0] = DMA_A_BYTES + (uint32_t)(bg0 + n) * 64 + cpos;
+        boffs[s][1] = DMA_A_BYTES + (uint32_t)(bg1 + n) * 64 + cpos;
+    }
+
+    for (int item = logical_block(); item < n_items; item += gridDim.x) {
+        const int nt = item / n_mt, mt = item % n_mt;
+        const MTile t = a.fat[mt];
+        const int rtw = max(0, min(4, (t.rows - wm * 128 + 31) >> 5));
+
+        // per-lane byte offsets of the DMA sources (k = 0); rows past the tile
+        // repeat its last row (their results are never stored)
+        uint32_t aoff[4], boff[4];
+        __amdgpu_buffer_rsrc_t wsrc;
         if (PHASE == 1) {
-            constexpr int LD = 72;                               // halves per staged row
-            uint16_t* sO = reinterpret_cast<uint16_t*>(smem) + wave * 64 * LD;
-#pragma unroll
-            for (int ri = 0; ri < 2; ++ri)
-#pragma unroll
-                for (int cj = 0; cj < 2; ++cj)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int m = ri * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                        const int n = cj * 32 + (lane & 31);
-                        sO[m * LD + n] = f32_to_f16_bits(silu_mul(acc[ri][cj][r], acc[ri][cj + 2][r]));
-                    }
-            __syncthreads();
-            const int n0 = nt * 128 + wn * 64;
-#pragma unroll
-            for (int it = 0; it < 8; ++it) {
-                const int m = it * 8 + (lane >> 3), ch = lane & 7;
-                const int row = wm * 64 + m;
-                if (row < t.rows)
-                    stg16(a.act + (size_t)(t.row0 + row) * a.I + n0 + ch * 8,
-                          *reinterpret_cast<const u32x4*>(sO + m * LD + ch * 8));
-            }
+            // waves 0-1 load gate rows, waves 2-3 the matching up rows
+            wsrc = make_rsrc((const char*)(wave < 2 ? a.wg : a.wu) + t.e * wbytes, (uint32_t)wbytes);
         } else {
-            constexpr int LD = 136;
-            uint16_t* sO = reinterpret_cast<uint16_t*>(smem) + wave * 64 * LD;
+            wsrc = make_rsrc((const char*)a.wd + t.e * wbytes, (uint32_t)wbytes);
+        }
 #pragma unroll
-            for (int ri = 0; ri < 2; ++ri)
+        for (int q = 0; q < 4; ++q) {
+            const int r = min(dma_row[q], t.rows - 1);
+            const uint32_t src = PHASE == 1 ? (uint32_t)(a.sorted_pair[t.row0 + r] / a.k) : (uint32_t)(t.row0 + r);
+            aoff[q] = src * (uint32_t)K * 2u + dma_ch[q] * 16;
+            const uint32_t wrow = PHASE == 1 ? (uint32_t)(nt * 128 + (dma_row[q] & 127))
+                                             : (uint32_t)(nt * 256 + dma_row[q]);
+            boff[q] = wrow * (uint32_t)K * 2u + dma_ch[q] * 16;
+        }
+
+        f32x16 acc[4][4];
 #pragma unroll
-                for (int cj = 0; cj < 4; ++cj)
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int m = ri * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                        const int n = cj * 32 + (lane & 31);
-                        sO[m * LD + n] = f32_to_f16_bits(acc[ri][cj][r]);
-                    }
-            __syncthreads();
-            const int n0 = nt * 256 + wn * 128;
+            for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+
+        auto issue = [&](int kt) {
+            u32x4* st = smem + (kt % DMA_STAGES) * (DMA_STAGE_BYTES / 16);
 #pragma unroll
-            for (int it = 0; it < 16; ++it) {
-                const int m = it * 4 + (lane >> 4), ch = lane & 15;
-                const int row = wm * 64 + m;
-                if (row < t.rows)
-                    stg16(a.y + (size_t)(t.row0 + row) * a.H + n0 + ch * 8,
-                          *reinterpret_cast<const u32x4*>(sO + m * LD + ch * 8));
+            for (int q = 0; q < 4; ++q)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(asrc, (lds_ptr_t)(st + (wave * 4 + q) * 64), 16, aoff[q],
+                                                         kt * 64, 0, 0);
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(wsrc, (lds_ptr_t)(st + DMA_A_BYTES / 16 + (wave * 4 + q) * 64),
+                                                         16, boff[q], kt * 64, 0, 0);
+        };
+        auto compute = [&](int kt, auto rt_c) {
+            constexpr int RT = decltype(rt_c)::value;           // row tiles with data (1..4)
+            const uint32_t st = sbase + (kt % DMA_STAGES) * DMA_STAGE_BYTES;
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                u32x4 af[4], bf[4];
+                const uint32_t aa = st + aoffs[s], b0 = st + boffs[s][0], b1 = st + boffs[s][1];
+                af[0] = ds_read16<0>(aa);
+                af[1] = ds_read16<2048>(aa);
+                af[2] = ds_read16<4096>(aa);
+                af[3] = ds_read16<6144>(aa);
+                bf[0] = ds_read16<0>(b0);
+                bf[1] = ds_read16<2048>(b0);
+                bf[2] = ds_read16<0>(b1);
+                bf[3] = ds_read16<2048>(b1);
+                lds_wait(af, bf);
+                if (PHASE == 2) {
+#pragma unroll
+                    for (int cj = 0; cj < 4; ++cj) bf[cj] = bf16x8_to_f16x8(bf[cj]);
+                }
+#pragma unroll
+                for (int ri = 0; ri < RT; ++ri)
+#pragma unroll
+                    for (int cj = 0; cj < 4; ++cj) acc[ri][cj] = mma<PHASE>(af[ri], bf[cj], acc[ri][cj]);
             }
+        };
+
+        // prologue: stages 0 .. DMA_STAGES-2 in flight (8 loads per stage per lane)
+#pragma unroll
+        for (int p = 0; p < DMA_STAGES - 1; ++p)
+            if (p < KT) issue(p);
+        // the K loop, specialised on this wave's row-tile count so the MFMA
+        // accumulators stay in accumulator registers (no conditional MFMAs)
+        auto kloop = [&](auto rt_c) {
+            for (int kt = 0; kt < KT; ++kt) {
+                // stage kt has landed once at most the later stages' loads are pending
+                const int later = min(DMA_STAGES - 2, KT - 1 - kt);
+                if (later >= 2) vm_wait<16>();
+                else if (later == 1) vm_wait<8>();
+                else vm_wait<0>();
+                __builtin_amdgcn_s_barrier();
+                // the slot of stage kt-1 is free: every wave passed the barrier after reading it
+                if (kt + DMA_STAGES - 1 < KT) issue(kt + DMA_STAGES - 1);
+                if (decltype(rt_c)::value > 0) compute(kt, rt_c);
+            }
+        };
+        switch (rtw) {
+            case 4: kloop(std::integral_constant<int, 4>{}); break;
+            case 3: kloop(std::integral_constant<int, 3>{}); break;
+            case 2: kloop(std::integral_constant<int, 2>{}); break;
+            case 1: kloop(std::integral_constant<int, 1>{}); break;
+            default: kloop(std::integral_constant<int, 0>{}); break;
         }
         __syncthreads();
+
+        fat_epilogue<PHASE>(a, acc, t, nt, rtw, smem);
     }
 }
 
@@ -364,7 +630,8 @@ template <int PHASE, int WFMT>
 __global__ __launch_bounds__(THIN_THREADS)
 void ffn_thin_kernel(FfnArgs a) {
     __shared__ float red[4][16][64];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform (SGPR)
     const int m = lane & 31, g = lane >> 5;
     const int K = PHASE == 1 ? a.H : a.I;
     const int NT = PHASE == 1 ? a.I / 16 : a.H / 32;
@@ -492,6 +759,13 @@ hipError_t dev_info(DevInfo& out) {
         int cus = 0;
         err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
         if (err != hipSuccess) return err;
+        // the fat kernels use 128 KB of dynamic LDS (more than the default cap)
+        const void* fats[4] = {(const void*)ffn_fat_dma_kernel<1>, (const void*)ffn_fat_dma_kernel<2>,
+                               (const void*)ffn_fat_kernel<1, 1>, (const void*)ffn_fat_kernel<2, 1>};
+        for (const void* f : fats) {
+            err = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)FAT_LDS_BYTES);
+            if (err != hipSuccess) return err;
+        }
         d.thin_blocks[0][0] = thin_occupancy<1, 0>();
         d.thin_blocks[0][1] = thin_occupancy<2, 0>();
         d.thin_blocks[1][0] = thin_occupancy<1, 1>();
@@ -510,7 +784,7 @@ FfnArgs make_args(const FfnLaunch& a) {
     fa.wg = a.wg; fa.wu = a.wu; fa.wd = a.wd;
     fa.sg = a.sg; fa.su = a.su; fa.sd = a.sd;
     fa.sorted_pair = a.sorted_pair;
-    fa.k = a.k; fa.H = a.H; fa.I = a.I;
+    fa.T = a.T; fa.k = a.k; fa.H = a.H; fa.I = a.I;
     fa.act = reinterpret_cast<uint16_t*>(ws + L.act);
     fa.y = a.y;
     fa.hdr = reinterpret_cast<FfnHeader*>(ws + L.hdr);
@@ -521,7 +795,8 @@ FfnArgs make_args(const FfnLaunch& a) {
 
 template <int PHASE, int WFMT>
 void launch_phase_t(const FfnArgs& fa, const DevInfo& d, hipStream_t s) {
-    ffn_fat_kernel<PHASE, WFMT><<<d.cus, FAT_THREADS, 0, s>>>(fa);
+    if (WFMT == 0) ffn_fat_dma_kernel<PHASE><<<d.cus, FAT_THREADS, FAT_LDS_BYTES, s>>>(fa);
+    else ffn_fat_kernel<PHASE, WFMT><<<d.cus, FAT_THREADS, FAT_LDS_BYTES, s>>>(fa);
     ffn_thin_kernel<PHASE, WFMT><<<d.cus * d.thin_blocks[WFMT][PHASE - 1], THIN_THREADS, 0, s>>>(fa);
 }
 
