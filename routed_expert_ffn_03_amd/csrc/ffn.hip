@@ -46,8 +46,10 @@
 namespace moe {
 namespace {
 
+// One M-tile of an expert's route list: rows [row0, row0 + rows) of the
+// sorted pairs; `first` / `count` locate all M-tiles of the same expert.
 struct MTile {
-    int32_t e, row0, rows, pad;
+    int32_t e, row0, rows, first, count, pad[3];
 };
 
 struct FfnHeader {
@@ -103,13 +105,15 @@ void build_tiles_kernel(const int32_t* __restrict__ offsets, int E, int thr, Ffn
     const int fi = block_inclusive_scan(nf, scratch);
     const int ti = block_inclusive_scan(nt, scratch);
     for (int i = 0; i < nf; ++i) {
-        MTile m;
-        m.e = e; m.row0 = r0 + i * FAT_BM; m.rows = min(FAT_BM, n - i * FAT_BM); m.pad = 0;
+        MTile m = {};
+        m.e = e; m.row0 = r0 + i * FAT_BM; m.rows = min(FAT_BM, n - i * FAT_BM);
+        m.first = fi - nf; m.count = nf;
         fat[fi - nf + i] = m;
     }
     for (int i = 0; i < nt; ++i) {
-        MTile m;
-        m.e = e; m.row0 = r0 + i * THIN_BM; m.rows = min(THIN_BM, n - i * THIN_BM); m.pad = 0;
+        MTile m = {};
+        m.e = e; m.row0 = r0 + i * THIN_BM; m.rows = min(THIN_BM, n - i * THIN_BM);
+        m.first = ti - nt; m.count = nt;
         thin[ti - nt + i] = m;
     }
     if (e == (int)blockDim.x - 1) {
@@ -250,6 +254,26 @@ struct WStage<1, PHASE> {
     }
 };
 
+// Fat work item -> (M-tile, N-tile).  The items of one expert (count M-tiles
+// x NT N-tiles) are contiguous and walked in super-tiles of gm M-tiles x gn
+// N-tiles (gm * gn = 32, gm <= 8): blocks on one XCD take 32 consecutive
+// items, so the activation rows of gm M-tiles and the weight tiles of gn
+// N-tiles are each fetched once into that XCD's L2 and shared.
+__device__ __forceinline__ void fat_item(const MTile* __restrict__ fat, int item, int NT, MTile& t, int& nt) {
+    const int q = item / NT;
+    const MTile t0 = fat[q];
+    const int me = t0.count, local = item - t0.first * NT;
+    int gm = 1;
+    while (gm * 2 <= min(me, 8)) gm *= 2;
+    const int gn = min(NT, 32 / gm);
+    const int mb = local / (gm * NT), rem = local - mb * gm * NT;
+    const int gmr = min(gm, me - mb * gm);
+    const int nb = rem / (gmr * gn), r = rem - nb * gmr * gn;
+    const int gnr = min(gn, NT - nb * gn);
+    t = fat[t0.first + mb * gm + r / gnr];
+    nt = nb * gn + r % gnr;
+}
+
 // Fat-tile epilogue: two passes of 64 rows per wave through LDS, 16-byte row
 // stores (MFMA 32x32 output: lane holds column n, rows 8(r>>2) + 4g + (r&3)).
 // Phase 1 stores silu(gate) * up as fp16 activations, phase 2 fp16 y rows.
@@ -337,8 +361,9 @@ void ffn_fat_kernel(FfnArgs a) {
     const size_t sbytes = wmat / 128 * 2;
 
     for (int item = logical_block(); item < n_items; item += gridDim.x) {
-        const int nt = item / n_mt, mt = item % n_mt;
-        const MTile t = a.fat[mt];
+        MTile t;
+        int nt;
+        fat_item(a.fat, item, NT, t, nt);
         const int rtw = max(0, min(4, (t.rows - wm * 128 + 31) >> 5));   // this wave's row tiles with data
 
         // activation rows: byte offsets of 8 rows (rows past the tile repeat its
@@ -524,8 +549,9 @@ void ffn_fat_dma_kernel(FfnArgs a) {
     }
 
     for (int item = logical_block(); item < n_items; item += gridDim.x) {
-        const int nt = item / n_mt, mt = item % n_mt;
-        const MTile t = a.fat[mt];
+        MTile t;
+        int nt;
+        fat_item(a.fat, item, NT, t, nt);
         const int rtw = max(0, min(4, (t.rows - wm * 128 + 31) >> 5));
 
         // per-lane byte offsets of the DMA sources (k = 0); rows past the tile
@@ -565,50 +591,87 @@ void ffn_fat_dma_kernel(FfnArgs a) {
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(wsrc, (lds_ptr_t)(st + DMA_A_BYTES / 16 + (wave * 4 + q) * 64),
                                                          16, boff[q], kt * 64, 0, 0);
         };
-        auto compute = [&](int kt, auto rt_c) {
-            constexpr int RT = decltype(rt_c)::value;           // row tiles with data (1..4)
+        // fragment reads of one 16-k sub-step s of stage kt (8 x 16 bytes)
+        auto reads = [&](int kt, int s, u32x4 (&af)[4], u32x4 (&bf)[4]) {
             const uint32_t st = sbase + (kt % DMA_STAGES) * DMA_STAGE_BYTES;
+            const uint32_t aa = st + aoffs[s], b0 = st + boffs[s][0], b1 = st + boffs[s][1];
+            af[0] = ds_read16<0>(aa);
+            af[1] = ds_read16<2048>(aa);
+            af[2] = ds_read16<4096>(aa);
+            af[3] = ds_read16<6144>(aa);
+            bf[0] = ds_read16<0>(b0);
+            bf[1] = ds_read16<2048>(b0);
+            bf[2] = ds_read16<0>(b1);
+            bf[3] = ds_read16<2048>(b1);
+        };
+        auto ready = [&](u32x4 (&af)[4], u32x4 (&bf)[4]) {
+            lds_wait(af, bf);
+            if (PHASE == 2) {
 #pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                u32x4 af[4], bf[4];
-                const uint32_t aa = st + aoffs[s], b0 = st + boffs[s][0], b1 = st + boffs[s][1];
-                af[0] = ds_read16<0>(aa);
-                af[1] = ds_read16<2048>(aa);
-                af[2] = ds_read16<4096>(aa);
-                af[3] = ds_read16<6144>(aa);
-                bf[0] = ds_read16<0>(b0);
-                bf[1] = ds_read16<2048>(b0);
-                bf[2] = ds_read16<0>(b1);
-                bf[3] = ds_read16<2048>(b1);
-                lds_wait(af, bf);
-                if (PHASE == 2) {
-#pragma unroll
-                    for (int cj = 0; cj < 4; ++cj) bf[cj] = bf16x8_to_f16x8(bf[cj]);
-                }
-#pragma unroll
-                for (int ri = 0; ri < RT; ++ri)
-#pragma unroll
-                    for (int cj = 0; cj < 4; ++cj) acc[ri][cj] = mma<PHASE>(af[ri], bf[cj], acc[ri][cj]);
+                for (int cj = 0; cj < 4; ++cj) bf[cj] = bf16x8_to_f16x8(bf[cj]);
             }
         };
-
-        // prologue: stages 0 .. DMA_STAGES-2 in flight (8 loads per stage per lane)
+        // MFMAs of row tiles [R0, R1) x all 4 column tiles
+        auto mfmas = [&](auto rt_c, auto r0_c, auto r1_c, const u32x4 (&af)[4], const u32x4 (&bf)[4]) {
+            constexpr int RT = decltype(rt_c)::value, R0 = decltype(r0_c)::value, R1 = decltype(r1_c)::value;
 #pragma unroll
-        for (int p = 0; p < DMA_STAGES - 1; ++p)
+            for (int ri = R0; ri < (R1 < RT ? R1 : RT); ++ri)
+#pragma unroll
+                for (int cj = 0; cj < 4; ++cj) acc[ri][cj] = mma<PHASE>(af[ri], bf[cj], acc[ri][cj]);
+        };
+        // stage kt+1 has landed once at most the stages after it are pending
+        auto wait_next = [&](int kt) {
+            const int later = min(2, KT - 2 - kt);
+            if (later >= 2) vm_wait<16>();
+            else if (later == 1) vm_wait<8>();
+            else vm_wait<0>();
+        };
+
+        // prologue: stages 0..3 in flight, wait for stage 0
+#pragma unroll
+        for (int p = 0; p < DMA_STAGES; ++p)
             if (p < KT) issue(p);
-        // the K loop, specialised on this wave's row-tile count so the MFMA
-        // accumulators stay in accumulator registers (no conditional MFMAs)
+        {
+            const int later = min(DMA_STAGES - 1, KT - 1);
+            if (later >= 3) vm_wait<24>();
+            else if (later == 2) vm_wait<16>();
+            else if (later == 1) vm_wait<8>();
+            else vm_wait<0>();
+        }
+        __builtin_amdgcn_s_barrier();
+
+        // K loop: the barrier for stage kt+1 and every LDS read sit between
+        // independent MFMA groups, so the MFMA pipe is not drained by them.
+        // Slot kt is refilled (stage kt+4) right after that barrier: every
+        // wave has finished reading it by then.
         auto kloop = [&](auto rt_c) {
+            using Z = std::integral_constant<int, 0>;
+            using H = std::integral_constant<int, 2>;
+            using F = std::integral_constant<int, 4>;
+            u32x4 a0[4], b0[4], a1[4], b1[4];
+            reads(0, 0, a0, b0);
             for (int kt = 0; kt < KT; ++kt) {
-                // stage kt has landed once at most the later stages' loads are pending
-                const int later = min(DMA_STAGES - 2, KT - 1 - kt);
-                if (later >= 2) vm_wait<16>();
-                else if (later == 1) vm_wait<8>();
-                else vm_wait<0>();
-                __builtin_amdgcn_s_barrier();
-                // the slot of stage kt-1 is free: every wave passed the barrier after reading it
-                if (kt + DMA_STAGES - 1 < KT) issue(kt + DMA_STAGES - 1);
-                if (decltype(rt_c)::value > 0) compute(kt, rt_c);
+                ready(a0, b0);
+                __builtin_amdgcn_sched_barrier(0);
+                mfmas(rt_c, Z{}, H{}, a0, b0);
+                __builtin_amdgcn_sched_barrier(0);
+                reads(kt, 1, a1, b1);
+                __builtin_amdgcn_sched_barrier(0);
+                mfmas(rt_c, H{}, F{}, a0, b0);
+                __builtin_amdgcn_sched_barrier(0);
+                ready(a1, b1);
+                if (kt + 1 < KT) {
+                    wait_next(kt);
+                    __builtin_amdgcn_s_barrier();
+                }
+                if (kt + DMA_STAGES < KT) issue(kt + DMA_STAGES);
+                __builtin_amdgcn_sched_barrier(0);
+                mfmas(rt_c, Z{}, H{}, a1, b1);
+                __builtin_amdgcn_sched_barrier(0);
+                if (kt + 1 < KT) reads(kt + 1, 0, a0, b0);
+                __builtin_amdgcn_sched_barrier(0);
+                mfmas(rt_c, H{}, F{}, a1, b1);
+                __builtin_amdgcn_sched_barrier(0);
             }
         };
         switch (rtw) {
