@@ -61,10 +61,9 @@ constexpr int FAT_BM = 256;              // rows per fat M-tile
 constexpr int FAT_THREADS = 256;
 constexpr int FAT_STAGE = (FAT_BM + 256) * 8;            // 16-byte chunks per LDS stage (A + B)
 constexpr size_t FAT_LDS_BYTES = 2 * FAT_STAGE * 16;     // 128 KB: double-buffered stages / epilogue
-constexpr int DMA_STAGES = 4;                            // LDS ring of the bf16 fat kernel
-constexpr uint32_t DMA_A_BYTES = 256 * 64;               // activations of one 32-k stage
-constexpr uint32_t DMA_STAGE_BYTES = 2 * DMA_A_BYTES;    // + the same for weights
-static_assert(DMA_STAGES * DMA_STAGE_BYTES <= FAT_LDS_BYTES, "LDS ring too large");
+constexpr uint32_t DMA_A_BYTES = 256 * 128;              // activations of one 64-k stage
+constexpr uint32_t DMA_STAGE_BYTES = 2 * DMA_A_BYTES;     // + the same for weights
+static_assert(2 * DMA_STAGE_BYTES <= FAT_LDS_BYTES, "LDS stages too large");
 constexpr int THIN_BM = 32;
 constexpr int THIN_THREADS = 256;
 constexpr int THIN_DEPTH = 4;             // chunks in flight per lane
@@ -498,14 +497,16 @@ __device__ __forceinline__ void vm_wait() {
 
 // Fat tile for bf16 weights: 256 rows x 256 weight rows, 4 waves as 2 x 2,
 // each wave 128 rows x 128 weight rows = 4 x 4 MFMA 32x32x16 accumulators.
-// Both operands stream into a ring of DMA_STAGES LDS stages of 32 k (16 KB of
-// activations + 16 KB of weights each) with direct-to-LDS buffer loads issued
-// DMA_STAGES - 1 stages ahead, so ~3 stages of loads are in flight without
-// holding any registers.  LDS rows are 64 bytes; the 16-byte chunk c of row r
-// sits at position c ^ ((r >> 2) & 3), which keeps each 16-lane phase of a
-// 16-byte fragment read on distinct banks.  A DMA instruction fills 1 KB of
-// consecutive LDS (lane L -> bytes 16 L), so lane L of block b loads row
-// 16 b + L / 4, chunk (L % 4) ^ swizzle.  One barrier per stage.
+// Both operands stream into two LDS stages of 64 k (32 KB of activations +
+// 32 KB of weights each) with direct-to-LDS buffer loads: every load
+// instruction reads 8 rows x 128 bytes (whole cache lines), the next stage is
+// in flight while the current one is computed, and no register holds staged
+// data.  LDS rows are 128 bytes; the 16-byte chunk c of row r sits at
+// position c ^ ((r >> 1) & 7), which keeps each 16-lane phase of a fragment
+// read on distinct banks.  A load instruction fills 1 KB of consecutive LDS
+// (lane L -> bytes 16 L), so lane L of block b loads row 8 b + L / 8, chunk
+// (L % 8) ^ swizzle.  The stage barrier and every LDS read are placed between
+// independent MFMA groups.
 template <int PHASE>
 __global__ __launch_bounds__(FAT_THREADS, 1)
 void ffn_fat_dma_kernel(FfnArgs a) {
@@ -520,32 +521,27 @@ void ffn_fat_dma_kernel(FfnArgs a) {
     const int NT = N / BN;
     const int n_mt = a.hdr->n_fat;
     const int n_items = n_mt * NT;
-    const int KT = K / 32;
+    const int KT = K / 64;
     const __amdgpu_buffer_rsrc_t asrc = PHASE == 1
         ? make_rsrc(a.x, (uint32_t)(a.T * a.H * 2))
         : make_rsrc(a.act, (uint32_t)((size_t)a.T * a.k * a.I * 2));
     const size_t wbytes = (size_t)a.I * a.H * 2;
-    // DMA roles of this lane: LDS block b = 4 wave + q (q = 0..3) of each operand
-    // holds rows 16 b .. 16 b + 15; lane L writes row 16 b + L/4, position L%4
-    int dma_row[4], dma_ch[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        dma_row[q] = (wave * 4 + q) * 16 + (lane >> 2);
-        dma_ch[q] = (lane & 3) ^ ((dma_row[q] >> 2) & 3);
-    }
+    // load roles of this lane: blocks 8 wave + q (q = 0..7) of each operand,
+    // row 8 (8 wave + q) + L/8 = 64 wave + 8 q + L/8, chunk (L%8) ^ swizzle
+    const int lrow = 64 * wave + (lane >> 3);             // + 8 q
     // fragment read addresses (bytes inside a stage): A row wm*128 + ri*32 + n,
-    // B rows of this wave's four 32-row groups; chunk 2s + g, swizzled by (n>>2)&3
+    // B rows of this wave's four 32-row groups; chunk 2s + g, swizzled by (n>>1)&7
     const uint32_t sbase = lds_addr(smem);
-    const int sw = (n >> 2) & 3;
-    uint32_t aoffs[2], boffs[2][2];
+    const int sw = (n >> 1) & 7;
+    const int bg0 = PHASE == 1 ? wn * 64 : wn * 128;
+    const int bg1 = PHASE == 1 ? 128 + wn * 64 : wn * 128 + 64;
+    uint32_t aoffs[4], boffs[4][2];
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
+    for (int s = 0; s < 4; ++s) {
         const uint32_t cpos = (uint32_t)(((2 * s + g) ^ sw) * 16);
-        aoffs[s] = (uint32_t)(wm * 128 + n) * 64 + cpos;
-        const int bg0 = PHASE == 1 ? wn * 64 : wn * 128;
-        const int bg1 = PHASE == 1 ? 128 + wn * 64 : wn * 128 + 64;
-        boffs[s][0] = DMA_A_BYTES + (uint32_t)(bg0 + n) * 64 + cpos;
-        boffs[s][1] = DMA_A_BYTES + (uint32_t)(bg1 + n) * 64 + cpos;
+        aoffs[s] = (uint32_t)(wm * 128 + n) * 128 + cpos;
+        boffs[s][0] = DMA_A_BYTES + (uint32_t)(bg0 + n) * 128 + cpos;
+        boffs[s][1] = DMA_A_BYTES + (uint32_t)(bg1 + n) * 128 + cpos;
     }
 
     for (int item = logical_block(); item < n_items; item += gridDim.x) {
@@ -554,9 +550,9 @@ void ffn_fat_dma_kernel(FfnArgs a) {
         fat_item(a.fat, item, NT, t, nt);
         const int rtw = max(0, min(4, (t.rows - wm * 128 + 31) >> 5));
 
-        // per-lane byte offsets of the DMA sources (k = 0); rows past the tile
+        // per-lane byte offsets of the load sources (k = 0); rows past the tile
         // repeat its last row (their results are never stored)
-        uint32_t aoff[4], boff[4];
+        uint32_t aoff[8], boff[8];
         __amdgpu_buffer_rsrc_t wsrc;
         if (PHASE == 1) {
             // waves 0-1 load gate rows, waves 2-3 the matching up rows
@@ -565,13 +561,14 @@ void ffn_fat_dma_kernel(FfnArgs a) {
             wsrc = make_rsrc((const char*)a.wd + t.e * wbytes, (uint32_t)wbytes);
         }
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int r = min(dma_row[q], t.rows - 1);
+        for (int q = 0; q < 8; ++q) {
+            const int row = lrow + 8 * q;
+            const int lch = (lane & 7) ^ ((row >> 1) & 7);   // global chunk landing at position L%8
+            const int r = min(row, t.rows - 1);
             const uint32_t src = PHASE == 1 ? (uint32_t)(a.sorted_pair[t.row0 + r] / a.k) : (uint32_t)(t.row0 + r);
-            aoff[q] = src * (uint32_t)K * 2u + dma_ch[q] * 16;
-            const uint32_t wrow = PHASE == 1 ? (uint32_t)(nt * 128 + (dma_row[q] & 127))
-                                             : (uint32_t)(nt * 256 + dma_row[q]);
-            boff[q] = wrow * (uint32_t)K * 2u + dma_ch[q] * 16;
+            aoff[q] = src * (uint32_t)K * 2u + lch * 16;
+            const uint32_t wrow = PHASE == 1 ? (uint32_t)(nt * 128 + (row & 127)) : (uint32_t)(nt * 256 + row);
+            boff[q] = wrow * (uint32_t)K * 2u + lch * 16;
         }
 
         f32x16 acc[4][4];
@@ -581,28 +578,28 @@ void ffn_fat_dma_kernel(FfnArgs a) {
             for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
 
         auto issue = [&](int kt) {
-            u32x4* st = smem + (kt % DMA_STAGES) * (DMA_STAGE_BYTES / 16);
+            u32x4* st = smem + (kt & 1) * (DMA_STAGE_BYTES / 16);
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(asrc, (lds_ptr_t)(st + (wave * 4 + q) * 64), 16, aoff[q],
-                                                         kt * 64, 0, 0);
+            for (int q = 0; q < 8; ++q)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(asrc, (lds_ptr_t)(st + (8 * wave + q) * 64), 16, aoff[q],
+                                                         kt * 128, 0, 0);
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(wsrc, (lds_ptr_t)(st + DMA_A_BYTES / 16 + (wave * 4 + q) * 64),
-                                                         16, boff[q], kt * 64, 0, 0);
+            for (int q = 0; q < 8; ++q)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(wsrc, (lds_ptr_t)(st + DMA_A_BYTES / 16 + (8 * wave + q) * 64),
+                                                         16, boff[q], kt * 128, 0, 0);
         };
         // fragment reads of one 16-k sub-step s of stage kt (8 x 16 bytes)
         auto reads = [&](int kt, int s, u32x4 (&af)[4], u32x4 (&bf)[4]) {
-            const uint32_t st = sbase + (kt % DMA_STAGES) * DMA_STAGE_BYTES;
+            const uint32_t st = sbase + (kt & 1) * DMA_STAGE_BYTES;
             const uint32_t aa = st + aoffs[s], b0 = st + boffs[s][0], b1 = st + boffs[s][1];
             af[0] = ds_read16<0>(aa);
-            af[1] = ds_read16<2048>(aa);
-            af[2] = ds_read16<4096>(aa);
-            af[3] = ds_read16<6144>(aa);
+            af[1] = ds_read16<4096>(aa);
+            af[2] = ds_read16<8192>(aa);
+            af[3] = ds_read16<12288>(aa);
             bf[0] = ds_read16<0>(b0);
-            bf[1] = ds_read16<2048>(b0);
+            bf[1] = ds_read16<4096>(b0);
             bf[2] = ds_read16<0>(b1);
-            bf[3] = ds_read16<2048>(b1);
+            bf[3] = ds_read16<4096>(b1);
         };
         auto ready = [&](u32x4 (&af)[4], u32x4 (&bf)[4]) {
             lds_wait(af, bf);
@@ -619,59 +616,47 @@ void ffn_fat_dma_kernel(FfnArgs a) {
 #pragma unroll
                 for (int cj = 0; cj < 4; ++cj) acc[ri][cj] = mma<PHASE>(af[ri], bf[cj], acc[ri][cj]);
         };
-        // stage kt+1 has landed once at most the stages after it are pending
-        auto wait_next = [&](int kt) {
-            const int later = min(2, KT - 2 - kt);
-            if (later >= 2) vm_wait<16>();
-            else if (later == 1) vm_wait<8>();
-            else vm_wait<0>();
-        };
 
-        // prologue: stages 0..3 in flight, wait for stage 0
-#pragma unroll
-        for (int p = 0; p < DMA_STAGES; ++p)
-            if (p < KT) issue(p);
-        {
-            const int later = min(DMA_STAGES - 1, KT - 1);
-            if (later >= 3) vm_wait<24>();
-            else if (later == 2) vm_wait<16>();
-            else if (later == 1) vm_wait<8>();
-            else vm_wait<0>();
+        // prologue: stages 0 and 1 in flight, wait for stage 0
+        issue(0);
+        if (KT > 1) {
+            issue(1);
+            vm_wait<16>();
+        } else {
+            vm_wait<0>();
         }
         __builtin_amdgcn_s_barrier();
 
-        // K loop: the barrier for stage kt+1 and every LDS read sit between
-        // independent MFMA groups, so the MFMA pipe is not drained by them.
-        // Slot kt is refilled (stage kt+4) right after that barrier: every
-        // wave has finished reading it by then.
         auto kloop = [&](auto rt_c) {
             using Z = std::integral_constant<int, 0>;
             using H = std::integral_constant<int, 2>;
             using F = std::integral_constant<int, 4>;
-            u32x4 a0[4], b0[4], a1[4], b1[4];
-            reads(0, 0, a0, b0);
+            u32x4 x0[4], y0[4], x1[4], y1[4];
+            reads(0, 0, x0, y0);
             for (int kt = 0; kt < KT; ++kt) {
-                ready(a0, b0);
-                __builtin_amdgcn_sched_barrier(0);
-                mfmas(rt_c, Z{}, H{}, a0, b0);
-                __builtin_amdgcn_sched_barrier(0);
-                reads(kt, 1, a1, b1);
-                __builtin_amdgcn_sched_barrier(0);
-                mfmas(rt_c, H{}, F{}, a0, b0);
-                __builtin_amdgcn_sched_barrier(0);
-                ready(a1, b1);
-                if (kt + 1 < KT) {
-                    wait_next(kt);
-                    __builtin_amdgcn_s_barrier();
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    u32x4 (&ca)[4] = (s & 1) ? x1 : x0;
+                    u32x4 (&cb)[4] = (s & 1) ? y1 : y0;
+                    u32x4 (&na)[4] = (s & 1) ? x0 : x1;
+                    u32x4 (&nb)[4] = (s & 1) ? y0 : y1;
+                    ready(ca, cb);
+                    __builtin_amdgcn_sched_barrier(0);
+                    mfmas(rt_c, Z{}, H{}, ca, cb);
+                    __builtin_amdgcn_sched_barrier(0);
+                    if (s < 3) {
+                        reads(kt, s + 1, na, nb);
+                    } else if (kt + 1 < KT) {
+                        // end of stage kt: every wave has read all of it
+                        vm_wait<0>();                        // stage kt+1 landed (this lane's loads)
+                        __builtin_amdgcn_s_barrier();        // ... and every other lane's
+                        if (kt + 2 < KT) issue(kt + 2);      // refill the slot of stage kt
+                        reads(kt + 1, 0, na, nb);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                    mfmas(rt_c, H{}, F{}, ca, cb);
+                    __builtin_amdgcn_sched_barrier(0);
                 }
-                if (kt + DMA_STAGES < KT) issue(kt + DMA_STAGES);
-                __builtin_amdgcn_sched_barrier(0);
-                mfmas(rt_c, Z{}, H{}, a1, b1);
-                __builtin_amdgcn_sched_barrier(0);
-                if (kt + 1 < KT) reads(kt + 1, 0, a0, b0);
-                __builtin_amdgcn_sched_barrier(0);
-                mfmas(rt_c, H{}, F{}, a1, b1);
-                __builtin_amdgcn_sched_barrier(0);
             }
         };
         switch (rtw) {
