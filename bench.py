@@ -27,6 +27,30 @@ PEAK_MFMA_TFLOPS = {"bf16": 2500.0, "fp16": 2500.0}      # dense, MI355X publish
 PEAK_HBM_GBS = 8000.0
 
 
+def ffn_source_hash() -> str:
+    import hashlib
+    src = os.path.join(ROOT, "routed_expert_ffn_03_amd", "csrc", "ffn.hip")
+    return hashlib.sha256(open(src, "rb").read()).hexdigest()[:12]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch of the gate/up phase from the committed counter
+    summary (profiles/hbm_traffic.md), or None when it was measured on a
+    different version of the kernel source."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.md")
+    if not os.path.exists(path):
+        return None
+    want = ffn_source_hash()
+    for line in open(path):
+        cells = [c.strip() for c in line.strip().strip("|").split("|")]
+        if len(cells) >= 6 and cells[0] == workload and cells[1] == "gate/up" and cells[2] == want:
+            try:
+                return float(cells[3]) + float(cells[4])
+            except ValueError:
+                return None
+    return None
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -41,7 +65,7 @@ def parse():
     p.add_argument("--decode-steps", type=int, default=200, help="steps of the secondary decode measurement")
     p.add_argument("--no-decode", action="store_true", help="skip the secondary decode measurement")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-sample", type=int, default=8, help="tokens of the batch the oracle is timed on")
+    p.add_argument("--cpu-sample", type=int, default=128, help="tokens of the batch the oracle is timed on")
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--fat-threshold", type=int, default=32)
     p.add_argument("--copy-calibration", action="store_true",
@@ -128,8 +152,9 @@ class Runner:
             r = {"bound": "hbm", "achieved": wbytes_gate_up / t / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
             per = f"{2 * s.I * s.H * 2} gate+up weight bytes per touched expert x {touched} experts"
         r["frac"] = r["achieved"] / r["peak"]
-        r["traffic"] = None
-        r["kernel"] = "gate/up phase (ffn_fat_kernel<1> + ffn_thin_kernel<1>)"
+        r["traffic"] = measured_traffic(s.name)
+        fat_name = "ffn_fat_dma_kernel<1>" if s.wfmt == "bf16" else "ffn_fat_kernel<1, 1>"
+        r["kernel"] = f"gate/up phase ({fat_name} + ffn_thin_kernel<1, {0 if s.wfmt == 'bf16' else 1}>)"
         r["kernel_ms"] = gate_up_ms
         r["algorithmic"] = per
         r["experts_touched"] = touched

@@ -18,15 +18,14 @@
 //                 epilogue; the activation a is stored fp16 [P, I].
 //   phase 2       down: fat kernel, then thin kernel; y stored fp16 [P, H].
 //
-// Fat kernel (MFMA-bound at large M): persistent, one 256-thread block per CU,
-// work item = (N-tile, M-tile) with the M-tile index fastest so consecutive
-// items share one expert weight tile; items are spread so each XCD walks a
-// contiguous range of them (its own L2 sees the shared weight tile).  Tile
-// 128 rows x 256 weight rows x 64 k, double-buffered in LDS (96 KB) with an
-// XOR swizzle that keeps 16-byte reads conflict-free; each wave owns 64 rows
-// x 128 weight rows = 2 x 4 MFMA 32x32x16 accumulators.  Phase 1's 256
-// weight rows are 128 gate rows and the matching 128 up rows, so every wave
-// holds gate and up for the same outputs and applies SwiGLU in registers.
+// Fat kernels (MFMA-bound at large M): persistent, one 256-thread block per
+// CU, 256-row M-tiles x 256 weight rows (phase 1: 128 gate rows + the
+// matching 128 up rows, so every wave applies SwiGLU to its own
+// accumulators), 4 waves of 128 x 128 (4 x 4 MFMA 32x32x16 tiles).  bf16
+// weights stream into LDS with direct-to-LDS buffer loads; 3-bit weights are
+// decoded on the way through registers.  Work items of one expert are walked
+// in super-tiles and 32 consecutive items run on one XCD, so tiles that share
+// activation rows or weights share that XCD's L2.
 //
 // Thin kernel (HBM-bound): persistent, several blocks per CU, work item =
 // (32 weight rows, thin M-tile); the four waves split the reduction index and
