@@ -108,11 +108,11 @@ class Runner:
         if ev is not None:
             ev[0].record()
         m.moe_ffn_gate_up(self.x, w["gate"], w["up"], b.sorted_pair, s.E, s.k, b.workspace,
-                          s_gate=w.get("gate_scale"), s_up=w.get("up_scale"), wfmt=self.wfmt)
+                          s_gate=w.get("gate_scale"), s_up=w.get("up_scale"), fat_threshold=self.thr, wfmt=self.wfmt)
         if ev is not None:
             ev[1].record()
         m.moe_ffn_down(w["down"], s.T, s.E, s.k, s.I, b.y_sorted, b.workspace, s_down=w.get("down_scale"),
-                       wfmt=self.wfmt)
+                       fat_threshold=self.thr, wfmt=self.wfmt)
         m.moe_combine(b.y_sorted, b.topk_w, b.pair_to_sorted, b.out)
 
     def measure(self, steps, warmup):

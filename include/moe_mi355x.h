@@ -181,15 +181,20 @@ moe_status moe_ffn_plan(const int32_t* expert_offsets, int T, int E, int k, int 
                         int fat_threshold, void* workspace, size_t workspace_bytes, void* stream);
 
 /* moe_ffn_gate_up -- a = silu(x W_gate^T) * (x W_up^T) for every planned batch,
- * stored fp16 in the workspace (row i of a belongs to sorted row i). */
+ * stored fp16 in the workspace (row i of a belongs to sorted row i).
+ * fat_threshold must equal the value given to moe_ffn_plan; with
+ * T < fat_threshold no route list can be fat, so the MFMA-tile kernel is not
+ * launched at all. */
 moe_status moe_ffn_gate_up(const uint16_t* x, int wfmt, const void* w_gate, const void* w_up,
                            const uint16_t* s_gate, const uint16_t* s_up, const int32_t* sorted_pair,
-                           int T, int E, int k, int H, int I, void* workspace, size_t workspace_bytes,
-                           void* stream);
+                           int T, int E, int k, int H, int I, int fat_threshold, void* workspace,
+                           size_t workspace_bytes, void* stream);
 
-/* moe_ffn_down -- y_sorted = a W_down^T for every planned batch. */
+/* moe_ffn_down -- y_sorted = a W_down^T for every planned batch (same
+ * fat_threshold rule as moe_ffn_gate_up). */
 moe_status moe_ffn_down(int wfmt, const void* w_down, const uint16_t* s_down, int T, int E, int k, int H, int I,
-                        uint16_t* y_sorted, void* workspace, size_t workspace_bytes, void* stream);
+                        int fat_threshold, uint16_t* y_sorted, void* workspace, size_t workspace_bytes,
+                        void* stream);
 
 /*
  * moe_combine -- out[t, :] = sum_{j=0..k-1} topk_w[t, j] * y_sorted[pair_to_sorted[t*k+j], :]

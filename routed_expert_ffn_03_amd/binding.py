@@ -58,9 +58,9 @@ def lib() -> ctypes.CDLL:
         L.moe_ffn_plan.restype = i32
         L.moe_ffn_plan.argtypes = [vp, i32, i32, i32, i32, i32, i32, i32, vp, sz, vp]
         L.moe_ffn_gate_up.restype = i32
-        L.moe_ffn_gate_up.argtypes = [vp, i32, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp, sz, vp]
+        L.moe_ffn_gate_up.argtypes = [vp, i32, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, sz, vp]
         L.moe_ffn_down.restype = i32
-        L.moe_ffn_down.argtypes = [i32, vp, vp, i32, i32, i32, i32, i32, vp, vp, sz, vp]
+        L.moe_ffn_down.argtypes = [i32, vp, vp, i32, i32, i32, i32, i32, i32, vp, vp, sz, vp]
         L.moe_combine.restype = i32
         L.moe_combine.argtypes = [vp, vp, vp, i32, i32, i32, vp, vp]
         _lib = L
@@ -153,17 +153,18 @@ def moe_ffn_plan(expert_offsets, T, k, H, I, workspace, fat_threshold=DEFAULT_FA
 
 
 def moe_ffn_gate_up(x, w_gate, w_up, sorted_pair, E, k, workspace, s_gate=None, s_up=None,
-                    wfmt=MOE_WFMT_BF16, stream=None):
+                    fat_threshold=DEFAULT_FAT_THRESHOLD, wfmt=MOE_WFMT_BF16, stream=None):
     T, H = x.shape
     I = w_gate.shape[1]
     _check(lib().moe_ffn_gate_up(_ptr(x), wfmt, _ptr(w_gate), _ptr(w_up), _ptr(s_gate), _ptr(s_up),
-                                 _ptr(sorted_pair), T, E, k, H, I, _ptr(workspace), workspace.numel(),
-                                 _stream(stream)), "moe_ffn_gate_up")
+                                 _ptr(sorted_pair), T, E, k, H, I, fat_threshold, _ptr(workspace),
+                                 workspace.numel(), _stream(stream)), "moe_ffn_gate_up")
 
 
-def moe_ffn_down(w_down, T, E, k, I, y_sorted, workspace, s_down=None, wfmt=MOE_WFMT_BF16, stream=None):
+def moe_ffn_down(w_down, T, E, k, I, y_sorted, workspace, s_down=None, fat_threshold=DEFAULT_FAT_THRESHOLD,
+                 wfmt=MOE_WFMT_BF16, stream=None):
     H = y_sorted.shape[1]
-    _check(lib().moe_ffn_down(wfmt, _ptr(w_down), _ptr(s_down), T, E, k, H, I, _ptr(y_sorted),
+    _check(lib().moe_ffn_down(wfmt, _ptr(w_down), _ptr(s_down), T, E, k, H, I, fat_threshold, _ptr(y_sorted),
                               _ptr(workspace), workspace.numel(), _stream(stream)), "moe_ffn_down")
 
 

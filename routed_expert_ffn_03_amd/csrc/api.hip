@@ -95,9 +95,9 @@ moe_status moe_ffn_plan(const int32_t* expert_offsets, int T, int E, int k, int 
 
 moe_status moe_ffn_gate_up(const uint16_t* x, int wfmt, const void* w_gate, const void* w_up,
                            const uint16_t* s_gate, const uint16_t* s_up, const int32_t* sorted_pair,
-                           int T, int E, int k, int H, int I, void* workspace, size_t workspace_bytes,
-                           void* stream) {
-    if (!x || !w_gate || !w_up || !sorted_pair) return MOE_ERR_INVALID_ARG;
+                           int T, int E, int k, int H, int I, int fat_threshold, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+    if (!x || !w_gate || !w_up || !sorted_pair || fat_threshold < 1) return MOE_ERR_INVALID_ARG;
     if ((wfmt == MOE_WFMT_BF16 || wfmt == MOE_WFMT_Q3G128) && !scales_ok(wfmt, s_gate, s_up))
         return MOE_ERR_INVALID_ARG;
     moe::FfnLaunch a;
@@ -107,12 +107,14 @@ moe_status moe_ffn_gate_up(const uint16_t* x, int wfmt, const void* w_gate, cons
     a.wg = w_gate; a.wu = w_up;
     a.sg = s_gate; a.su = s_up;
     a.sorted_pair = sorted_pair;
+    a.fat_threshold = fat_threshold;
     return hip_status(moe::launch_ffn_phase(a, 1, reinterpret_cast<hipStream_t>(stream)));
 }
 
 moe_status moe_ffn_down(int wfmt, const void* w_down, const uint16_t* s_down, int T, int E, int k, int H, int I,
-                        uint16_t* y_sorted, void* workspace, size_t workspace_bytes, void* stream) {
-    if (!w_down || !y_sorted) return MOE_ERR_INVALID_ARG;
+                        int fat_threshold, uint16_t* y_sorted, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+    if (!w_down || !y_sorted || fat_threshold < 1) return MOE_ERR_INVALID_ARG;
     if ((wfmt == MOE_WFMT_BF16 || wfmt == MOE_WFMT_Q3G128) && !scales_ok(wfmt, s_down, s_down))
         return MOE_ERR_INVALID_ARG;
     moe::FfnLaunch a;
@@ -121,6 +123,7 @@ moe_status moe_ffn_down(int wfmt, const void* w_down, const uint16_t* s_down, in
     a.wd = w_down;
     a.sd = s_down;
     a.y = y_sorted;
+    a.fat_threshold = fat_threshold;
     return hip_status(moe::launch_ffn_phase(a, 2, reinterpret_cast<hipStream_t>(stream)));
 }
 
@@ -140,10 +143,11 @@ moe_status moe_grouped_ffn(const uint16_t* x, int wfmt, const void* w_gate, cons
     if (st != MOE_OK) return st;
     st = moe_ffn_plan(expert_offsets, T, E, k, H, I, wfmt, fat_threshold, workspace, workspace_bytes, stream);
     if (st != MOE_OK) return st;
-    st = moe_ffn_gate_up(x, wfmt, w_gate, w_up, s_gate, s_up, sorted_pair, T, E, k, H, I, workspace,
+    st = moe_ffn_gate_up(x, wfmt, w_gate, w_up, s_gate, s_up, sorted_pair, T, E, k, H, I, fat_threshold, workspace,
                          workspace_bytes, stream);
     if (st != MOE_OK) return st;
-    return moe_ffn_down(wfmt, w_down, s_down, T, E, k, H, I, y_sorted, workspace, workspace_bytes, stream);
+    return moe_ffn_down(wfmt, w_down, s_down, T, E, k, H, I, fat_threshold, y_sorted, workspace, workspace_bytes,
+                        stream);
 }
 
 moe_status moe_combine(const uint16_t* y_sorted, const float* topk_w, const int32_t* pair_to_sorted, int T, int k,

@@ -65,7 +65,6 @@ constexpr uint32_t DMA_STAGE_BYTES = 2 * DMA_A_BYTES;     // + the same for weig
 static_assert(2 * DMA_STAGE_BYTES <= FAT_LDS_BYTES, "LDS stages too large");
 constexpr int THIN_BM = 32;
 constexpr int THIN_THREADS = 256;
-constexpr int THIN_DEPTH = 4;             // chunks in flight per lane
 
 constexpr int Q3_WORDS = 13;
 
@@ -673,9 +672,13 @@ void ffn_fat_dma_kernel(FfnArgs a) {
 
 // ------------------------------------------------------------ thin kernel
 
-template <int PHASE, int WFMT>
+// CW: 16-byte pieces per lane and row per chunk; lane half g covers 8*CW
+// consecutive k of a 16*CW-wide chunk, so with CW = 4 every row is read in
+// whole 128-byte lines.  D: chunks in the register ring (D - 1 in flight).
+template <int PHASE, int WFMT, int CW>
 __global__ __launch_bounds__(THIN_THREADS)
 void ffn_thin_kernel(FfnArgs a) {
+    constexpr int D = CW == 4 ? 3 : 4;
     __shared__ float red[4][16][64];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform (SGPR)
@@ -685,8 +688,8 @@ void ffn_thin_kernel(FfnArgs a) {
     const int n_mt = a.hdr->n_thin;
     const int n_items = n_mt * NT;
     const int Kw = K / 4;                   // reduction slice of this wave
-    const int nch = Kw / 32;                // 32-k chunks: lane half g covers 16 of them
-    const int kbase = wave * Kw + g * 16;
+    const int nch = Kw / (16 * CW);         // chunks: lane half g covers 8 CW k of each
+    const int kbase = wave * Kw + g * 8 * CW;
 
     for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
         const int nt = item / n_mt, mt = item % n_mt;
@@ -704,32 +707,29 @@ void ffn_thin_kernel(FfnArgs a) {
             brow = weight_row<WFMT>(a.wd, a.sd, (size_t)t.e * a.H + nt * 32 + m, K);
         }
 
-        u32x4 ra[THIN_DEPTH][2], rw[THIN_DEPTH][2];
-        auto load = [&](int ch, u32x4 (&xa)[2], u32x4 (&xw)[2]) {
-            const int k0 = kbase + ch * 32;
-            xa[0] = u32x4{0, 0, 0, 0};
-            xa[1] = u32x4{0, 0, 0, 0};
-            if (arow) {
-                xa[0] = ldg16(arow + k0);
-                xa[1] = ldg16(arow + k0 + 8);
+        u32x4 ra[D][CW], rw[D][CW];
+        auto load = [&](int ch, u32x4 (&xa)[CW], u32x4 (&xw)[CW]) {
+            const int k0 = kbase + ch * 16 * CW;
+#pragma unroll
+            for (int c = 0; c < CW; ++c) {
+                xa[c] = u32x4{0, 0, 0, 0};
+                if (arow) xa[c] = ldg16(arow + k0 + 8 * c);
             }
-            xw[0] = load_w8<WFMT, PHASE>(brow, k0);
-            xw[1] = load_w8<WFMT, PHASE>(brow, k0 + 8);
+#pragma unroll
+            for (int c = 0; c < CW; ++c) xw[c] = load_w8<WFMT, PHASE>(brow, k0 + 8 * c);
         };
         f32x16 acc = f32x16{};
 #pragma unroll
-        for (int d = 0; d < THIN_DEPTH - 1; ++d)
+        for (int d = 0; d < D - 1; ++d)
             if (d < nch) load(d, ra[d], rw[d]);
-        for (int c0 = 0; c0 < nch; c0 += THIN_DEPTH) {
+        for (int c0 = 0; c0 < nch; c0 += D) {
 #pragma unroll
-            for (int d = 0; d < THIN_DEPTH; ++d) {
+            for (int d = 0; d < D; ++d) {
                 const int ch = c0 + d;
-                if (ch + THIN_DEPTH - 1 < nch)
-                    load(ch + THIN_DEPTH - 1, ra[(d + THIN_DEPTH - 1) % THIN_DEPTH],
-                         rw[(d + THIN_DEPTH - 1) % THIN_DEPTH]);
+                if (ch + D - 1 < nch) load(ch + D - 1, ra[(d + D - 1) % D], rw[(d + D - 1) % D]);
                 if (ch < nch) {
-                    acc = mma<PHASE>(ra[d][0], rw[d][0], acc);
-                    acc = mma<PHASE>(ra[d][1], rw[d][1], acc);
+#pragma unroll
+                    for (int c = 0; c < CW; ++c) acc = mma<PHASE>(ra[d][c], rw[d][c], acc);
                 }
             }
         }
@@ -780,16 +780,16 @@ FfnLayout ffn_layout(int T, int E, int k, int H, int I) {
 
 struct DevInfo {
     int cus = 0;
-    int thin_blocks[2][2] = {{0, 0}, {0, 0}};   // [wfmt][phase-1]
+    int thin_blocks[2][2][2] = {};              // [wfmt][phase-1][chunk width 2 / 4]
 };
 
 std::mutex g_dev_mu;
 DevInfo g_dev[64];
 
-template <int PHASE, int WFMT>
+template <int PHASE, int WFMT, int CW>
 int thin_occupancy() {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, ffn_thin_kernel<PHASE, WFMT>, THIN_THREADS, 0) !=
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, ffn_thin_kernel<PHASE, WFMT, CW>, THIN_THREADS, 0) !=
         hipSuccess || n < 1)
         n = 1;
     return n;
@@ -813,10 +813,14 @@ hipError_t dev_info(DevInfo& out) {
             err = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)FAT_LDS_BYTES);
             if (err != hipSuccess) return err;
         }
-        d.thin_blocks[0][0] = thin_occupancy<1, 0>();
-        d.thin_blocks[0][1] = thin_occupancy<2, 0>();
-        d.thin_blocks[1][0] = thin_occupancy<1, 1>();
-        d.thin_blocks[1][1] = thin_occupancy<2, 1>();
+        d.thin_blocks[0][0][0] = thin_occupancy<1, 0, 2>();
+        d.thin_blocks[0][0][1] = thin_occupancy<1, 0, 4>();
+        d.thin_blocks[0][1][0] = thin_occupancy<2, 0, 2>();
+        d.thin_blocks[0][1][1] = thin_occupancy<2, 0, 4>();
+        d.thin_blocks[1][0][0] = thin_occupancy<1, 1, 2>();
+        d.thin_blocks[1][0][1] = thin_occupancy<1, 1, 4>();
+        d.thin_blocks[1][1][0] = thin_occupancy<2, 1, 2>();
+        d.thin_blocks[1][1][1] = thin_occupancy<2, 1, 4>();
         d.cus = cus;
     }
     out = d;
@@ -840,11 +844,21 @@ FfnArgs make_args(const FfnLaunch& a) {
     return fa;
 }
 
+// Fat tiles need a route list of at least fat_threshold rows, and a token
+// selects an expert at most once, so with T < fat_threshold (decode) there is
+// no fat work and that launch is skipped.
 template <int PHASE, int WFMT>
-void launch_phase_t(const FfnArgs& fa, const DevInfo& d, hipStream_t s) {
-    if (WFMT == 0) ffn_fat_dma_kernel<PHASE><<<d.cus, FAT_THREADS, FAT_LDS_BYTES, s>>>(fa);
-    else ffn_fat_kernel<PHASE, WFMT><<<d.cus, FAT_THREADS, FAT_LDS_BYTES, s>>>(fa);
-    ffn_thin_kernel<PHASE, WFMT><<<d.cus * d.thin_blocks[WFMT][PHASE - 1], THIN_THREADS, 0, s>>>(fa);
+void launch_phase_t(const FfnArgs& fa, const DevInfo& d, bool fat_possible, hipStream_t s) {
+    if (fat_possible) {
+        if (WFMT == 0) ffn_fat_dma_kernel<PHASE><<<d.cus, FAT_THREADS, FAT_LDS_BYTES, s>>>(fa);
+        else ffn_fat_kernel<PHASE, WFMT><<<d.cus, FAT_THREADS, FAT_LDS_BYTES, s>>>(fa);
+    }
+    // whole 128-byte lines per row when each wave's quarter of K is a multiple of 64
+    const int K = PHASE == 1 ? fa.H : fa.I;
+    if ((K / 4) % 64 == 0)
+        ffn_thin_kernel<PHASE, WFMT, 4><<<d.cus * d.thin_blocks[WFMT][PHASE - 1][1], THIN_THREADS, 0, s>>>(fa);
+    else
+        ffn_thin_kernel<PHASE, WFMT, 2><<<d.cus * d.thin_blocks[WFMT][PHASE - 1][0], THIN_THREADS, 0, s>>>(fa);
 }
 
 }  // namespace
@@ -866,12 +880,13 @@ hipError_t launch_ffn_phase(const FfnLaunch& a, int phase, hipStream_t s) {
     hipError_t err = dev_info(d);
     if (err != hipSuccess) return err;
     const FfnArgs fa = make_args(a);
+    const bool fat = a.T >= a.fat_threshold;
     if (phase == 1) {
-        if (a.wfmt == 0) launch_phase_t<1, 0>(fa, d, s);
-        else launch_phase_t<1, 1>(fa, d, s);
+        if (a.wfmt == 0) launch_phase_t<1, 0>(fa, d, fat, s);
+        else launch_phase_t<1, 1>(fa, d, fat, s);
     } else {
-        if (a.wfmt == 0) launch_phase_t<2, 0>(fa, d, s);
-        else launch_phase_t<2, 1>(fa, d, s);
+        if (a.wfmt == 0) launch_phase_t<2, 0>(fa, d, fat, s);
+        else launch_phase_t<2, 1>(fa, d, fat, s);
     }
     return hipGetLastError();
 }

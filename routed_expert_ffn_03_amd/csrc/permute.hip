@@ -15,6 +15,7 @@
 //      pairs of the same expert is (pairs of lower waves) + (lower lanes of
 //      its own wave), read off 64-bit lane masks built with LDS atomic OR.
 //      Since a token picks an expert at most once, lane order = pair order.
+// Up to 1024 tokens the same three steps run inside one block.
 #include "common.h"
 #include "kernels.h"
 
@@ -23,6 +24,7 @@ namespace {
 
 constexpr int PB_TOKENS = 256;            // tokens (= threads) per block
 constexpr int PB_WAVES = PB_TOKENS / WAVE;
+constexpr int PB_SMALL_T = 1024;          // one-block path up to this many tokens
 
 __global__ __launch_bounds__(PB_TOKENS)
 void permute_hist_kernel(const int32_t* __restrict__ ids, int T, int E, int k,
@@ -85,6 +87,69 @@ void permute_scatter_kernel(const int32_t* __restrict__ ids, int T, int E, int k
     }
 }
 
+// Small batches (T <= PB_SMALL_T): the three passes in one block.  Counts,
+// the scan and the running per-expert bases stay in LDS; tokens go through in
+// chunks of 256 with the same lane-mask ranking as the scatter pass.
+__global__ __launch_bounds__(PB_TOKENS)
+void permute_small_kernel(const int32_t* __restrict__ ids, int T, int E, int k, int32_t* __restrict__ offsets,
+                          int32_t* __restrict__ sorted_pair, int32_t* __restrict__ pair_to_sorted) {
+    __shared__ int base[MAX_EXPERTS];
+    __shared__ unsigned long long mask[PB_WAVES][MAX_EXPERTS];
+    __shared__ int scratch[16];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    for (int e = tid; e < E; e += PB_TOKENS) base[e] = 0;
+    __syncthreads();
+    for (int t = tid; t < T; t += PB_TOKENS)
+        for (int j = 0; j < k; ++j) atomicAdd(&base[ids[(size_t)t * k + j]], 1);
+    __syncthreads();
+    // exclusive scan of the counts: 4 consecutive experts per thread
+    int c[4], sum = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int e = 4 * tid + i;
+        c[i] = e < E ? base[e] : 0;
+        sum += c[i];
+    }
+    int run = block_inclusive_scan(sum, scratch) - sum;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int e = 4 * tid + i;
+        if (e < E) {
+            base[e] = run;
+            offsets[e] = run;
+        }
+        run += c[i];
+    }
+    if (tid == 0) offsets[E] = T * k;
+    __syncthreads();
+    const unsigned long long bit = 1ull << lane;
+    for (int t0 = 0; t0 < T; t0 += PB_TOKENS) {
+        for (int i = tid; i < PB_WAVES * E; i += PB_TOKENS) mask[i / E][i % E] = 0ull;
+        __syncthreads();
+        const int t = t0 + tid;
+        if (t < T)
+            for (int j = 0; j < k; ++j) atomicOr(&mask[wave][ids[(size_t)t * k + j]], bit);
+        __syncthreads();
+        if (t < T) {
+            for (int j = 0; j < k; ++j) {
+                const int p = t * k + j;
+                const int e = ids[p];
+                int pos = base[e] + __popcll(mask[wave][e] & (bit - 1ull));
+                for (int w = 0; w < wave; ++w) pos += __popcll(mask[w][e]);
+                sorted_pair[pos] = p;
+                pair_to_sorted[p] = pos;
+            }
+        }
+        __syncthreads();
+        for (int e = tid; e < E; e += PB_TOKENS) {
+            int n = 0;
+            for (int w = 0; w < PB_WAVES; ++w) n += __popcll(mask[w][e]);
+            base[e] += n;
+        }
+        __syncthreads();
+    }
+}
+
 }  // namespace
 
 size_t permute_ws_bytes(int T, int E) {
@@ -95,6 +160,10 @@ size_t permute_ws_bytes(int T, int E) {
 hipError_t launch_permute(const int32_t* ids, int T, int E, int k, int32_t* offsets,
                           int32_t* sorted_pair, int32_t* pair_to_sorted, int32_t* block_hist,
                           hipStream_t s) {
+    if (T <= PB_SMALL_T) {
+        permute_small_kernel<<<1, PB_TOKENS, 0, s>>>(ids, T, E, k, offsets, sorted_pair, pair_to_sorted);
+        return hipGetLastError();
+    }
     const int nb = (T + PB_TOKENS - 1) / PB_TOKENS;
     permute_hist_kernel<<<nb, PB_TOKENS, 0, s>>>(ids, T, E, k, block_hist);
     permute_scan_kernel<<<1, 1024, 0, s>>>(block_hist, nb, E, T * k, offsets);

@@ -19,7 +19,6 @@ namespace {
 
 constexpr int ROUTE_THREADS = 256;
 constexpr int ROUTE_WAVES = ROUTE_THREADS / WAVE;
-constexpr int MAX_PER_LANE = MAX_EXPERTS / WAVE;   // 16
 
 __device__ __forceinline__ uint32_t ordered_bits(float v) {
     if (v == 0.0f) v = 0.0f;                        // -0 -> +0
@@ -51,6 +50,7 @@ __device__ __forceinline__ float wave_sum(float v) {
 // tokens_per_block tokens per block; waves take tokens round-robin.
 // direct_counts: the grid is one block covering all tokens, so the block
 // histogram is the answer (no zeroing pass, no atomics).
+template <int NV>                                   // keys per lane (>= E / 64)
 __global__ __launch_bounds__(ROUTE_THREADS)
 void route_topk_kernel(const float* __restrict__ logits, int T, int E, int k, int tokens_per_block,
                        int direct_counts, int32_t* __restrict__ topk_ids, float* __restrict__ topk_w,
@@ -64,9 +64,9 @@ void route_topk_kernel(const float* __restrict__ logits, int T, int E, int k, in
     const int t1 = min(T, t0 + tokens_per_block);
     for (int t = t0 + wave; t < t1; t += ROUTE_WAVES) {
         const float* row = logits + (size_t)t * E;
-        uint64_t key[MAX_PER_LANE];
+        uint64_t key[NV];
 #pragma unroll
-        for (int i = 0; i < MAX_PER_LANE; ++i) {
+        for (int i = 0; i < NV; ++i) {
             const int e = lane + WAVE * i;
             key[i] = 0;
             if (e < E) key[i] = ((uint64_t)ordered_bits(row[e]) << 32) | (uint32_t)(~e);
@@ -76,12 +76,12 @@ void route_topk_kernel(const float* __restrict__ logits, int T, int E, int k, in
         for (int j = 0; j < k; ++j) {
             uint64_t m = 0;
 #pragma unroll
-            for (int i = 0; i < MAX_PER_LANE; ++i) m = key[i] > m ? key[i] : m;
+            for (int i = 0; i < NV; ++i) m = key[i] > m ? key[i] : m;
             m = wave_max_u64(m);
             const int win = (int)(~(uint32_t)m);
             if ((win & 63) == lane) {
 #pragma unroll
-                for (int i = 0; i < MAX_PER_LANE; ++i)
+                for (int i = 0; i < NV; ++i)
                     if (i == (win >> 6)) key[i] = 0;
             }
             if (lane == j) {
@@ -110,10 +110,9 @@ __global__ void zero_i32_kernel(int32_t* p, int n) {
     if (i < n) p[i] = 0;
 }
 
-}  // namespace
-
-hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* topk_ids,
-                             float* topk_w, int32_t* counts, hipStream_t s) {
+template <int NV>
+void route_launch(const float* logits, int T, int E, int k, int32_t* topk_ids, float* topk_w, int32_t* counts,
+                  hipStream_t s) {
     // Small batches: one block owns every token and writes the histogram
     // directly.  Larger ones: 16 tokens per block (4 per wave) keeps ~1k
     // blocks in flight at 16k tokens; bins merge with integer atomics after a
@@ -121,13 +120,25 @@ hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* 
     // deterministic).
     const int single_max = 64;
     if (T <= single_max) {
-        route_topk_kernel<<<1, ROUTE_THREADS, 0, s>>>(logits, T, E, k, T, 1, topk_ids, topk_w, counts);
-        return hipGetLastError();
+        route_topk_kernel<NV><<<1, ROUTE_THREADS, 0, s>>>(logits, T, E, k, T, 1, topk_ids, topk_w, counts);
+        return;
     }
     const int tpb = 16;
     zero_i32_kernel<<<(E + 255) / 256, 256, 0, s>>>(counts, E);
     const int blocks = (T + tpb - 1) / tpb;
-    route_topk_kernel<<<blocks, ROUTE_THREADS, 0, s>>>(logits, T, E, k, tpb, 0, topk_ids, topk_w, counts);
+    route_topk_kernel<NV><<<blocks, ROUTE_THREADS, 0, s>>>(logits, T, E, k, tpb, 0, topk_ids, topk_w, counts);
+}
+
+}  // namespace
+
+hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* topk_ids,
+                             float* topk_w, int32_t* counts, hipStream_t s) {
+    const int nv = (E + WAVE - 1) / WAVE;
+    if (nv <= 1) route_launch<1>(logits, T, E, k, topk_ids, topk_w, counts, s);
+    else if (nv <= 2) route_launch<2>(logits, T, E, k, topk_ids, topk_w, counts, s);
+    else if (nv <= 4) route_launch<4>(logits, T, E, k, topk_ids, topk_w, counts, s);
+    else if (nv <= 8) route_launch<8>(logits, T, E, k, topk_ids, topk_w, counts, s);
+    else route_launch<16>(logits, T, E, k, topk_ids, topk_w, counts, s);
     return hipGetLastError();
 }
 

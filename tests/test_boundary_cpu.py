@@ -103,15 +103,19 @@ def test_split_ffn_rejects(L):
     assert L.moe_ffn_plan(FAKE, 64, 16, 2, 256, 128, 0, 32, FAKE, 16, None) == moe.MOE_ERR_WORKSPACE
     assert L.moe_ffn_plan(FAKE, 64, 16, 2, 250, 128, 0, 32, FAKE, 1 << 40, None) == moe.MOE_ERR_UNSUPPORTED
     gu = lambda **kw: L.moe_ffn_gate_up(kw.get("x", FAKE), kw.get("wfmt", 0), FAKE, FAKE, kw.get("sg"),
-                                        kw.get("su"), FAKE, 64, 16, 2, 256, 128, FAKE, kw.get("wsb", 1 << 40), None)
+                                        kw.get("su"), FAKE, 64, 16, 2, 256, 128, kw.get("thr", 32), FAKE,
+                                        kw.get("wsb", 1 << 40), None)
     assert gu(x=None) == moe.MOE_ERR_INVALID_ARG
     assert gu(sg=FAKE) == moe.MOE_ERR_INVALID_ARG
     assert gu(wfmt=1, sg=FAKE) == moe.MOE_ERR_INVALID_ARG
     assert gu(wfmt=3) == moe.MOE_ERR_UNSUPPORTED
     assert gu(wsb=8) == moe.MOE_ERR_WORKSPACE
-    assert L.moe_ffn_down(0, FAKE, None, 64, 16, 2, 256, 128, None, FAKE, 1 << 40, None) == moe.MOE_ERR_INVALID_ARG
-    assert L.moe_ffn_down(1, FAKE, None, 64, 16, 2, 256, 128, FAKE, FAKE, 1 << 40, None) == moe.MOE_ERR_INVALID_ARG
-    assert L.moe_ffn_down(0, FAKE, FAKE, 64, 16, 2, 256, 128, FAKE, FAKE, 1 << 40, None) == moe.MOE_ERR_INVALID_ARG
+    assert gu(thr=0) == moe.MOE_ERR_INVALID_ARG
+    dn = lambda *a: L.moe_ffn_down(*a, FAKE, 1 << 40, None)
+    assert dn(0, FAKE, None, 64, 16, 2, 256, 128, 32, None) == moe.MOE_ERR_INVALID_ARG
+    assert dn(1, FAKE, None, 64, 16, 2, 256, 128, 32, FAKE) == moe.MOE_ERR_INVALID_ARG
+    assert dn(0, FAKE, FAKE, 64, 16, 2, 256, 128, 32, FAKE) == moe.MOE_ERR_INVALID_ARG
+    assert dn(0, FAKE, None, 64, 16, 2, 256, 128, 0, FAKE) == moe.MOE_ERR_INVALID_ARG
 
 
 def test_combine_rejects(L):
