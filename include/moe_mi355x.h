@@ -147,15 +147,19 @@ moe_status moe_permute(const int32_t* topk_ids, int T, int E, int k,
  *            scale * (field - 4).
  * expert_offsets, sorted_pair   as produced by moe_permute.
  * fat_threshold  experts with at least this many rows run as MFMA tiles of
- *            128 rows with weight tiles staged in LDS; smaller experts stream
- *            their weights once through a 32-row tile.  Both paths compute the
- *            same function (rounding differs only in summation order).
+ *            up to 256 rows (the list split evenly into 32-row multiples)
+ *            with weight tiles staged in LDS; smaller experts stream their
+ *            weights once through a 32-row tile.  Both paths compute the same
+ *            function (rounding differs only in summation order).
  *            Must be >= 1.
  * y_sorted   fp16 [T*k, H] output in sorted-row order.
  * Precision: products accumulate in fp32; a is stored as fp16 and the down
  * projection multiplies fp16 a by W_down converted to fp16 (exact for
  * |w| in [2^-14, 65504]; smaller magnitudes lose at most 2^-24 absolute).
- * Shapes: H % 256 == 0 and I % 128 == 0, else MOE_ERR_UNSUPPORTED.
+ * Shapes: H % 256 == 0 and I % 128 == 0, and each of x (T*H*2 bytes), the
+ * activation a (T*k*I*2 bytes) and one expert's bf16 matrix (I*H*2 bytes)
+ * below 4 GiB (the kernels address them with 32-bit buffer offsets), else
+ * MOE_ERR_UNSUPPORTED.
  * Workspace: >= moe_workspace_size(T, E, k, H, I, wfmt) bytes.
  */
 moe_status moe_grouped_ffn(const uint16_t* x, int wfmt,
@@ -174,7 +178,8 @@ moe_status moe_grouped_ffn(const uint16_t* x, int wfmt,
  *
  * moe_ffn_plan -- cut every non-empty route list into batches that share one
  * read of the expert's weights (wiki file table, segment patch entry): lists
- * of at least fat_threshold rows into 128-row MFMA batches, shorter lists
+ * of at least fat_threshold rows into MFMA batches of up to 256 rows (equal
+ * multiples of 32 rows, the last one ragged), shorter lists
  * into 32-row streaming batches.  Reads expert_offsets only.
  */
 moe_status moe_ffn_plan(const int32_t* expert_offsets, int T, int E, int k, int H, int I, int wfmt,

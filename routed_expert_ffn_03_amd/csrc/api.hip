@@ -17,7 +17,14 @@ bool bad_tek(int T, int E, int k) {
     return false;
 }
 
-bool ffn_shape_ok(int H, int I) { return H >= 256 && I >= 128 && H % 256 == 0 && I % 128 == 0; }
+// The fat kernels address x, the activation a and one expert's matrix with
+// 32-bit buffer offsets: each must stay below 4 GiB.
+bool ffn_shape_ok(int T, int k, int H, int I) {
+    if (H < 256 || I < 128 || H % 256 != 0 || I % 128 != 0) return false;
+    const unsigned long long lim = 1ULL << 32;
+    return (unsigned long long)T * H * 2 < lim && (unsigned long long)T * k * I * 2 < lim &&
+           (unsigned long long)I * H * 2 < lim;
+}
 
 moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
@@ -39,7 +46,7 @@ const char* moe_status_string(moe_status s) {
 const char* moe_version(void) { return "0.1.0"; }
 
 size_t moe_workspace_size(int T, int E, int k, int H, int I, int wfmt) {
-    if (bad_tek(T, E, k) || !ffn_shape_ok(H, I)) return 0;
+    if (bad_tek(T, E, k) || !ffn_shape_ok(T, k, H, I)) return 0;
     if (wfmt != MOE_WFMT_BF16 && wfmt != MOE_WFMT_Q3G128) return 0;
     return align256(moe::permute_ws_bytes(T, E)) + moe::ffn_ws_bytes(T, E, k, H, I);
 }
@@ -68,7 +75,7 @@ static moe_status ffn_prepare(moe::FfnLaunch& a, int wfmt, int T, int E, int k, 
                               void* workspace, size_t workspace_bytes) {
     if (bad_tek(T, E, k) || H < 1 || I < 1) return MOE_ERR_INVALID_ARG;
     if (wfmt != MOE_WFMT_BF16 && wfmt != MOE_WFMT_Q3G128) return MOE_ERR_UNSUPPORTED;
-    if (!ffn_shape_ok(H, I)) return MOE_ERR_UNSUPPORTED;
+    if (!ffn_shape_ok(T, k, H, I)) return MOE_ERR_UNSUPPORTED;
     const size_t need = moe_workspace_size(T, E, k, H, I, wfmt);
     if (!workspace || workspace_bytes < need) return MOE_ERR_WORKSPACE;
     a = moe::FfnLaunch{};

@@ -60,9 +60,6 @@ constexpr int FAT_BM = 256;              // rows per fat M-tile
 constexpr int FAT_THREADS = 256;
 constexpr int FAT_STAGE = (FAT_BM + 256) * 8;            // 16-byte chunks per LDS stage (A + B)
 constexpr size_t FAT_LDS_BYTES = 2 * FAT_STAGE * 16;     // 128 KB: double-buffered stages / epilogue
-constexpr uint32_t DMA_A_BYTES = 256 * 128;              // activations of one 64-k stage
-constexpr uint32_t DMA_STAGE_BYTES = 2 * DMA_A_BYTES;     // + the same for weights
-static_assert(2 * DMA_STAGE_BYTES <= FAT_LDS_BYTES, "LDS stages too large");
 constexpr int THIN_BM = 32;
 constexpr int THIN_THREADS = 256;
 
@@ -101,9 +98,14 @@ void build_tiles_kernel(const int32_t* __restrict__ offsets, int E, int thr, Ffn
     }
     const int fi = block_inclusive_scan(nf, scratch);
     const int ti = block_inclusive_scan(nt, scratch);
+    // the expert's 32-row tiles are spread evenly over its nf M-tiles, so the
+    // M-tiles of one expert cost the same and walk the weights in step
+    const int rt = (n + 31) >> 5;
     for (int i = 0; i < nf; ++i) {
+        const int rt0 = i * (rt / nf) + min(i, rt % nf);
+        const int rti = rt / nf + (i < rt % nf ? 1 : 0);
         MTile m = {};
-        m.e = e; m.row0 = r0 + i * FAT_BM; m.rows = min(FAT_BM, n - i * FAT_BM);
+        m.e = e; m.row0 = r0 + 32 * rt0; m.rows = min(32 * rti, n - 32 * rt0);
         m.first = fi - nf; m.count = nf;
         fat[fi - nf + i] = m;
     }
@@ -271,12 +273,24 @@ __device__ __forceinline__ void fat_item(const MTile* __restrict__ fat, int item
     nt = nb * gn + r % gnr;
 }
 
+// Row tiles of a fat M-tile owned by wave row wm: the tile's 32-row tiles are
+// dealt alternately to the two wave rows (tile 2 ri + wm is the wave's ri-th).
+__device__ __forceinline__ int fat_row_tiles(int rows, int wm) {
+    const int rt = (rows + 31) >> 5;
+    return max(0, min(4, (rt - wm + 1) >> 1));
+}
+
 // Fat-tile epilogue: two passes of 64 rows per wave through LDS, 16-byte row
 // stores (MFMA 32x32 output: lane holds column n, rows 8(r>>2) + 4g + (r&3)).
+// Pass p stages the wave's row tiles 2p and 2p + 1 (tile rows 32 (2 ri + wm)).
 // Phase 1 stores silu(gate) * up as fp16 activations, phase 2 fp16 y rows.
-template <int PHASE>
+// RTW (this wave's row tiles with data) is a compile-time constant, and the
+// epilogue runs inside the K-loop instantiation of that count, so the
+// accumulators never merge across instantiations (a merge would route all of
+// them through VGPRs).
+template <int PHASE, int RTW>
 __device__ __forceinline__ void fat_epilogue(const FfnArgs& a, const f32x16 (&acc)[4][4], const MTile& t, int nt,
-                                             int rtw, u32x4* smem) {
+                                             u32x4* smem) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform (SGPR)
     const int wm = wave >> 1, wn = wave & 1;
@@ -293,15 +307,20 @@ __device__ __forceinline__ void fat_epilogue(const FfnArgs& a, const f32x16 (&ac
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const int ri = pass * 2 + h;
-            if (ri < rtw) {
+            if (ri < RTW) {
 #pragma unroll
-                for (int cj = 0; cj < (PHASE == 1 ? 2 : 4); ++cj)
+                for (int cj = 0; cj < (PHASE == 1 ? 2 : 4); ++cj) {
+                    // one accumulator tile at a time: keeps the compiler from
+                    // moving every accumulator into VGPRs at once
+                    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
                         const int m = h * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
                         const float v = PHASE == 1 ? silu_mul(acc[ri][cj][r], acc[ri][cj + 2][r]) : acc[ri][cj][r];
                         sO[m * LD + cj * 32 + n] = f32_to_f16_bits(v);
                     }
+                }
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
         __syncthreads();
@@ -309,7 +328,7 @@ __device__ __forceinline__ void fat_epilogue(const FfnArgs& a, const f32x16 (&ac
 #pragma unroll
         for (int it = 0; it < 64 * LPR / 64; ++it) {
             const int m = it * (64 / LPR) + lane / LPR, ch = lane % LPR;
-            const int row = wm * 128 + pass * 64 + m;
+            const int row = (2 * (pass * 2 + (m >> 5)) + wm) * 32 + (m & 31);
             if (row < t.rows)
                 stg16(dst + (size_t)(t.row0 + row) * N + col0 + ch * 8,
                       *reinterpret_cast<const u32x4*>(sO + m * LD + ch * 8));
@@ -351,7 +370,7 @@ void ffn_fat_kernel(FfnArgs a) {
     const int bg1 = PHASE == 1 ? 128 + wn * 64 : wn * 128 + 64;
     // activation source: x (gathered rows) or the fp16 activation
     const __amdgpu_buffer_rsrc_t asrc = PHASE == 1
-        ? make_rsrc(a.x, (uint32_t)(a.T * a.H * 2))
+        ? make_rsrc(a.x, (uint32_t)((size_t)a.T * a.H * 2))
         : make_rsrc(a.act, (uint32_t)((size_t)a.T * a.k * a.I * 2));
     const size_t wmat = (size_t)a.I * a.H;                // weights per matrix per expert
     const size_t wbytes = WFMT == 0 ? wmat * 2 : wmat / 128 * Q3_WORDS * 4;
@@ -361,7 +380,7 @@ void ffn_fat_kernel(FfnArgs a) {
         MTile t;
         int nt;
         fat_item(a.fat, item, NT, t, nt);
-        const int rtw = max(0, min(4, (t.rows - wm * 128 + 31) >> 5));   // this wave's row tiles with data
+        const int rtw = fat_row_tiles(t.rows, wm);   // this wave's row tiles with data
 
         // activation rows: byte offsets of 8 rows (rows past the tile repeat its
         // last row; their results are never stored)
@@ -424,7 +443,7 @@ void ffn_fat_kernel(FfnArgs a) {
                 u32x4 af[4], bf[4];
 #pragma unroll
                 for (int ri = 0; ri < 4; ++ri) {
-                    const int r = wm * 128 + ri * 32 + n;
+                    const int r = (2 * ri + wm) * 32 + n;
                     af[ri] = sA[r * 8 + (ch ^ ((r >> 1) & 7))];
                 }
 #pragma unroll
@@ -450,6 +469,7 @@ void ffn_fat_kernel(FfnArgs a) {
                 if (kt + 1 < KT) sstore(kt + 1, (kt + 1) & 1);
                 __syncthreads();
             }
+            fat_epilogue<PHASE, decltype(rt_c)::value>(a, acc, t, nt, smem);
         };
         switch (rtw) {
             case 4: kloop(std::integral_constant<int, 4>{}); break;
@@ -458,8 +478,6 @@ void ffn_fat_kernel(FfnArgs a) {
             case 1: kloop(std::integral_constant<int, 1>{}); break;
             default: kloop(std::integral_constant<int, 0>{}); break;
         }
-
-        fat_epilogue<PHASE>(a, acc, t, nt, rtw, smem);
     }
 }
 
@@ -493,80 +511,99 @@ __device__ __forceinline__ void vm_wait() {
     asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
 }
 
+constexpr int DMA_BK = 32;                                  // k per LDS stage
+constexpr uint32_t DMA_ROW = DMA_BK * 2;                    // bytes of one row per stage
+constexpr uint32_t DMA_OPER = FAT_BM * DMA_ROW;             // 16 KB: one operand of a stage
+constexpr uint32_t DMA_STAGE = 2 * DMA_OPER;                // activations + weights
+constexpr int DMA_LOADS = 8;                                // load instructions per wave per stage
+
+template <int NS>
+constexpr size_t dma_lds_bytes() {
+    return (size_t)NS * DMA_STAGE > FAT_LDS_BYTES ? (size_t)NS * DMA_STAGE : FAT_LDS_BYTES;
+}
+
+// Wait until at most `stages` stages of this wave's loads are outstanding
+// (loads complete in issue order, DMA_LOADS per stage).
+__device__ __forceinline__ void vm_wait_stages(int stages) {
+    switch (stages) {
+        case 0: vm_wait<0>(); break;
+        case 1: vm_wait<DMA_LOADS>(); break;
+        case 2: vm_wait<2 * DMA_LOADS>(); break;
+        case 3: vm_wait<3 * DMA_LOADS>(); break;
+        default: vm_wait<4 * DMA_LOADS>(); break;
+    }
+}
+
 // Fat tile for bf16 weights: 256 rows x 256 weight rows, 4 waves as 2 x 2,
-// each wave 128 rows x 128 weight rows = 4 x 4 MFMA 32x32x16 accumulators.
-// Both operands stream into two LDS stages of 64 k (32 KB of activations +
-// 32 KB of weights each) with direct-to-LDS buffer loads: every load
-// instruction reads 8 rows x 128 bytes (whole cache lines), the next stage is
-// in flight while the current one is computed, and no register holds staged
-// data.  LDS rows are 128 bytes; the 16-byte chunk c of row r sits at
-// position c ^ ((r >> 1) & 7), which keeps each 16-lane phase of a fragment
-// read on distinct banks.  A load instruction fills 1 KB of consecutive LDS
-// (lane L -> bytes 16 L), so lane L of block b loads row 8 b + L / 8, chunk
-// (L % 8) ^ swizzle.  The stage barrier and every LDS read are placed between
-// independent MFMA groups.
-template <int PHASE>
+// each wave 4 row tiles x 4 column tiles of MFMA 32x32x16 (wave row wm owns
+// the interleaved row tiles wm, wm + 2, wm + 4, wm + 6, so a partial M-tile
+// keeps both wave rows busy).  Both operands stream through a ring of NS LDS
+// stages of 32 k (16 KB of activations + 16 KB of weights) filled by
+// direct-to-LDS buffer loads; stages kt+1 .. kt+NS-1 are in flight while
+// stage kt is computed, and no register holds staged data.  LDS rows are 64
+// bytes; 16-byte chunk c of row r sits at position c ^ ((r >> 2) & 3), so
+// each 16-lane group of a fragment read covers all banks once.  A load
+// instruction fills 1 KB of consecutive LDS (lane L -> bytes 16 L): 16 rows x
+// 64 bytes, lane L taking row L / 4 and the chunk that lands at position
+// L % 4.  Fragment reads run one 16-k step ahead of the MFMAs; the stage
+// barrier sits between two independent MFMA groups.
+template <int PHASE, int NS>
 __global__ __launch_bounds__(FAT_THREADS, 1)
 void ffn_fat_dma_kernel(FfnArgs a) {
+    static_assert(NS >= 2 && NS - 1 <= 4, "ring depth outside the wait table");
     extern __shared__ u32x4 smem[];
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (SGPR)
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform (SGPR)
     const int wm = wave >> 1, wn = wave & 1;
     const int n = lane & 31, g = lane >> 5;
     const int K = PHASE == 1 ? a.H : a.I;
     const int N = PHASE == 1 ? a.I : a.H;
     constexpr int BN = PHASE == 1 ? 128 : 256;
     const int NT = N / BN;
-    const int n_mt = a.hdr->n_fat;
-    const int n_items = n_mt * NT;
-    const int KT = K / 64;
+    const int n_items = a.hdr->n_fat * NT;
+    const int KT = K / DMA_BK;
     const __amdgpu_buffer_rsrc_t asrc = PHASE == 1
-        ? make_rsrc(a.x, (uint32_t)(a.T * a.H * 2))
+        ? make_rsrc(a.x, (uint32_t)((size_t)a.T * a.H * 2))
         : make_rsrc(a.act, (uint32_t)((size_t)a.T * a.k * a.I * 2));
     const size_t wbytes = (size_t)a.I * a.H * 2;
-    // load roles of this lane: blocks 8 wave + q (q = 0..7) of each operand,
-    // row 8 (8 wave + q) + L/8 = 64 wave + 8 q + L/8, chunk (L%8) ^ swizzle
-    const int lrow = 64 * wave + (lane >> 3);             // + 8 q
-    // fragment read addresses (bytes inside a stage): A row wm*128 + ri*32 + n,
-    // B rows of this wave's four 32-row groups; chunk 2s + g, swizzled by (n>>1)&7
+    // load roles: instruction q of this wave fills rows 64 wave + 16 q + L/4;
+    // the chunk landing at position L%4 is (L%4) ^ ((row >> 2) & 3)
+    const int lrow = 64 * wave + (lane >> 2);
+    const uint32_t lch16 = (uint32_t)(((lane & 3) ^ ((lane >> 4) & 3)) * 16);
+    // fragment reads: A rows (2 ri + wm) 32 + n, B rows of the wave's four
+    // 32-row groups; chunk 2 s + g of the stage, swizzled by (n >> 2) & 3
     const uint32_t sbase = lds_addr(smem);
-    const int sw = (n >> 1) & 7;
     const int bg0 = PHASE == 1 ? wn * 64 : wn * 128;
-    const int bg1 = PHASE == 1 ? 128 + wn * 64 : wn * 128 + 64;
-    uint32_t aoffs[4], boffs[4][2];
+    uint32_t aoffs[2], boffs[2];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-        const uint32_t cpos = (uint32_t)(((2 * s + g) ^ sw) * 16);
-        aoffs[s] = (uint32_t)(wm * 128 + n) * 128 + cpos;
-        boffs[s][0] = DMA_A_BYTES + (uint32_t)(bg0 + n) * 128 + cpos;
-        boffs[s][1] = DMA_A_BYTES + (uint32_t)(bg1 + n) * 128 + cpos;
+    for (int s = 0; s < 2; ++s) {
+        const uint32_t cpos = (uint32_t)(((2 * s + g) ^ ((n >> 2) & 3)) * 16);
+        aoffs[s] = (uint32_t)(wm * 32 + n) * DMA_ROW + cpos;
+        boffs[s] = DMA_OPER + (uint32_t)(bg0 + n) * DMA_ROW + cpos;
     }
+    // B group offsets: phase 1 gate rows +0, +32 and up rows +128, +160
+    constexpr int B2 = PHASE == 1 ? 128 * DMA_ROW : 64 * DMA_ROW;
 
     for (int item = logical_block(); item < n_items; item += gridDim.x) {
         MTile t;
         int nt;
         fat_item(a.fat, item, NT, t, nt);
-        const int rtw = max(0, min(4, (t.rows - wm * 128 + 31) >> 5));
+        const int rtw = fat_row_tiles(t.rows, wm);
 
-        // per-lane byte offsets of the load sources (k = 0); rows past the tile
-        // repeat its last row (their results are never stored)
-        uint32_t aoff[8], boff[8];
-        __amdgpu_buffer_rsrc_t wsrc;
-        if (PHASE == 1) {
-            // waves 0-1 load gate rows, waves 2-3 the matching up rows
-            wsrc = make_rsrc((const char*)(wave < 2 ? a.wg : a.wu) + t.e * wbytes, (uint32_t)wbytes);
-        } else {
-            wsrc = make_rsrc((const char*)a.wd + t.e * wbytes, (uint32_t)wbytes);
-        }
+        // per-lane byte offsets of the load sources at k = 0; rows past the
+        // tile repeat its last row (their results are never stored)
+        uint32_t aoff[4], boff[4];
+        const __amdgpu_buffer_rsrc_t wsrc = PHASE == 1
+            ? make_rsrc((const char*)(wave < 2 ? a.wg : a.wu) + t.e * wbytes, (uint32_t)wbytes)  // gate | up rows
+            : make_rsrc((const char*)a.wd + t.e * wbytes, (uint32_t)wbytes);
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            const int row = lrow + 8 * q;
-            const int lch = (lane & 7) ^ ((row >> 1) & 7);   // global chunk landing at position L%8
+        for (int q = 0; q < 4; ++q) {
+            const int row = lrow + 16 * q;
             const int r = min(row, t.rows - 1);
             const uint32_t src = PHASE == 1 ? (uint32_t)(a.sorted_pair[t.row0 + r] / a.k) : (uint32_t)(t.row0 + r);
-            aoff[q] = src * (uint32_t)K * 2u + lch * 16;
+            aoff[q] = src * (uint32_t)K * 2u + lch16;
             const uint32_t wrow = PHASE == 1 ? (uint32_t)(nt * 128 + (row & 127)) : (uint32_t)(nt * 256 + row);
-            boff[q] = wrow * (uint32_t)K * 2u + lch * 16;
+            boff[q] = wrow * (uint32_t)K * 2u + lch16;
         }
 
         f32x16 acc[4][4];
@@ -575,29 +612,29 @@ void ffn_fat_dma_kernel(FfnArgs a) {
 #pragma unroll
             for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
 
-        auto issue = [&](int kt) {
-            u32x4* st = smem + (kt & 1) * (DMA_STAGE_BYTES / 16);
+        auto issue = [&](int kt, int slot) {
+            char* st = reinterpret_cast<char*>(smem) + slot * DMA_STAGE;
 #pragma unroll
-            for (int q = 0; q < 8; ++q)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(asrc, (lds_ptr_t)(st + (8 * wave + q) * 64), 16, aoff[q],
-                                                         kt * 128, 0, 0);
+            for (int q = 0; q < 4; ++q)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(asrc, (lds_ptr_t)(st + (4 * wave + q) * 1024), 16, aoff[q],
+                                                         kt * DMA_ROW, 0, 0);
 #pragma unroll
-            for (int q = 0; q < 8; ++q)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(wsrc, (lds_ptr_t)(st + DMA_A_BYTES / 16 + (8 * wave + q) * 64),
-                                                         16, boff[q], kt * 128, 0, 0);
+            for (int q = 0; q < 4; ++q)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(wsrc, (lds_ptr_t)(st + DMA_OPER + (4 * wave + q) * 1024),
+                                                         16, boff[q], kt * DMA_ROW, 0, 0);
         };
-        // fragment reads of one 16-k sub-step s of stage kt (8 x 16 bytes)
-        auto reads = [&](int kt, int s, u32x4 (&af)[4], u32x4 (&bf)[4]) {
-            const uint32_t st = sbase + (kt & 1) * DMA_STAGE_BYTES;
-            const uint32_t aa = st + aoffs[s], b0 = st + boffs[s][0], b1 = st + boffs[s][1];
+        // fragment reads of 16-k step s of the stage in `slot` (8 x 16 bytes)
+        auto reads = [&](int slot, int s, u32x4 (&af)[4], u32x4 (&bf)[4]) {
+            const uint32_t st = sbase + slot * DMA_STAGE;
+            const uint32_t aa = st + aoffs[s], bb = st + boffs[s];
             af[0] = ds_read16<0>(aa);
-            af[1] = ds_read16<4096>(aa);
-            af[2] = ds_read16<8192>(aa);
-            af[3] = ds_read16<12288>(aa);
-            bf[0] = ds_read16<0>(b0);
-            bf[1] = ds_read16<4096>(b0);
-            bf[2] = ds_read16<0>(b1);
-            bf[3] = ds_read16<4096>(b1);
+            af[1] = ds_read16<2 * 32 * DMA_ROW>(aa);
+            af[2] = ds_read16<4 * 32 * DMA_ROW>(aa);
+            af[3] = ds_read16<6 * 32 * DMA_ROW>(aa);
+            bf[0] = ds_read16<0>(bb);
+            bf[1] = ds_read16<32 * DMA_ROW>(bb);
+            bf[2] = ds_read16<B2>(bb);
+            bf[3] = ds_read16<B2 + 32 * DMA_ROW>(bb);
         };
         auto ready = [&](u32x4 (&af)[4], u32x4 (&bf)[4]) {
             lds_wait(af, bf);
@@ -615,14 +652,10 @@ void ffn_fat_dma_kernel(FfnArgs a) {
                 for (int cj = 0; cj < 4; ++cj) acc[ri][cj] = mma<PHASE>(af[ri], bf[cj], acc[ri][cj]);
         };
 
-        // prologue: stages 0 and 1 in flight, wait for stage 0
-        issue(0);
-        if (KT > 1) {
-            issue(1);
-            vm_wait<16>();
-        } else {
-            vm_wait<0>();
-        }
+        // prologue: the whole ring in flight, wait for stage 0
+        const int pro = min(NS, KT);
+        for (int s = 0; s < pro; ++s) issue(s, s);
+        vm_wait_stages(pro - 1);
         __builtin_amdgcn_s_barrier();
 
         auto kloop = [&](auto rt_c) {
@@ -631,31 +664,36 @@ void ffn_fat_dma_kernel(FfnArgs a) {
             using F = std::integral_constant<int, 4>;
             u32x4 x0[4], y0[4], x1[4], y1[4];
             reads(0, 0, x0, y0);
+            int slot = 0;
             for (int kt = 0; kt < KT; ++kt) {
-#pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    u32x4 (&ca)[4] = (s & 1) ? x1 : x0;
-                    u32x4 (&cb)[4] = (s & 1) ? y1 : y0;
-                    u32x4 (&na)[4] = (s & 1) ? x0 : x1;
-                    u32x4 (&nb)[4] = (s & 1) ? y0 : y1;
-                    ready(ca, cb);
-                    __builtin_amdgcn_sched_barrier(0);
-                    mfmas(rt_c, Z{}, H{}, ca, cb);
-                    __builtin_amdgcn_sched_barrier(0);
-                    if (s < 3) {
-                        reads(kt, s + 1, na, nb);
-                    } else if (kt + 1 < KT) {
-                        // end of stage kt: every wave has read all of it
-                        vm_wait<0>();                        // stage kt+1 landed (this lane's loads)
-                        __builtin_amdgcn_s_barrier();        // ... and every other lane's
-                        if (kt + 2 < KT) issue(kt + 2);      // refill the slot of stage kt
-                        reads(kt + 1, 0, na, nb);
-                    }
-                    __builtin_amdgcn_sched_barrier(0);
-                    mfmas(rt_c, H{}, F{}, ca, cb);
-                    __builtin_amdgcn_sched_barrier(0);
+                const int nslot = slot + 1 == NS ? 0 : slot + 1;
+                // step 0 of stage kt
+                ready(x0, y0);
+                __builtin_amdgcn_sched_barrier(0);
+                mfmas(rt_c, Z{}, H{}, x0, y0);
+                __builtin_amdgcn_sched_barrier(0);
+                reads(slot, 1, x1, y1);
+                __builtin_amdgcn_sched_barrier(0);
+                mfmas(rt_c, H{}, F{}, x0, y0);
+                __builtin_amdgcn_sched_barrier(0);
+                // step 1 of stage kt; every fragment of stage kt is then in registers
+                ready(x1, y1);
+                __builtin_amdgcn_sched_barrier(0);
+                mfmas(rt_c, Z{}, H{}, x1, y1);
+                __builtin_amdgcn_sched_barrier(0);
+                if (kt + 1 < KT) {
+                    vm_wait_stages(min(NS - 2, KT - 2 - kt));    // stage kt+1 landed (this lane's loads)
+                    __builtin_amdgcn_s_barrier();                // ... and every lane's; stage kt fully read
+                    if (kt + NS < KT) issue(kt + NS, slot);      // refill the slot of stage kt
+                    reads(nslot, 0, x0, y0);
                 }
+                __builtin_amdgcn_sched_barrier(0);
+                mfmas(rt_c, H{}, F{}, x1, y1);
+                __builtin_amdgcn_sched_barrier(0);
+                slot = nslot;
             }
+            __syncthreads();
+            fat_epilogue<PHASE, decltype(rt_c)::value>(a, acc, t, nt, smem);
         };
         switch (rtw) {
             case 4: kloop(std::integral_constant<int, 4>{}); break;
@@ -664,9 +702,6 @@ void ffn_fat_dma_kernel(FfnArgs a) {
             case 1: kloop(std::integral_constant<int, 1>{}); break;
             default: kloop(std::integral_constant<int, 0>{}); break;
         }
-        __syncthreads();
-
-        fat_epilogue<PHASE>(a, acc, t, nt, rtw, smem);
     }
 }
 
@@ -780,6 +815,7 @@ FfnLayout ffn_layout(int T, int E, int k, int H, int I) {
 
 struct DevInfo {
     int cus = 0;
+    int ring = 4;                               // LDS stages of the bf16 fat kernels (4 or 5)
     int thin_blocks[2][2][2] = {};              // [wfmt][phase-1][chunk width 2 / 4]
 };
 
@@ -806,11 +842,25 @@ hipError_t dev_info(DevInfo& out) {
         int cus = 0;
         err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
         if (err != hipSuccess) return err;
-        // the fat kernels use 128 KB of dynamic LDS (more than the default cap)
-        const void* fats[4] = {(const void*)ffn_fat_dma_kernel<1>, (const void*)ffn_fat_dma_kernel<2>,
-                               (const void*)ffn_fat_kernel<1, 1>, (const void*)ffn_fat_kernel<2, 1>};
-        for (const void* f : fats) {
-            err = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)FAT_LDS_BYTES);
+        // the fat kernels use 128 KB or more of dynamic LDS (above the default
+        // cap); the bf16 ones take a fifth 32 KB stage where a block may hold
+        // 160 KB
+        int lds_max = 0;
+        err = hipDeviceGetAttribute(&lds_max, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
+        if (err != hipSuccess) return err;
+        const struct {
+            const void* f;
+            size_t bytes;
+        } fats[6] = {{(const void*)ffn_fat_dma_kernel<1, 4>, dma_lds_bytes<4>()},
+                     {(const void*)ffn_fat_dma_kernel<2, 4>, dma_lds_bytes<4>()},
+                     {(const void*)ffn_fat_dma_kernel<1, 5>, dma_lds_bytes<5>()},
+                     {(const void*)ffn_fat_dma_kernel<2, 5>, dma_lds_bytes<5>()},
+                     {(const void*)ffn_fat_kernel<1, 1>, FAT_LDS_BYTES},
+                     {(const void*)ffn_fat_kernel<2, 1>, FAT_LDS_BYTES}};
+        d.ring = (size_t)lds_max >= dma_lds_bytes<5>() ? 5 : 4;
+        for (const auto& f : fats) {
+            if (f.bytes > (size_t)lds_max) continue;
+            err = hipFuncSetAttribute(f.f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)f.bytes);
             if (err != hipSuccess) return err;
         }
         d.thin_blocks[0][0][0] = thin_occupancy<1, 0, 2>();
@@ -850,8 +900,12 @@ FfnArgs make_args(const FfnLaunch& a) {
 template <int PHASE, int WFMT>
 void launch_phase_t(const FfnArgs& fa, const DevInfo& d, bool fat_possible, hipStream_t s) {
     if (fat_possible) {
-        if (WFMT == 0) ffn_fat_dma_kernel<PHASE><<<d.cus, FAT_THREADS, FAT_LDS_BYTES, s>>>(fa);
-        else ffn_fat_kernel<PHASE, WFMT><<<d.cus, FAT_THREADS, FAT_LDS_BYTES, s>>>(fa);
+        if constexpr (WFMT != 0)
+            ffn_fat_kernel<PHASE, WFMT><<<d.cus, FAT_THREADS, FAT_LDS_BYTES, s>>>(fa);
+        else if (d.ring == 5)
+            ffn_fat_dma_kernel<PHASE, 5><<<d.cus, FAT_THREADS, dma_lds_bytes<5>(), s>>>(fa);
+        else
+            ffn_fat_dma_kernel<PHASE, 4><<<d.cus, FAT_THREADS, dma_lds_bytes<4>(), s>>>(fa);
     }
     // whole 128-byte lines per row when each wave's quarter of K is a multiple of 64
     const int K = PHASE == 1 ? fa.H : fa.I;

@@ -52,7 +52,8 @@ def test_workspace_size(L):
     assert L.moe_workspace_size(4, 384, 8, 4096, 2048, 0) > 0
     for bad in [(0, 384, 8, 4096, 2048, 0), (4, 2000, 8, 4096, 2048, 0), (4, 384, 0, 4096, 2048, 0),
                 (4, 384, 33, 4096, 2048, 0), (4, 4, 5, 4096, 2048, 0), (4, 384, 8, 4000, 2048, 0),
-                (4, 384, 8, 4096, 2000, 0), (4, 384, 8, 4096, 2048, 5), (1 << 28, 384, 8, 4096, 2048, 0)]:
+                (4, 384, 8, 4096, 2000, 0), (4, 384, 8, 4096, 2048, 5), (1 << 28, 384, 8, 4096, 2048, 0),
+                (1 << 19, 384, 8, 4096, 2048, 0)]:
         assert L.moe_workspace_size(*bad) == 0, bad
 
 
@@ -92,6 +93,10 @@ def test_grouped_ffn_rejects(L):
     assert _ffn(L, wfmt=2) == moe.MOE_ERR_UNSUPPORTED
     assert _ffn(L, H=384) == moe.MOE_ERR_UNSUPPORTED
     assert _ffn(L, I=192) == moe.MOE_ERR_UNSUPPORTED
+    # 32-bit buffer offsets: x, the activation and one expert matrix stay below 4 GiB
+    assert _ffn(L, T=1 << 19, H=4096, I=128, k=1) == moe.MOE_ERR_UNSUPPORTED    # x = 4 GiB
+    assert _ffn(L, T=1 << 18, H=256, I=4096, k=2) == moe.MOE_ERR_UNSUPPORTED    # a = 4 GiB
+    assert _ffn(L, T=64, H=65536, I=32768, k=2) == moe.MOE_ERR_UNSUPPORTED      # W = 4 GiB
     assert _ffn(L, k=17) == moe.MOE_ERR_INVALID_ARG
     assert _ffn(L, ws=None) == moe.MOE_ERR_WORKSPACE
     assert _ffn(L, wsb=1024) == moe.MOE_ERR_WORKSPACE
