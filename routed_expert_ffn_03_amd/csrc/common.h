@@ -10,6 +10,7 @@ namespace moe {
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
 typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
 
@@ -58,8 +59,9 @@ __device__ __forceinline__ void stg16(void* p, u32x4 v) {
     *reinterpret_cast<u32x4*>(p) = v;
 }
 
+// silu(g) * u with the hardware reciprocal (1 ulp) in place of a division.
 __device__ __forceinline__ float silu_mul(float g, float u) {
-    return g / (1.0f + __expf(-g)) * u;
+    return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
 }
 
 // Inclusive prefix sum of one int per thread over a block of up to 1024

@@ -141,13 +141,11 @@ __device__ __forceinline__ u32x4 q3_decode8(uint32_t bits, uint32_t scale_bits) 
         const float v0 = fmaf((float)((bits >> (6 * i)) & 7u), s, m4);
         const float v1 = fmaf((float)((bits >> (6 * i + 3)) & 7u), s, m4);
         if (TO_F16) {
-            const _Float16 h0 = (_Float16)v0, h1 = (_Float16)v1;
-            r[i] = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+            const f16x2 h = {(_Float16)v0, (_Float16)v1};          // v_cvt_pk_f16_f32, nearest even
+            r[i] = __builtin_bit_cast(uint32_t, h);
         } else {
-            uint32_t u0 = __float_as_uint(v0), u1 = __float_as_uint(v1);
-            u0 += 0x7FFFu + ((u0 >> 16) & 1u);
-            u1 += 0x7FFFu + ((u1 >> 16) & 1u);
-            r[i] = (u0 >> 16) | (u1 & 0xFFFF0000u);
+            const bf16x2 b = {(__bf16)v0, (__bf16)v1};             // v_cvt_pk_bf16_f32, nearest even
+            r[i] = __builtin_bit_cast(uint32_t, b);
         }
     }
     return r;
@@ -497,18 +495,50 @@ __device__ __forceinline__ u32x4 ds_read16(uint32_t addr) {
     return v;
 }
 
-// Wait for this wave's outstanding LDS reads; the fragments are tied to the
-// wait so no use of them can be scheduled before it.
+// Wait until at most N of this wave's LDS reads are outstanding (they
+// complete in issue order); the fragments that wait is for are tied to it so
+// no use of them can be scheduled before it.
+template <int N = 0>
 __device__ __forceinline__ void lds_wait(u32x4 (&a)[4], u32x4 (&b)[4]) {
-    asm volatile("s_waitcnt lgkmcnt(0)"
+    asm volatile("s_waitcnt lgkmcnt(%8)"
                  : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(b[0]), "+v"(b[1]), "+v"(b[2]), "+v"(b[3])
-                 :
+                 : "n"(N)
                  : "memory");
 }
 
 template <int N>
 __device__ __forceinline__ void vm_wait() {
     asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>{}), ...);
+}
+
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// One 16-k step of a fat tile: MFMA slot i (row tile i / 4, column tile
+// i % 4) for the RT row tiles with data, each preceded by side(i); slots past
+// the last MFMA still run their side work, in order.  Scheduling barriers
+// keep exactly this order, so the side work (LDS reads, loads, the stage
+// barrier, 3-bit decode) issues while the MFMA before it executes instead of
+// stalling the matrix pipe.
+template <int PHASE, int RT, class Side>
+__device__ __forceinline__ void step_slots(f32x16 (&acc)[4][4], const u32x4 (&af)[4], const u32x4 (&bf)[4],
+                                           Side&& side) {
+    static_for<16>([&](auto i) {
+        constexpr int I = decltype(i)::value;
+        side(i);
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (I / 4 < RT) {
+            acc[I / 4][I % 4] = mma<PHASE>(af[I / 4], bf[I % 4], acc[I / 4][I % 4]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    });
 }
 
 constexpr int DMA_BK = 32;                                  // k per LDS stage
@@ -523,14 +553,16 @@ constexpr size_t dma_lds_bytes() {
 }
 
 // Wait until at most `stages` stages of this wave's loads are outstanding
-// (loads complete in issue order, DMA_LOADS per stage).
+// (loads complete in issue order, L load instructions per stage).
+template <int L>
 __device__ __forceinline__ void vm_wait_stages(int stages) {
     switch (stages) {
         case 0: vm_wait<0>(); break;
-        case 1: vm_wait<DMA_LOADS>(); break;
-        case 2: vm_wait<2 * DMA_LOADS>(); break;
-        case 3: vm_wait<3 * DMA_LOADS>(); break;
-        default: vm_wait<4 * DMA_LOADS>(); break;
+        case 1: vm_wait<L>(); break;
+        case 2: vm_wait<2 * L>(); break;
+        case 3: vm_wait<3 * L>(); break;
+        case 4: vm_wait<4 * L>(); break;
+        default: vm_wait<5 * L>(); break;
     }
 }
 
@@ -550,7 +582,7 @@ __device__ __forceinline__ void vm_wait_stages(int stages) {
 template <int PHASE, int NS>
 __global__ __launch_bounds__(FAT_THREADS, 1)
 void ffn_fat_dma_kernel(FfnArgs a) {
-    static_assert(NS >= 2 && NS - 1 <= 4, "ring depth outside the wait table");
+    static_assert(NS >= 2 && NS - 1 <= 5, "ring depth outside the wait table");
     extern __shared__ u32x4 smem[];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform (SGPR)
@@ -636,64 +668,56 @@ void ffn_fat_dma_kernel(FfnArgs a) {
             bf[2] = ds_read16<B2>(bb);
             bf[3] = ds_read16<B2 + 32 * DMA_ROW>(bb);
         };
-        auto ready = [&](u32x4 (&af)[4], u32x4 (&bf)[4]) {
-            lds_wait(af, bf);
-            if (PHASE == 2) {
-#pragma unroll
-                for (int cj = 0; cj < 4; ++cj) bf[cj] = bf16x8_to_f16x8(bf[cj]);
-            }
-        };
-        // MFMAs of row tiles [R0, R1) x all 4 column tiles
-        auto mfmas = [&](auto rt_c, auto r0_c, auto r1_c, const u32x4 (&af)[4], const u32x4 (&bf)[4]) {
-            constexpr int RT = decltype(rt_c)::value, R0 = decltype(r0_c)::value, R1 = decltype(r1_c)::value;
-#pragma unroll
-            for (int ri = R0; ri < (R1 < RT ? R1 : RT); ++ri)
-#pragma unroll
-                for (int cj = 0; cj < 4; ++cj) acc[ri][cj] = mma<PHASE>(af[ri], bf[cj], acc[ri][cj]);
-        };
-
         // prologue: the whole ring in flight, wait for stage 0
         const int pro = min(NS, KT);
         for (int s = 0; s < pro; ++s) issue(s, s);
-        vm_wait_stages(pro - 1);
+        vm_wait_stages<DMA_LOADS>(pro - 1);
         __builtin_amdgcn_s_barrier();
 
+        // per stage: step 0 issues step 1's fragment reads; step 1 waits for the
+        // next stage, passes the barrier (every wave is done with this stage),
+        // refills this stage's slot and reads the next stage's first step
         auto kloop = [&](auto rt_c) {
-            using Z = std::integral_constant<int, 0>;
-            using H = std::integral_constant<int, 2>;
-            using F = std::integral_constant<int, 4>;
+            constexpr int RT = decltype(rt_c)::value;
+            constexpr int BAR = RT;                      // step-1 slot of the stage barrier
             u32x4 x0[4], y0[4], x1[4], y1[4];
             reads(0, 0, x0, y0);
             int slot = 0;
-            for (int kt = 0; kt < KT; ++kt) {
+            // the last stage is peeled off so that `more` is a constant
+            auto stage = [&](int kt, auto more_c) {
+                constexpr bool more = decltype(more_c)::value;
                 const int nslot = slot + 1 == NS ? 0 : slot + 1;
-                // step 0 of stage kt
-                ready(x0, y0);
+                lds_wait<0>(x0, y0);
                 __builtin_amdgcn_sched_barrier(0);
-                mfmas(rt_c, Z{}, H{}, x0, y0);
+                step_slots<PHASE, RT>(acc, x0, y0, [&](auto i) {
+                    constexpr int I = decltype(i)::value;
+                    if constexpr (PHASE == 2 && I < 4) y0[I] = bf16x8_to_f16x8(y0[I]);
+                    if constexpr (I == 0) reads(slot, 1, x1, y1);
+                });
+                lds_wait<0>(x1, y1);
                 __builtin_amdgcn_sched_barrier(0);
-                reads(slot, 1, x1, y1);
-                __builtin_amdgcn_sched_barrier(0);
-                mfmas(rt_c, H{}, F{}, x0, y0);
-                __builtin_amdgcn_sched_barrier(0);
-                // step 1 of stage kt; every fragment of stage kt is then in registers
-                ready(x1, y1);
-                __builtin_amdgcn_sched_barrier(0);
-                mfmas(rt_c, Z{}, H{}, x1, y1);
-                __builtin_amdgcn_sched_barrier(0);
-                if (kt + 1 < KT) {
-                    vm_wait_stages(min(NS - 2, KT - 2 - kt));    // stage kt+1 landed (this lane's loads)
-                    __builtin_amdgcn_s_barrier();                // ... and every lane's; stage kt fully read
-                    if (kt + NS < KT) issue(kt + NS, slot);      // refill the slot of stage kt
-                    reads(nslot, 0, x0, y0);
-                }
-                __builtin_amdgcn_sched_barrier(0);
-                mfmas(rt_c, H{}, F{}, x1, y1);
-                __builtin_amdgcn_sched_barrier(0);
+                step_slots<PHASE, RT>(acc, x1, y1, [&](auto i) {
+                    constexpr int I = decltype(i)::value;
+                    if constexpr (PHASE == 2 && I < 4) y1[I] = bf16x8_to_f16x8(y1[I]);
+                    if constexpr (I == BAR) {
+                        if constexpr (more) {
+                            vm_wait_stages<DMA_LOADS>(min(NS - 2, KT - 2 - kt));   // stage kt+1 landed here
+                            __builtin_amdgcn_s_barrier();                          // ... and in every lane
+                        }
+                    }
+                    if constexpr (I == BAR + 1) {
+                        if (kt + NS < KT) issue(kt + NS, slot);                     // refill this stage's slot
+                    }
+                    if constexpr (I == BAR + 2) {
+                        if constexpr (more) reads(nslot, 0, x0, y0);
+                    }
+                });
                 slot = nslot;
-            }
+            };
+            for (int kt = 0; kt + 1 < KT; ++kt) stage(kt, std::true_type{});
+            stage(KT - 1, std::false_type{});
             __syncthreads();
-            fat_epilogue<PHASE, decltype(rt_c)::value>(a, acc, t, nt, smem);
+            fat_epilogue<PHASE, RT>(a, acc, t, nt, smem);
         };
         switch (rtw) {
             case 4: kloop(std::integral_constant<int, 4>{}); break;
@@ -701,6 +725,355 @@ void ffn_fat_dma_kernel(FfnArgs a) {
             case 2: kloop(std::integral_constant<int, 2>{}); break;
             case 1: kloop(std::integral_constant<int, 1>{}); break;
             default: kloop(std::integral_constant<int, 0>{}); break;
+        }
+    }
+}
+
+// ------------------------------------------------------------ fat kernel, 3-bit weights
+
+constexpr uint32_t Q3_RAW = FAT_BM * 16;                    // 4 words of each weight row per 32-k stage
+constexpr uint32_t Q3_SCL = FAT_BM * 4;                     // the dword holding each row's group scale
+constexpr uint32_t Q3_STAGE = DMA_OPER + Q3_RAW + Q3_SCL;   // activations + packed words + scales: 21 KB
+constexpr int Q3_LOADS = 6;                                 // load instructions per wave per stage
+
+template <int NS>
+constexpr size_t q3_lds_bytes() {
+    return (size_t)NS * Q3_STAGE > FAT_LDS_BYTES ? (size_t)NS * Q3_STAGE : FAT_LDS_BYTES;
+}
+
+__device__ __forceinline__ uint32_t ds_read4(uint32_t addr) {
+    uint32_t v;
+    asm volatile("ds_read_b32 %0, %1" : "=v"(v) : "v"(addr));
+    return v;
+}
+
+// Epilogue of the 1 x 4 tile: wave w holds every row tile of its 64 weight
+// rows (phase 1: 32 gate rows and the matching 32 up rows, i.e. 32 output
+// columns; phase 2: 64 output columns).  Passes of 64 rows through LDS,
+// 16-byte row stores.
+template <int PHASE, int RT>
+__device__ __forceinline__ void fat_epilogue_1x4(const FfnArgs& a, const f32x16 (&acc)[8][2], const MTile& t,
+                                                 int nt, u32x4* smem) {
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int n = lane & 31, g = lane >> 5;
+    const int N = PHASE == 1 ? a.I : a.H;
+    constexpr int OC = PHASE == 1 ? 32 : 64;            // output columns per wave
+    constexpr int LD = OC + 8;                          // staged row length (halves)
+    uint16_t* sO = reinterpret_cast<uint16_t*>(smem) + wave * 64 * LD;
+    uint16_t* dst = PHASE == 1 ? a.act : a.y;
+    const int col0 = PHASE == 1 ? nt * 128 + 32 * wave : nt * 256 + 64 * wave;
+    static_for<(RT + 1) / 2>([&](auto pass_c) {
+        constexpr int PASS = decltype(pass_c)::value;
+        static_for<2>([&](auto h_c) {
+            constexpr int H = decltype(h_c)::value, RI = 2 * PASS + H;
+            if constexpr (RI < RT) {
+                static_for<PHASE == 1 ? 1 : 2>([&](auto cj_c) {
+                    constexpr int CJ = decltype(cj_c)::value;
+                    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int m = H * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
+                        const float v = PHASE == 1 ? silu_mul(acc[RI][0][r], acc[RI][1][r]) : acc[RI][CJ][r];
+                        sO[m * LD + CJ * 32 + n] = f32_to_f16_bits(v);
+                    }
+                });
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        });
+        __syncthreads();
+        constexpr int LPR = OC / 8;                     // lanes per staged row
+#pragma unroll
+        for (int it = 0; it < LPR; ++it) {
+            const int m = it * (64 / LPR) + lane / LPR, ch = lane % LPR;
+            const int row = PASS * 64 + m;
+            if (row < t.rows)
+                stg16(dst + (size_t)(t.row0 + row) * N + col0 + ch * 8,
+                      *reinterpret_cast<const u32x4*>(sO + m * LD + ch * 8));
+        }
+        __syncthreads();
+    });
+}
+
+// One 16-k step of the 1 x 4 tile: MFMA slot i (row tile i / 2, column tile
+// i % 2) for the RT row tiles, each preceded by side(i), in exactly this order.
+template <int PHASE, int RT, class Side>
+__device__ __forceinline__ void step_slots_1x4(f32x16 (&acc)[8][2], const u32x4 (&af)[8], const u32x4 (&bf)[2],
+                                               Side&& side) {
+    static_for<16>([&](auto i) {
+        constexpr int I = decltype(i)::value;
+        side(i);
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (I / 2 < RT) {
+            acc[I / 2][I % 2] = mma<PHASE>(af[I / 2], bf[I % 2], acc[I / 2][I % 2]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    });
+}
+
+template <int N>
+__device__ __forceinline__ void lds_wait_tied(u32x4 (&v)[8]) {
+    asm volatile("s_waitcnt lgkmcnt(%8)"
+                 : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]), "+v"(v[6]), "+v"(v[7])
+                 : "n"(N)
+                 : "memory");
+}
+
+// The packed words and scale dwords one lane reads to decode its weights of
+// one stage: for 16-k step s and column tile c, the word holding its first
+// field (lo) and the next one (hi); the scale dword of each of its two rows.
+struct Q3Raw {
+    uint32_t lo[2][2], hi[2][2], sc[2];
+};
+
+// Fat tile for 3-bit weights: 256 rows x 256 weight rows with the four waves
+// side by side (1 x 4).  Wave w owns weight rows [64 w, 64 w + 64) of the tile
+// as two 32-row column tiles (phase 1: gate rows 32 w.. and the matching up
+// rows 128 + 32 w..) against every 32-row tile of the M-tile, so each wave
+// decodes exactly the weights its own MFMAs use, straight into operand
+// registers: no decoded weight passes through LDS, whose write bandwidth is
+// the scarce resource.  A ring stage carries the activations (16 KB,
+// swizzled 64-byte rows as in the bf16 kernel), the four packed words per
+// weight row that hold the stage's 32 k (4 KB) and each row's scale dword
+// (1 KB).  During stage kt every lane reads, for both of its weight rows and
+// both 16-k steps of stage kt+1, the word holding its first field and the
+// next one (two 4-byte LDS reads at a per-lane offset: field f sits in word
+// f / 10 at bit 3 (f % 10)), and decodes the 32 weights in 16 pieces placed
+// between the MFMAs of stage kt; one barrier per stage frees the ring slot
+// just read and confirms that the stage after next has landed.
+template <int PHASE, int NS>
+__global__ __launch_bounds__(FAT_THREADS, 1)
+void ffn_fat_q3_kernel(FfnArgs a) {
+    static_assert(NS >= 3 && NS - 1 <= 5, "ring depth outside the wait table");
+    extern __shared__ u32x4 smem[];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (SGPR)
+    const int n = lane & 31, g = lane >> 5;
+    const int K = PHASE == 1 ? a.H : a.I;
+    const int N = PHASE == 1 ? a.I : a.H;
+    constexpr int BN = PHASE == 1 ? 128 : 256;
+    const int NT = N / BN;
+    const int n_items = a.hdr->n_fat * NT;
+    const int KT = K / DMA_BK;                                // a multiple of 4 (K % 128 == 0)
+    const int GR = K >> 7;                                    // scale groups per weight row
+    const uint32_t row_bytes = (uint32_t)GR * (Q3_WORDS * 4);
+    const __amdgpu_buffer_rsrc_t asrc = PHASE == 1
+        ? make_rsrc(a.x, (uint32_t)((size_t)a.T * a.H * 2))
+        : make_rsrc(a.act, (uint32_t)((size_t)a.T * a.k * a.I * 2));
+    const size_t wmat = (size_t)a.I * a.H;
+    const size_t wbytes = wmat / 128 * Q3_WORDS * 4, sbytes = wmat / 128 * 2;
+    const int lrow = 64 * wave + (lane >> 2);
+    const uint32_t lch16 = (uint32_t)(((lane & 3) ^ ((lane >> 4) & 3)) * 16);
+    const uint32_t sbase = lds_addr(smem);
+    uint32_t aoffs[2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) aoffs[s] = (uint32_t)n * DMA_ROW + (uint32_t)(((2 * s + g) ^ ((n >> 2) & 3)) * 16);
+    // the two weight rows (tile rows) this lane decodes: column tiles 0 and 1
+    const int brow[2] = {PHASE == 1 ? 32 * wave + n : 64 * wave + n,
+                         PHASE == 1 ? 128 + 32 * wave + n : 64 * wave + 32 + n};
+
+    for (int item = logical_block(); item < n_items; item += gridDim.x) {
+        MTile t;
+        int nt;
+        fat_item(a.fat, item, NT, t, nt);
+        const int rt = (t.rows + 31) >> 5;                   // row tiles with data, the same for every wave
+
+        // waves 0-1 load gate rows, waves 2-3 the matching up rows (phase 1)
+        const char* wmatp = reinterpret_cast<const char*>(PHASE == 1 ? (wave < 2 ? a.wg : a.wu) : a.wd);
+        const char* smatp = reinterpret_cast<const char*>(PHASE == 1 ? (wave < 2 ? a.sg : a.su) : a.sd);
+        const __amdgpu_buffer_rsrc_t wsrc = make_rsrc(wmatp + t.e * wbytes, (uint32_t)wbytes);
+        const __amdgpu_buffer_rsrc_t ssrc = make_rsrc(smatp + t.e * sbytes, (uint32_t)sbytes);
+        uint32_t aoff[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int r = min(lrow + 16 * q, t.rows - 1);
+            const uint32_t src = PHASE == 1 ? (uint32_t)(a.sorted_pair[t.row0 + r] / a.k) : (uint32_t)(t.row0 + r);
+            aoff[q] = src * (uint32_t)K * 2u + lch16;
+        }
+        // this lane loads the words and the scale of tile row 64 wave + lane
+        const int lr = 64 * wave + lane;
+        const uint32_t lgr = PHASE == 1 ? (uint32_t)(nt * 128 + (lr & 127)) : (uint32_t)(nt * 256 + lr);
+        const uint32_t roff = lgr * row_bytes;
+        const uint32_t sidx = lgr * (uint32_t)GR;
+        // scale parity of the decoded rows: the scale of group grp sits in the
+        // high half of its dword when (row * GR + grp) is odd
+        uint32_t spar[2];
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            const uint32_t gr = PHASE == 1 ? (uint32_t)(nt * 128 + (brow[c] & 127)) : (uint32_t)(nt * 256 + brow[c]);
+            spar[c] = (gr * (uint32_t)GR) & 1u;
+        }
+
+        f32x16 acc[8][2];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+
+        auto issue = [&](int kt, int slot) {
+            char* st = reinterpret_cast<char*>(smem) + slot * Q3_STAGE;
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(asrc, (lds_ptr_t)(st + (4 * wave + q) * 1024), 16, aoff[q],
+                                                         kt * DMA_ROW, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(wsrc, (lds_ptr_t)(st + DMA_OPER + wave * 1024), 16, roff,
+                                                     (kt >> 2) * (Q3_WORDS * 4) + (kt & 3) * 12, 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ssrc, (lds_ptr_t)(st + DMA_OPER + Q3_RAW + wave * 256), 4,
+                                                     ((sidx + (uint32_t)(kt >> 2)) >> 1) * 4u, 0, 0, 0);
+        };
+        // A fragments of 16-k step s (row tiles 0..RT-1)
+        auto areads = [&](auto rt_c, int slot, int s, u32x4 (&af)[8]) {
+            constexpr int RT = decltype(rt_c)::value;
+            const uint32_t aa = sbase + slot * Q3_STAGE + aoffs[s];
+            static_for<RT>([&](auto r_c) {
+                constexpr int R = decltype(r_c)::value;
+                af[R] = ds_read16<R * 32 * DMA_ROW>(aa);
+            });
+        };
+        // packed words and scales of stage kt (in `slot`) for this lane; a
+        // `hi` word past the row's four (never used: its fields land above
+        // bit 23) is the next row's first word
+        auto rreads = [&](int slot, int kt, Q3Raw& rw) {
+            const uint32_t rb = sbase + slot * Q3_STAGE + DMA_OPER;
+            const int j = kt & 3;
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                const int f0 = 32 * j + 16 * s + 8 * g;        // first field (group-relative)
+                const uint32_t wo = (uint32_t)(f0 / 10 - 3 * j) * 4u;
+#pragma unroll
+                for (int c = 0; c < 2; ++c) {
+                    rw.lo[s][c] = ds_read4(rb + (uint32_t)brow[c] * 16u + wo);
+                    rw.hi[s][c] = ds_read4(rb + (uint32_t)brow[c] * 16u + wo + 4u);
+                }
+            }
+#pragma unroll
+            for (int c = 0; c < 2; ++c) rw.sc[c] = ds_read4(rb + Q3_RAW + (uint32_t)brow[c] * 4u);
+        };
+        auto rwait = [&](Q3Raw& rw) {
+            asm volatile("s_waitcnt lgkmcnt(0)"
+                         : "+v"(rw.lo[0][0]), "+v"(rw.lo[0][1]), "+v"(rw.lo[1][0]), "+v"(rw.lo[1][1]),
+                           "+v"(rw.hi[0][0]), "+v"(rw.hi[0][1]), "+v"(rw.hi[1][0]), "+v"(rw.hi[1][1]),
+                           "+v"(rw.sc[0]), "+v"(rw.sc[1])
+                         :
+                         : "memory");
+        };
+        // decode piece P of stage kt: chunk C = P / 4 (step C / 2, column tile
+        // C % 2), weights 2 Q and 2 Q + 1 of its 8 (Q = P % 4)
+        auto piece = [&](auto p_c, int kt, const Q3Raw& rw, uint32_t (&bits)[4], float (&sf)[2], float (&m4)[2],
+                         u32x4 (&bo)[2][2]) {
+            constexpr int P = decltype(p_c)::value, C = P / 4, Q = P % 4, S = C / 2, CJ = C % 2;
+            if constexpr (P == 0) {
+#pragma unroll
+                for (int c = 0; c < 2; ++c) {
+                    const uint32_t sb = ((spar[c] + (uint32_t)(kt >> 2)) & 1u) ? (rw.sc[c] >> 16) : (rw.sc[c] & 0xFFFFu);
+                    sf[c] = (float)__builtin_bit_cast(_Float16, (uint16_t)sb);
+                    m4[c] = -4.0f * sf[c];
+                }
+            }
+            if constexpr (Q == 0) {
+                const int sh = 3 * ((32 * (kt & 3) + 16 * S + 8 * g) % 10);
+                bits[C] = ((rw.lo[S][CJ] & 0x3FFFFFFFu) >> sh) | (rw.hi[S][CJ] << (30 - sh));
+            }
+            const float v0 = fmaf((float)((bits[C] >> (6 * Q)) & 7u), sf[CJ], m4[CJ]);
+            const float v1 = fmaf((float)((bits[C] >> (6 * Q + 3)) & 7u), sf[CJ], m4[CJ]);
+            if constexpr (PHASE == 2) {
+                const f16x2 h = {(_Float16)v0, (_Float16)v1};
+                bo[S][CJ][Q] = __builtin_bit_cast(uint32_t, h);
+            } else {
+                const bf16x2 h = {(__bf16)v0, (__bf16)v1};
+                bo[S][CJ][Q] = __builtin_bit_cast(uint32_t, h);
+            }
+        };
+
+        // prologue: the ring in flight; stages 0 and 1 landed; stage 0 decoded
+        const int pro = min(NS, KT);
+        for (int s = 0; s < pro; ++s) issue(s, s);
+        vm_wait_stages<Q3_LOADS>(pro - 2);
+        __builtin_amdgcn_s_barrier();
+        u32x4 B0[2][2], B1[2][2];
+        {
+            Q3Raw rw;
+            uint32_t bits[4];
+            float sf[2], m4[2];
+            rreads(0, 0, rw);
+            rwait(rw);
+            static_for<16>([&](auto p) { piece(p, 0, rw, bits, sf, m4, B0); });
+        }
+
+        auto kloop = [&](auto rt_c) {
+            constexpr int RT = decltype(rt_c)::value, S = 2 * RT;
+            constexpr int BAR = S / 4;                               // step-1 slot of the stage barrier
+            constexpr int DW = S >= 8 ? 3 : (S >= 4 ? 1 : 0);        // step-0 slot of the words' wait
+            constexpr int AV0 = S > DW + 1 ? S - DW - 1 : 0;         // decode slots in step 0
+            constexpr int AV = AV0 + BAR;                            // ... and in step 1
+            u32x4 x0[8], x1[8];
+            areads(rt_c, 0, 0, x0);
+            int slot = 0;
+            // stage kt computes with bc and decodes stage kt+1 into bn
+            auto stage = [&](int kt, auto more_c, u32x4 (&bc)[2][2], u32x4 (&bn)[2][2]) {
+                constexpr bool more = decltype(more_c)::value;
+                const int nslot = slot + 1 == NS ? 0 : slot + 1;
+                Q3Raw rw;
+                uint32_t bits[4];
+                float sf[2], m4[2];
+                auto pieces_at = [&](auto step_c, auto slot_c) {
+                    constexpr int STEP = decltype(step_c)::value, I = decltype(slot_c)::value;
+                    static_for<16>([&](auto p_c) {
+                        constexpr int P = decltype(p_c)::value;
+                        constexpr int G = AV > 0 ? P * AV / 16 : 0;
+                        constexpr int ST = (AV == 0 || G < AV0) ? 0 : 1;
+                        constexpr int SL = AV == 0 ? DW + 1 : (G < AV0 ? DW + 1 + G : G - AV0);
+                        if constexpr (more && ST == STEP && SL == I) piece(p_c, kt + 1, rw, bits, sf, m4, bn);
+                    });
+                };
+                using St0 = std::integral_constant<int, 0>;
+                using St1 = std::integral_constant<int, 1>;
+                lds_wait_tied<0>(x0);
+                __builtin_amdgcn_sched_barrier(0);
+                step_slots_1x4<PHASE, RT>(acc, x0, bc[0], [&](auto i) {
+                    constexpr int I = decltype(i)::value;
+                    if constexpr (I == 0) {
+                        areads(rt_c, slot, 1, x1);
+                        if constexpr (more) rreads(nslot, kt + 1, rw);
+                    }
+                    if constexpr (I == DW && more) rwait(rw);
+                    pieces_at(St0{}, i);
+                });
+                lds_wait_tied<0>(x1);
+                __builtin_amdgcn_sched_barrier(0);
+                step_slots_1x4<PHASE, RT>(acc, x1, bc[1], [&](auto i) {
+                    constexpr int I = decltype(i)::value;
+                    pieces_at(St1{}, i);
+                    if constexpr (I == BAR && more) {
+                        // the stage after next must have landed: it is decoded during the next stage
+                        vm_wait_stages<Q3_LOADS>(max(0, min(NS - 3, KT - 3 - kt)));
+                        __builtin_amdgcn_s_barrier();
+                    }
+                    if constexpr (I == BAR + 1) {
+                        if (kt + NS < KT) issue(kt + NS, slot);
+                    }
+                    if constexpr (I == BAR + 2 && more) areads(rt_c, nslot, 0, x0);
+                });
+                slot = nslot;
+            };
+            for (int kt = 0; kt + 2 < KT; kt += 2) {
+                stage(kt, std::true_type{}, B0, B1);
+                stage(kt + 1, std::true_type{}, B1, B0);
+            }
+            stage(KT - 2, std::true_type{}, B0, B1);
+            stage(KT - 1, std::false_type{}, B1, B0);
+            __syncthreads();
+            fat_epilogue_1x4<PHASE, RT>(a, acc, t, nt, smem);
+        };
+        switch (rt) {
+            case 8: kloop(std::integral_constant<int, 8>{}); break;
+            case 7: kloop(std::integral_constant<int, 7>{}); break;
+            case 6: kloop(std::integral_constant<int, 6>{}); break;
+            case 5: kloop(std::integral_constant<int, 5>{}); break;
+            case 4: kloop(std::integral_constant<int, 4>{}); break;
+            case 3: kloop(std::integral_constant<int, 3>{}); break;
+            case 2: kloop(std::integral_constant<int, 2>{}); break;
+            default: kloop(std::integral_constant<int, 1>{}); break;
         }
     }
 }
@@ -816,6 +1189,7 @@ FfnLayout ffn_layout(int T, int E, int k, int H, int I) {
 struct DevInfo {
     int cus = 0;
     int ring = 4;                               // LDS stages of the bf16 fat kernels (4 or 5)
+    int q3ring = 5;                             // LDS stages of the 3-bit fat kernels (5 or 6)
     int thin_blocks[2][2][2] = {};              // [wfmt][phase-1][chunk width 2 / 4]
 };
 
@@ -851,13 +1225,16 @@ hipError_t dev_info(DevInfo& out) {
         const struct {
             const void* f;
             size_t bytes;
-        } fats[6] = {{(const void*)ffn_fat_dma_kernel<1, 4>, dma_lds_bytes<4>()},
+        } fats[8] = {{(const void*)ffn_fat_dma_kernel<1, 4>, dma_lds_bytes<4>()},
                      {(const void*)ffn_fat_dma_kernel<2, 4>, dma_lds_bytes<4>()},
                      {(const void*)ffn_fat_dma_kernel<1, 5>, dma_lds_bytes<5>()},
                      {(const void*)ffn_fat_dma_kernel<2, 5>, dma_lds_bytes<5>()},
-                     {(const void*)ffn_fat_kernel<1, 1>, FAT_LDS_BYTES},
-                     {(const void*)ffn_fat_kernel<2, 1>, FAT_LDS_BYTES}};
+                     {(const void*)ffn_fat_q3_kernel<1, 5>, q3_lds_bytes<5>()},
+                     {(const void*)ffn_fat_q3_kernel<2, 5>, q3_lds_bytes<5>()},
+                     {(const void*)ffn_fat_q3_kernel<1, 6>, q3_lds_bytes<6>()},
+                     {(const void*)ffn_fat_q3_kernel<2, 6>, q3_lds_bytes<6>()}};
         d.ring = (size_t)lds_max >= dma_lds_bytes<5>() ? 5 : 4;
+        d.q3ring = (size_t)lds_max >= q3_lds_bytes<6>() ? 6 : 5;
         for (const auto& f : fats) {
             if (f.bytes > (size_t)lds_max) continue;
             err = hipFuncSetAttribute(f.f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)f.bytes);
@@ -900,9 +1277,12 @@ FfnArgs make_args(const FfnLaunch& a) {
 template <int PHASE, int WFMT>
 void launch_phase_t(const FfnArgs& fa, const DevInfo& d, bool fat_possible, hipStream_t s) {
     if (fat_possible) {
-        if constexpr (WFMT != 0)
-            ffn_fat_kernel<PHASE, WFMT><<<d.cus, FAT_THREADS, FAT_LDS_BYTES, s>>>(fa);
-        else if (d.ring == 5)
+        if constexpr (WFMT != 0) {
+            if (d.q3ring == 6)
+                ffn_fat_q3_kernel<PHASE, 6><<<d.cus, FAT_THREADS, q3_lds_bytes<6>(), s>>>(fa);
+            else
+                ffn_fat_q3_kernel<PHASE, 5><<<d.cus, FAT_THREADS, q3_lds_bytes<5>(), s>>>(fa);
+        } else if (d.ring == 5)
             ffn_fat_dma_kernel<PHASE, 5><<<d.cus, FAT_THREADS, dma_lds_bytes<5>(), s>>>(fa);
         else
             ffn_fat_dma_kernel<PHASE, 4><<<d.cus, FAT_THREADS, dma_lds_bytes<4>(), s>>>(fa);
