@@ -741,6 +741,15 @@ constexpr size_t q3_lds_bytes() {
     return (size_t)NS * Q3_STAGE > FAT_LDS_BYTES ? (size_t)NS * Q3_STAGE : FAT_LDS_BYTES;
 }
 
+// 3-bit field at bit OFF as one v_bfe_u32 (left to the compiler, a constant
+// offset becomes a shift, a mask and a byte conversion: one more instruction)
+template <int OFF>
+__device__ __forceinline__ uint32_t field3(uint32_t bits) {
+    uint32_t r;
+    asm("v_bfe_u32 %0, %1, %2, 3" : "=v"(r) : "v"(bits), "n"(OFF));
+    return r;
+}
+
 __device__ __forceinline__ uint32_t ds_read4(uint32_t addr) {
     uint32_t v;
     asm volatile("ds_read_b32 %0, %1" : "=v"(v) : "v"(addr));
@@ -974,8 +983,9 @@ void ffn_fat_q3_kernel(FfnArgs a) {
                 const int sh = 3 * ((32 * (kt & 3) + 16 * S + 8 * g) % 10);
                 bits[C] = ((rw.lo[S][CJ] & 0x3FFFFFFFu) >> sh) | (rw.hi[S][CJ] << (30 - sh));
             }
-            const float v0 = fmaf((float)((bits[C] >> (6 * Q)) & 7u), sf[CJ], m4[CJ]);
-            const float v1 = fmaf((float)((bits[C] >> (6 * Q + 3)) & 7u), sf[CJ], m4[CJ]);
+            // one bit-field extract, one conversion and one fma per weight
+            const float v0 = fmaf((float)field3<6 * Q>(bits[C]), sf[CJ], m4[CJ]);
+            const float v1 = fmaf((float)field3<6 * Q + 3>(bits[C]), sf[CJ], m4[CJ]);
             if constexpr (PHASE == 2) {
                 const f16x2 h = {(_Float16)v0, (_Float16)v1};
                 bo[S][CJ][Q] = __builtin_bit_cast(uint32_t, h);
