@@ -58,8 +58,6 @@ struct FfnHeader {
 
 constexpr int FAT_BM = 256;              // rows per fat M-tile
 constexpr int FAT_THREADS = 256;
-constexpr int FAT_STAGE = (FAT_BM + 256) * 8;            // 16-byte chunks per LDS stage (A + B)
-constexpr size_t FAT_LDS_BYTES = 2 * FAT_STAGE * 16;     // 128 KB: double-buffered stages / epilogue
 constexpr int THIN_BM = 32;
 constexpr int THIN_THREADS = 256;
 
@@ -214,43 +212,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-// One 16-byte staging chunk of a weight row (8 weights k..k+7) on its way
-// from memory to the LDS tile: raw bf16, or the 3-bit words it is decoded
-// from.  `row` is the row index inside one expert's matrix of K columns.
-template <int WFMT, int PHASE>
-struct WStage;
-
-template <int PHASE>
-struct WStage<0, PHASE> {
-    u32x4 raw;
-    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t w, __amdgpu_buffer_rsrc_t, uint32_t row, int K,
-                                         int k) {
-        raw = __builtin_amdgcn_raw_buffer_load_b128(w, (row * (uint32_t)K + k) * 2u, 0, 0);
-    }
-    __device__ __forceinline__ u32x4 value(int) const { return PHASE == 2 ? bf16x8_to_f16x8(raw) : raw; }
-};
-
-template <int PHASE>
-struct WStage<1, PHASE> {
-    uint32_t w0, w1, sc;
-    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t w, __amdgpu_buffer_rsrc_t s, uint32_t row, int K,
-                                         int k) {
-        const uint32_t grp = row * (uint32_t)(K >> 7) + (k >> 7);
-        const int wl = (k & 127) / 10;
-        const uint32_t base = grp * (Q3_WORDS * 4);
-        w0 = __builtin_amdgcn_raw_buffer_load_b32(w, base + wl * 4, 0, 0);
-        w1 = __builtin_amdgcn_raw_buffer_load_b32(w, base + (wl + 1 < Q3_WORDS ? wl + 1 : Q3_WORDS - 1) * 4, 0, 0);
-        sc = __builtin_amdgcn_raw_buffer_load_b32(s, (grp * 2) & ~3u, 0, 0) >> ((grp & 1) * 16);
-    }
-    __device__ __forceinline__ u32x4 value(int k) const {
-        const int f = k & 127;
-        const int n0 = f - (f / 10) * 10;
-        uint32_t bits = (w0 & 0x3FFFFFFFu) >> (3 * n0);
-        if (n0 > 2) bits |= w1 << (30 - 3 * n0);
-        return q3_decode8<PHASE == 2>(bits, sc & 0xFFFFu);
-    }
-};
-
 // Fat work item -> (M-tile, N-tile).  The items of one expert (count M-tiles
 // x NT N-tiles) are contiguous and walked in super-tiles of gm M-tiles x gn
 // N-tiles (gm * gn = 32, gm <= 8): blocks on one XCD take 32 consecutive
@@ -271,223 +232,13 @@ __device__ __forceinline__ void fat_item(const MTile* __restrict__ fat, int item
     nt = nb * gn + r % gnr;
 }
 
-// Row tiles of a fat M-tile owned by wave row wm: the tile's 32-row tiles are
-// dealt alternately to the two wave rows (tile 2 ri + wm is the wave's ri-th).
-__device__ __forceinline__ int fat_row_tiles(int rows, int wm) {
-    const int rt = (rows + 31) >> 5;
-    return max(0, min(4, (rt - wm + 1) >> 1));
-}
-
-// Fat-tile epilogue: two passes of 64 rows per wave through LDS, 16-byte row
-// stores (MFMA 32x32 output: lane holds column n, rows 8(r>>2) + 4g + (r&3)).
-// Pass p stages the wave's row tiles 2p and 2p + 1 (tile rows 32 (2 ri + wm)).
-// Phase 1 stores silu(gate) * up as fp16 activations, phase 2 fp16 y rows.
-// RTW (this wave's row tiles with data) is a compile-time constant, and the
-// epilogue runs inside the K-loop instantiation of that count, so the
-// accumulators never merge across instantiations (a merge would route all of
-// them through VGPRs).
-template <int PHASE, int RTW>
-__device__ __forceinline__ void fat_epilogue(const FfnArgs& a, const f32x16 (&acc)[4][4], const MTile& t, int nt,
-                                             u32x4* smem) {
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform (SGPR)
-    const int wm = wave >> 1, wn = wave & 1;
-    const int n = lane & 31, g = lane >> 5;
-    const int N = PHASE == 1 ? a.I : a.H;
-    constexpr int BN = PHASE == 1 ? 128 : 256;
-    constexpr int OC = PHASE == 1 ? 64 : 128;           // output columns per wave
-    constexpr int LD = OC + 8;                          // staged row length (halves)
-    uint16_t* sO = reinterpret_cast<uint16_t*>(smem) + wave * 64 * LD;
-    uint16_t* dst = PHASE == 1 ? a.act : a.y;
-    const int col0 = nt * BN + wn * OC;
-#pragma unroll
-    for (int pass = 0; pass < 2; ++pass) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int ri = pass * 2 + h;
-            if (ri < RTW) {
-#pragma unroll
-                for (int cj = 0; cj < (PHASE == 1 ? 2 : 4); ++cj) {
-                    // one accumulator tile at a time: keeps the compiler from
-                    // moving every accumulator into VGPRs at once
-                    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int m = h * 32 + 8 * (r >> 2) + 4 * g + (r & 3);
-                        const float v = PHASE == 1 ? silu_mul(acc[ri][cj][r], acc[ri][cj + 2][r]) : acc[ri][cj][r];
-                        sO[m * LD + cj * 32 + n] = f32_to_f16_bits(v);
-                    }
-                }
-                __builtin_amdgcn_sched_barrier(0);
-            }
-        }
-        __syncthreads();
-        constexpr int LPR = OC / 8;                     // lanes per staged row
-#pragma unroll
-        for (int it = 0; it < 64 * LPR / 64; ++it) {
-            const int m = it * (64 / LPR) + lane / LPR, ch = lane % LPR;
-            const int row = (2 * (pass * 2 + (m >> 5)) + wm) * 32 + (m & 31);
-            if (row < t.rows)
-                stg16(dst + (size_t)(t.row0 + row) * N + col0 + ch * 8,
-                      *reinterpret_cast<const u32x4*>(sO + m * LD + ch * 8));
-        }
-        __syncthreads();
-    }
-}
-
-// Fat tile: 256 rows x 256 weight rows x 64 k per stage, 4 waves as 2 x 2,
-// each wave 128 rows x 128 weight rows = 4 x 4 MFMA 32x32x16 accumulators
-// (256 accumulator registers).  Both operands are staged through LDS with
-// coalesced 128-byte row loads (8 lanes per row, buffer loads against one
-// resource per matrix so every per-thread address is a 32-bit offset); the
-// next stage's loads are in flight in registers while the current one is
-// computed, LDS is double-buffered (2 x 64 KB), one barrier per stage.
-// Phase 1's 256 weight rows are 128 gate rows followed by the matching 128 up
-// rows; wave column wn takes gate rows 64 wn.. and up rows 128 + 64 wn.., so
-// each wave applies SwiGLU to its own accumulators.
-template <int PHASE, int WFMT>
-__global__ __launch_bounds__(FAT_THREADS, 1)
-void ffn_fat_kernel(FfnArgs a) {
-    extern __shared__ u32x4 smem[];
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (SGPR)
-    const int wm = wave >> 1, wn = wave & 1;
-    const int n = lane & 31, g = lane >> 5;
-    const int K = PHASE == 1 ? a.H : a.I;
-    const int N = PHASE == 1 ? a.I : a.H;                 // outputs per row
-    constexpr int BN = PHASE == 1 ? 128 : 256;            // outputs per tile
-    const int NT = N / BN;
-    const int n_mt = a.hdr->n_fat;
-    const int n_items = n_mt * NT;
-    const int KT = K / 64;
-    // staging: thread t moves chunk c = t % 8 of rows t/8 + 32 i
-    const int c = tid & 7, rb = tid >> 3;
-    const int swz = (rb >> 1) & 7;                        // rows rb + 32 i share it
-    // this wave's 4 weight-row groups of 32 inside the tile
-    const int bg0 = PHASE == 1 ? wn * 64 : wn * 128;
-    const int bg1 = PHASE == 1 ? 128 + wn * 64 : wn * 128 + 64;
-    // activation source: x (gathered rows) or the fp16 activation
-    const __amdgpu_buffer_rsrc_t asrc = PHASE == 1
-        ? make_rsrc(a.x, (uint32_t)((size_t)a.T * a.H * 2))
-        : make_rsrc(a.act, (uint32_t)((size_t)a.T * a.k * a.I * 2));
-    const size_t wmat = (size_t)a.I * a.H;                // weights per matrix per expert
-    const size_t wbytes = WFMT == 0 ? wmat * 2 : wmat / 128 * Q3_WORDS * 4;
-    const size_t sbytes = wmat / 128 * 2;
-
-    for (int item = logical_block(); item < n_items; item += gridDim.x) {
-        MTile t;
-        int nt;
-        fat_item(a.fat, item, NT, t, nt);
-        const int rtw = fat_row_tiles(t.rows, wm);   // this wave's row tiles with data
-
-        // activation rows: byte offsets of 8 rows (rows past the tile repeat its
-        // last row; their results are never stored)
-        uint32_t aoff[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int r = min(rb + 32 * i, t.rows - 1);
-            const uint32_t src_row = PHASE == 1 ? (uint32_t)(a.sorted_pair[t.row0 + r] / a.k) : (uint32_t)(t.row0 + r);
-            aoff[i] = src_row * (uint32_t)K * 2u + c * 16;
-        }
-        // weight matrices of this expert
-        __amdgpu_buffer_rsrc_t wr0, wr1, sr0, sr1;
-        if (PHASE == 1) {
-            wr0 = make_rsrc((const char*)a.wg + t.e * wbytes, (uint32_t)wbytes);
-            wr1 = make_rsrc((const char*)a.wu + t.e * wbytes, (uint32_t)wbytes);
-            sr0 = make_rsrc(a.sg ? (const char*)a.sg + t.e * sbytes : nullptr, a.sg ? (uint32_t)sbytes : 0u);
-            sr1 = make_rsrc(a.su ? (const char*)a.su + t.e * sbytes : nullptr, a.su ? (uint32_t)sbytes : 0u);
-        } else {
-            wr0 = wr1 = make_rsrc((const char*)a.wd + t.e * wbytes, (uint32_t)wbytes);
-            sr0 = sr1 = make_rsrc(a.sd ? (const char*)a.sd + t.e * sbytes : nullptr, a.sd ? (uint32_t)sbytes : 0u);
-        }
-        const uint32_t brow0 = PHASE == 1 ? (uint32_t)(nt * 128 + rb) : (uint32_t)(nt * 256 + rb);
-
-        u32x4 ast[8];
-        WStage<WFMT, PHASE> bst[8];
-        f32x16 acc[4][4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
-
-        auto gload = [&](int kt) {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) ast[i] = __builtin_amdgcn_raw_buffer_load_b128(asrc, aoff[i], kt * 128, 0);
-            const int k = kt * 64 + c * 8;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                // phase 1: i < 4 are gate rows, i >= 4 the matching up rows
-                const uint32_t row = PHASE == 1 ? brow0 + 32 * (i & 3) : brow0 + 32 * i;
-                if (PHASE == 1 && i >= 4) bst[i].load(wr1, sr1, row, K, k);
-                else bst[i].load(wr0, sr0, row, K, k);
-            }
-        };
-        auto sstore = [&](int kt, int slot) {
-            u32x4* sA = smem + slot * FAT_STAGE;
-            u32x4* sB = sA + FAT_BM * 8;
-            const int k = kt * 64 + c * 8;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) sA[(rb + 32 * i) * 8 + (c ^ swz)] = ast[i];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) sB[(rb + 32 * i) * 8 + (c ^ swz)] = bst[i].value(k);
-        };
-        auto compute = [&](int slot, auto rt_c) {
-            constexpr int RT = decltype(rt_c)::value;           // row tiles with data (1..4)
-            const u32x4* sA = smem + slot * FAT_STAGE;
-            const u32x4* sB = sA + FAT_BM * 8;
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const int ch = 2 * s + g;
-                u32x4 af[4], bf[4];
-#pragma unroll
-                for (int ri = 0; ri < 4; ++ri) {
-                    const int r = (2 * ri + wm) * 32 + n;
-                    af[ri] = sA[r * 8 + (ch ^ ((r >> 1) & 7))];
-                }
-#pragma unroll
-                for (int cj = 0; cj < 4; ++cj) {
-                    const int r = ((cj >> 1) ? bg1 : bg0) + (cj & 1) * 32 + n;
-                    bf[cj] = sB[r * 8 + (ch ^ ((r >> 1) & 7))];
-                }
-#pragma unroll
-                for (int ri = 0; ri < RT; ++ri)
-#pragma unroll
-                    for (int cj = 0; cj < 4; ++cj) acc[ri][cj] = mma<PHASE>(af[ri], bf[cj], acc[ri][cj]);
-            }
-        };
-
-        // one stage in flight in registers while the other is computed from LDS
-        gload(0);
-        sstore(0, 0);
-        __syncthreads();
-        auto kloop = [&](auto rt_c) {
-            for (int kt = 0; kt < KT; ++kt) {
-                if (kt + 1 < KT) gload(kt + 1);
-                if (decltype(rt_c)::value > 0) compute(kt & 1, rt_c);
-                if (kt + 1 < KT) sstore(kt + 1, (kt + 1) & 1);
-                __syncthreads();
-            }
-            fat_epilogue<PHASE, decltype(rt_c)::value>(a, acc, t, nt, smem);
-        };
-        switch (rtw) {
-            case 4: kloop(std::integral_constant<int, 4>{}); break;
-            case 3: kloop(std::integral_constant<int, 3>{}); break;
-            case 2: kloop(std::integral_constant<int, 2>{}); break;
-            case 1: kloop(std::integral_constant<int, 1>{}); break;
-            default: kloop(std::integral_constant<int, 0>{}); break;
-        }
-    }
-}
-
-// ------------------------------------------------------------ fat kernel, bf16 weights
-
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)p; }
 
-// 16-byte LDS read issued as inline asm: the operand reads of the fat tile
-// must not wait on the direct-to-LDS loads of later stages that are still in
-// flight (the compiler would make every LDS read wait for all of them).
+// LDS reads issued as inline asm: the operand reads of the fat tile must not
+// wait on the direct-to-LDS loads of later stages that are still in flight
+// (the compiler would make every LDS read wait for all of them).
 template <int OFF>
 __device__ __forceinline__ u32x4 ds_read16(uint32_t addr) {
     u32x4 v;
@@ -495,13 +246,20 @@ __device__ __forceinline__ u32x4 ds_read16(uint32_t addr) {
     return v;
 }
 
-// Wait until at most N of this wave's LDS reads are outstanding (they
-// complete in issue order); the fragments that wait is for are tied to it so
-// no use of them can be scheduled before it.
-template <int N = 0>
-__device__ __forceinline__ void lds_wait(u32x4 (&a)[4], u32x4 (&b)[4]) {
-    asm volatile("s_waitcnt lgkmcnt(%8)"
-                 : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(b[0]), "+v"(b[1]), "+v"(b[2]), "+v"(b[3])
+__device__ __forceinline__ uint32_t ds_read4(uint32_t addr) {
+    uint32_t v;
+    asm volatile("ds_read_b32 %0, %1" : "=v"(v) : "v"(addr));
+    return v;
+}
+
+// Wait until at most N of this wave's LDS reads are outstanding; the operand
+// registers the wait is for are tied to it, so no use of them is scheduled
+// before it.
+template <int N>
+__device__ __forceinline__ void lds_wait_frag(u32x4 (&x)[8], u32x4 (&y)[2]) {
+    asm volatile("s_waitcnt lgkmcnt(%10)"
+                 : "+v"(x[0]), "+v"(x[1]), "+v"(x[2]), "+v"(x[3]), "+v"(x[4]), "+v"(x[5]), "+v"(x[6]), "+v"(x[7]),
+                   "+v"(y[0]), "+v"(y[1])
                  : "n"(N)
                  : "memory");
 }
@@ -509,47 +267,6 @@ __device__ __forceinline__ void lds_wait(u32x4 (&a)[4], u32x4 (&b)[4]) {
 template <int N>
 __device__ __forceinline__ void vm_wait() {
     asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
-}
-
-template <class F, int... I>
-__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
-    (f(std::integral_constant<int, I>{}), ...);
-}
-
-template <int N, class F>
-__device__ __forceinline__ void static_for(F&& f) {
-    static_for_impl(f, std::make_integer_sequence<int, N>{});
-}
-
-// One 16-k step of a fat tile: MFMA slot i (row tile i / 4, column tile
-// i % 4) for the RT row tiles with data, each preceded by side(i); slots past
-// the last MFMA still run their side work, in order.  Scheduling barriers
-// keep exactly this order, so the side work (LDS reads, loads, the stage
-// barrier, 3-bit decode) issues while the MFMA before it executes instead of
-// stalling the matrix pipe.
-template <int PHASE, int RT, class Side>
-__device__ __forceinline__ void step_slots(f32x16 (&acc)[4][4], const u32x4 (&af)[4], const u32x4 (&bf)[4],
-                                           Side&& side) {
-    static_for<16>([&](auto i) {
-        constexpr int I = decltype(i)::value;
-        side(i);
-        __builtin_amdgcn_sched_barrier(0);
-        if constexpr (I / 4 < RT) {
-            acc[I / 4][I % 4] = mma<PHASE>(af[I / 4], bf[I % 4], acc[I / 4][I % 4]);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-    });
-}
-
-constexpr int DMA_BK = 32;                                  // k per LDS stage
-constexpr uint32_t DMA_ROW = DMA_BK * 2;                    // bytes of one row per stage
-constexpr uint32_t DMA_OPER = FAT_BM * DMA_ROW;             // 16 KB: one operand of a stage
-constexpr uint32_t DMA_STAGE = 2 * DMA_OPER;                // activations + weights
-constexpr int DMA_LOADS = 8;                                // load instructions per wave per stage
-
-template <int NS>
-constexpr size_t dma_lds_bytes() {
-    return (size_t)NS * DMA_STAGE > FAT_LDS_BYTES ? (size_t)NS * DMA_STAGE : FAT_LDS_BYTES;
 }
 
 // Wait until at most `stages` stages of this wave's loads are outstanding
@@ -566,179 +283,14 @@ __device__ __forceinline__ void vm_wait_stages(int stages) {
     }
 }
 
-// Fat tile for bf16 weights: 256 rows x 256 weight rows, 4 waves as 2 x 2,
-// each wave 4 row tiles x 4 column tiles of MFMA 32x32x16 (wave row wm owns
-// the interleaved row tiles wm, wm + 2, wm + 4, wm + 6, so a partial M-tile
-// keeps both wave rows busy).  Both operands stream through a ring of NS LDS
-// stages of 32 k (16 KB of activations + 16 KB of weights) filled by
-// direct-to-LDS buffer loads; stages kt+1 .. kt+NS-1 are in flight while
-// stage kt is computed, and no register holds staged data.  LDS rows are 64
-// bytes; 16-byte chunk c of row r sits at position c ^ ((r >> 2) & 3), so
-// each 16-lane group of a fragment read covers all banks once.  A load
-// instruction fills 1 KB of consecutive LDS (lane L -> bytes 16 L): 16 rows x
-// 64 bytes, lane L taking row L / 4 and the chunk that lands at position
-// L % 4.  Fragment reads run one 16-k step ahead of the MFMAs; the stage
-// barrier sits between two independent MFMA groups.
-template <int PHASE, int NS>
-__global__ __launch_bounds__(FAT_THREADS, 1)
-void ffn_fat_dma_kernel(FfnArgs a) {
-    static_assert(NS >= 2 && NS - 1 <= 5, "ring depth outside the wait table");
-    extern __shared__ u32x4 smem[];
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform (SGPR)
-    const int wm = wave >> 1, wn = wave & 1;
-    const int n = lane & 31, g = lane >> 5;
-    const int K = PHASE == 1 ? a.H : a.I;
-    const int N = PHASE == 1 ? a.I : a.H;
-    constexpr int BN = PHASE == 1 ? 128 : 256;
-    const int NT = N / BN;
-    const int n_items = a.hdr->n_fat * NT;
-    const int KT = K / DMA_BK;
-    const __amdgpu_buffer_rsrc_t asrc = PHASE == 1
-        ? make_rsrc(a.x, (uint32_t)((size_t)a.T * a.H * 2))
-        : make_rsrc(a.act, (uint32_t)((size_t)a.T * a.k * a.I * 2));
-    const size_t wbytes = (size_t)a.I * a.H * 2;
-    // load roles: instruction q of this wave fills rows 64 wave + 16 q + L/4;
-    // the chunk landing at position L%4 is (L%4) ^ ((row >> 2) & 3)
-    const int lrow = 64 * wave + (lane >> 2);
-    const uint32_t lch16 = (uint32_t)(((lane & 3) ^ ((lane >> 4) & 3)) * 16);
-    // fragment reads: A rows (2 ri + wm) 32 + n, B rows of the wave's four
-    // 32-row groups; chunk 2 s + g of the stage, swizzled by (n >> 2) & 3
-    const uint32_t sbase = lds_addr(smem);
-    const int bg0 = PHASE == 1 ? wn * 64 : wn * 128;
-    uint32_t aoffs[2], boffs[2];
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-        const uint32_t cpos = (uint32_t)(((2 * s + g) ^ ((n >> 2) & 3)) * 16);
-        aoffs[s] = (uint32_t)(wm * 32 + n) * DMA_ROW + cpos;
-        boffs[s] = DMA_OPER + (uint32_t)(bg0 + n) * DMA_ROW + cpos;
-    }
-    // B group offsets: phase 1 gate rows +0, +32 and up rows +128, +160
-    constexpr int B2 = PHASE == 1 ? 128 * DMA_ROW : 64 * DMA_ROW;
-
-    for (int item = logical_block(); item < n_items; item += gridDim.x) {
-        MTile t;
-        int nt;
-        fat_item(a.fat, item, NT, t, nt);
-        const int rtw = fat_row_tiles(t.rows, wm);
-
-        // per-lane byte offsets of the load sources at k = 0; rows past the
-        // tile repeat its last row (their results are never stored)
-        uint32_t aoff[4], boff[4];
-        const __amdgpu_buffer_rsrc_t wsrc = PHASE == 1
-            ? make_rsrc((const char*)(wave < 2 ? a.wg : a.wu) + t.e * wbytes, (uint32_t)wbytes)  // gate | up rows
-            : make_rsrc((const char*)a.wd + t.e * wbytes, (uint32_t)wbytes);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int row = lrow + 16 * q;
-            const int r = min(row, t.rows - 1);
-            const uint32_t src = PHASE == 1 ? (uint32_t)(a.sorted_pair[t.row0 + r] / a.k) : (uint32_t)(t.row0 + r);
-            aoff[q] = src * (uint32_t)K * 2u + lch16;
-            const uint32_t wrow = PHASE == 1 ? (uint32_t)(nt * 128 + (row & 127)) : (uint32_t)(nt * 256 + row);
-            boff[q] = wrow * (uint32_t)K * 2u + lch16;
-        }
-
-        f32x16 acc[4][4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
-
-        auto issue = [&](int kt, int slot) {
-            char* st = reinterpret_cast<char*>(smem) + slot * DMA_STAGE;
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(asrc, (lds_ptr_t)(st + (4 * wave + q) * 1024), 16, aoff[q],
-                                                         kt * DMA_ROW, 0, 0);
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(wsrc, (lds_ptr_t)(st + DMA_OPER + (4 * wave + q) * 1024),
-                                                         16, boff[q], kt * DMA_ROW, 0, 0);
-        };
-        // fragment reads of 16-k step s of the stage in `slot` (8 x 16 bytes)
-        auto reads = [&](int slot, int s, u32x4 (&af)[4], u32x4 (&bf)[4]) {
-            const uint32_t st = sbase + slot * DMA_STAGE;
-            const uint32_t aa = st + aoffs[s], bb = st + boffs[s];
-            af[0] = ds_read16<0>(aa);
-            af[1] = ds_read16<2 * 32 * DMA_ROW>(aa);
-            af[2] = ds_read16<4 * 32 * DMA_ROW>(aa);
-            af[3] = ds_read16<6 * 32 * DMA_ROW>(aa);
-            bf[0] = ds_read16<0>(bb);
-            bf[1] = ds_read16<32 * DMA_ROW>(bb);
-            bf[2] = ds_read16<B2>(bb);
-            bf[3] = ds_read16<B2 + 32 * DMA_ROW>(bb);
-        };
-        // prologue: the whole ring in flight, wait for stage 0
-        const int pro = min(NS, KT);
-        for (int s = 0; s < pro; ++s) issue(s, s);
-        vm_wait_stages<DMA_LOADS>(pro - 1);
-        __builtin_amdgcn_s_barrier();
-
-        // per stage: step 0 issues step 1's fragment reads; step 1 waits for the
-        // next stage, passes the barrier (every wave is done with this stage),
-        // refills this stage's slot and reads the next stage's first step
-        auto kloop = [&](auto rt_c) {
-            constexpr int RT = decltype(rt_c)::value;
-            constexpr int BAR = RT;                      // step-1 slot of the stage barrier
-            u32x4 x0[4], y0[4], x1[4], y1[4];
-            reads(0, 0, x0, y0);
-            int slot = 0;
-            // the last stage is peeled off so that `more` is a constant
-            auto stage = [&](int kt, auto more_c) {
-                constexpr bool more = decltype(more_c)::value;
-                const int nslot = slot + 1 == NS ? 0 : slot + 1;
-                lds_wait<0>(x0, y0);
-                __builtin_amdgcn_sched_barrier(0);
-                step_slots<PHASE, RT>(acc, x0, y0, [&](auto i) {
-                    constexpr int I = decltype(i)::value;
-                    if constexpr (PHASE == 2 && I < 4) y0[I] = bf16x8_to_f16x8(y0[I]);
-                    if constexpr (I == 0) reads(slot, 1, x1, y1);
-                });
-                lds_wait<0>(x1, y1);
-                __builtin_amdgcn_sched_barrier(0);
-                step_slots<PHASE, RT>(acc, x1, y1, [&](auto i) {
-                    constexpr int I = decltype(i)::value;
-                    if constexpr (PHASE == 2 && I < 4) y1[I] = bf16x8_to_f16x8(y1[I]);
-                    if constexpr (I == BAR) {
-                        if constexpr (more) {
-                            vm_wait_stages<DMA_LOADS>(min(NS - 2, KT - 2 - kt));   // stage kt+1 landed here
-                            __builtin_amdgcn_s_barrier();                          // ... and in every lane
-                        }
-                    }
-                    if constexpr (I == BAR + 1) {
-                        if (kt + NS < KT) issue(kt + NS, slot);                     // refill this stage's slot
-                    }
-                    if constexpr (I == BAR + 2) {
-                        if constexpr (more) reads(nslot, 0, x0, y0);
-                    }
-                });
-                slot = nslot;
-            };
-            for (int kt = 0; kt + 1 < KT; ++kt) stage(kt, std::true_type{});
-            stage(KT - 1, std::false_type{});
-            __syncthreads();
-            fat_epilogue<PHASE, RT>(a, acc, t, nt, smem);
-        };
-        switch (rtw) {
-            case 4: kloop(std::integral_constant<int, 4>{}); break;
-            case 3: kloop(std::integral_constant<int, 3>{}); break;
-            case 2: kloop(std::integral_constant<int, 2>{}); break;
-            case 1: kloop(std::integral_constant<int, 1>{}); break;
-            default: kloop(std::integral_constant<int, 0>{}); break;
-        }
-    }
+template <class F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+    (f(std::integral_constant<int, I>{}), ...);
 }
 
-// ------------------------------------------------------------ fat kernel, 3-bit weights
-
-constexpr uint32_t Q3_RAW = FAT_BM * 16;                    // 4 words of each weight row per 32-k stage
-constexpr uint32_t Q3_SCL = FAT_BM * 4;                     // the dword holding each row's group scale
-constexpr uint32_t Q3_STAGE = DMA_OPER + Q3_RAW + Q3_SCL;   // activations + packed words + scales: 21 KB
-constexpr int Q3_LOADS = 6;                                 // load instructions per wave per stage
-
-template <int NS>
-constexpr size_t q3_lds_bytes() {
-    return (size_t)NS * Q3_STAGE > FAT_LDS_BYTES ? (size_t)NS * Q3_STAGE : FAT_LDS_BYTES;
+template <int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
 // 3-bit field at bit OFF as one v_bfe_u32 (left to the compiler, a constant
@@ -750,19 +302,46 @@ __device__ __forceinline__ uint32_t field3(uint32_t bits) {
     return r;
 }
 
-__device__ __forceinline__ uint32_t ds_read4(uint32_t addr) {
-    uint32_t v;
-    asm volatile("ds_read_b32 %0, %1" : "=v"(v) : "v"(addr));
-    return v;
+constexpr int DMA_BK = 32;                                  // k per LDS stage
+constexpr uint32_t DMA_ROW = DMA_BK * 2;                    // bytes of one row per stage
+constexpr uint32_t DMA_OPER = FAT_BM * DMA_ROW;             // 16 KB: 256 rows of one operand
+
+// Ring stage layout of the fat kernel per weight format.  bf16: activations
+// and weight rows, 16 KB each, 64-byte rows.  3-bit: activations, the four
+// packed words of each weight row that hold the stage's 32 k (16 bytes) and
+// the dword holding the row's group scale.  LOADS: load instructions per wave
+// per stage; AHEAD: how many stages past the one being computed must have
+// landed at its barrier (the 3-bit kernel decodes one stage ahead).
+template <int WFMT>
+struct FatStage;
+template <>
+struct FatStage<0> {
+    static constexpr uint32_t BYTES = 2 * DMA_OPER;
+    static constexpr int LOADS = 8, AHEAD = 1;
+};
+template <>
+struct FatStage<1> {
+    static constexpr uint32_t RAW = FAT_BM * 16, SCL = FAT_BM * 4;
+    static constexpr uint32_t BYTES = DMA_OPER + RAW + SCL;
+    static constexpr int LOADS = 6, AHEAD = 2;
+};
+
+template <int WFMT, int NS>
+constexpr size_t fat_lds_bytes() {
+    return (size_t)NS * FatStage<WFMT>::BYTES;
 }
 
-// Epilogue of the 1 x 4 tile: wave w holds every row tile of its 64 weight
-// rows (phase 1: 32 gate rows and the matching 32 up rows, i.e. 32 output
-// columns; phase 2: 64 output columns).  Passes of 64 rows through LDS,
-// 16-byte row stores.
+// Epilogue: wave w holds every row tile of its 64 weight rows (phase 1: 32
+// gate rows and the matching 32 up rows, i.e. 32 output columns; phase 2: 64
+// output columns).  Passes of 64 rows through LDS, 16-byte row stores (MFMA
+// 32x32 output: lane holds column n, rows 8 (r >> 2) + 4 g + (r & 3)).  Phase
+// 1 stores silu(gate) * up as fp16 activations, phase 2 fp16 y rows.  RT is a
+// compile-time constant and the epilogue runs inside the K-loop instantiation
+// of that count, so the accumulators never merge across instantiations (a
+// merge would route all of them through VGPRs).
 template <int PHASE, int RT>
-__device__ __forceinline__ void fat_epilogue_1x4(const FfnArgs& a, const f32x16 (&acc)[8][2], const MTile& t,
-                                                 int nt, u32x4* smem) {
+__device__ __forceinline__ void fat_epilogue(const FfnArgs& a, const f32x16 (&acc)[8][2], const MTile& t, int nt,
+                                             u32x4* smem) {
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int n = lane & 31, g = lane >> 5;
@@ -804,11 +383,14 @@ __device__ __forceinline__ void fat_epilogue_1x4(const FfnArgs& a, const f32x16 
     });
 }
 
-// One 16-k step of the 1 x 4 tile: MFMA slot i (row tile i / 2, column tile
-// i % 2) for the RT row tiles, each preceded by side(i), in exactly this order.
+// One 16-k step: MFMA slot i (row tile i / 2, column tile i % 2) for the RT
+// row tiles, each preceded by side(i); slots past the last MFMA still run
+// their side work, in order.  Scheduling barriers keep exactly this order,
+// so the side work (LDS reads, loads, the stage barrier, conversions, 3-bit
+// decode) issues while the MFMA before it executes.
 template <int PHASE, int RT, class Side>
-__device__ __forceinline__ void step_slots_1x4(f32x16 (&acc)[8][2], const u32x4 (&af)[8], const u32x4 (&bf)[2],
-                                               Side&& side) {
+__device__ __forceinline__ void step_slots(f32x16 (&acc)[8][2], const u32x4 (&af)[8], const u32x4 (&bf)[2],
+                                           Side&& side) {
     static_for<16>([&](auto i) {
         constexpr int I = decltype(i)::value;
         side(i);
@@ -820,14 +402,6 @@ __device__ __forceinline__ void step_slots_1x4(f32x16 (&acc)[8][2], const u32x4 
     });
 }
 
-template <int N>
-__device__ __forceinline__ void lds_wait_tied(u32x4 (&v)[8]) {
-    asm volatile("s_waitcnt lgkmcnt(%8)"
-                 : "+v"(v[0]), "+v"(v[1]), "+v"(v[2]), "+v"(v[3]), "+v"(v[4]), "+v"(v[5]), "+v"(v[6]), "+v"(v[7])
-                 : "n"(N)
-                 : "memory");
-}
-
 // The packed words and scale dwords one lane reads to decode its weights of
 // one stage: for 16-k step s and column tile c, the word holding its first
 // field (lo) and the next one (hi); the scale dword of each of its two rows.
@@ -835,25 +409,31 @@ struct Q3Raw {
     uint32_t lo[2][2], hi[2][2], sc[2];
 };
 
-// Fat tile for 3-bit weights: 256 rows x 256 weight rows with the four waves
-// side by side (1 x 4).  Wave w owns weight rows [64 w, 64 w + 64) of the tile
-// as two 32-row column tiles (phase 1: gate rows 32 w.. and the matching up
-// rows 128 + 32 w..) against every 32-row tile of the M-tile, so each wave
-// decodes exactly the weights its own MFMAs use, straight into operand
-// registers: no decoded weight passes through LDS, whose write bandwidth is
-// the scarce resource.  A ring stage carries the activations (16 KB,
-// swizzled 64-byte rows as in the bf16 kernel), the four packed words per
-// weight row that hold the stage's 32 k (4 KB) and each row's scale dword
-// (1 KB).  During stage kt every lane reads, for both of its weight rows and
-// both 16-k steps of stage kt+1, the word holding its first field and the
-// next one (two 4-byte LDS reads at a per-lane offset: field f sits in word
-// f / 10 at bit 3 (f % 10)), and decodes the 32 weights in 16 pieces placed
-// between the MFMAs of stage kt; one barrier per stage frees the ring slot
-// just read and confirms that the stage after next has landed.
-template <int PHASE, int NS>
+// Fat tile: 256 rows x 256 weight rows with the four waves side by side
+// (1 x 4).  Wave w owns weight rows [64 w, 64 w + 64) of the tile as two
+// 32-row column tiles (phase 1: gate rows 32 w.. and the matching up rows
+// 128 + 32 w.., so SwiGLU is applied in registers) against every 32-row tile
+// of the M-tile; all waves therefore have the same number of row tiles, and
+// each wave prepares only the weight operands its own MFMAs use (the bf16 ->
+// fp16 conversion of phase 2, or the 3-bit decode).  Operands stream through
+// a ring of NS stages of 32 k filled by direct-to-LDS buffer loads (16 rows x
+// 64 bytes per instruction for activations and bf16 weights); LDS rows are 64
+// bytes with the 16-byte chunk c of row r at position c ^ ((r >> 2) & 3), so
+// each 16-lane group of a fragment read covers all banks once.  Stages
+// kt+1 .. kt+NS-1 are in flight while stage kt is computed; one barrier per
+// stage frees the slot just read.
+//
+// 3-bit weights: during stage kt every lane reads, for both of its weight rows
+// and both 16-k steps of stage kt+1, the packed word holding its first field
+// and the next one (field f of a group sits in word f / 10 at bit 3 (f % 10)),
+// and decodes the 32 weights (scale * (field - 4), exact in fp32, rounded once)
+// in 16 pieces placed between the MFMAs of stage kt.  No decoded weight goes
+// through LDS: b128 LDS writes are the scarce LDS resource.
+template <int PHASE, int WFMT, int NS>
 __global__ __launch_bounds__(FAT_THREADS, 1)
-void ffn_fat_q3_kernel(FfnArgs a) {
-    static_assert(NS >= 3 && NS - 1 <= 5, "ring depth outside the wait table");
+void ffn_fat_kernel(FfnArgs a) {
+    using Stage = FatStage<WFMT>;
+    static_assert(NS >= 2 + Stage::AHEAD - 1 && NS - 1 <= 5, "ring depth outside the wait table");
     extern __shared__ u32x4 smem[];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform (SGPR)
@@ -864,20 +444,24 @@ void ffn_fat_q3_kernel(FfnArgs a) {
     const int NT = N / BN;
     const int n_items = a.hdr->n_fat * NT;
     const int KT = K / DMA_BK;                                // a multiple of 4 (K % 128 == 0)
-    const int GR = K >> 7;                                    // scale groups per weight row
-    const uint32_t row_bytes = (uint32_t)GR * (Q3_WORDS * 4);
     const __amdgpu_buffer_rsrc_t asrc = PHASE == 1
         ? make_rsrc(a.x, (uint32_t)((size_t)a.T * a.H * 2))
         : make_rsrc(a.act, (uint32_t)((size_t)a.T * a.k * a.I * 2));
     const size_t wmat = (size_t)a.I * a.H;
-    const size_t wbytes = wmat / 128 * Q3_WORDS * 4, sbytes = wmat / 128 * 2;
+    const size_t wbytes = WFMT == 0 ? wmat * 2 : wmat / 128 * Q3_WORDS * 4;
+    const size_t sbytes = wmat / 128 * 2;
+    const int GR = K >> 7;                                    // 3-bit scale groups per weight row
+    const uint32_t q3_row_bytes = (uint32_t)GR * (Q3_WORDS * 4);
+    // load roles: instruction q of this wave fills rows 64 wave + 16 q + L/4 of
+    // an operand; the chunk landing at position L%4 is (L%4) ^ ((row >> 2) & 3)
     const int lrow = 64 * wave + (lane >> 2);
     const uint32_t lch16 = (uint32_t)(((lane & 3) ^ ((lane >> 4) & 3)) * 16);
     const uint32_t sbase = lds_addr(smem);
+    // fragment reads: chunk 2 s + g of row r, swizzled by (r >> 2) & 3 = (n >> 2) & 3
     uint32_t aoffs[2];
 #pragma unroll
     for (int s = 0; s < 2; ++s) aoffs[s] = (uint32_t)n * DMA_ROW + (uint32_t)(((2 * s + g) ^ ((n >> 2) & 3)) * 16);
-    // the two weight rows (tile rows) this lane decodes: column tiles 0 and 1
+    // the two weight rows (tile rows) of this lane's B operands: column tiles 0 and 1
     const int brow[2] = {PHASE == 1 ? 32 * wave + n : 64 * wave + n,
                          PHASE == 1 ? 128 + 32 * wave + n : 64 * wave + 32 + n};
 
@@ -889,28 +473,35 @@ void ffn_fat_q3_kernel(FfnArgs a) {
 
         // waves 0-1 load gate rows, waves 2-3 the matching up rows (phase 1)
         const char* wmatp = reinterpret_cast<const char*>(PHASE == 1 ? (wave < 2 ? a.wg : a.wu) : a.wd);
-        const char* smatp = reinterpret_cast<const char*>(PHASE == 1 ? (wave < 2 ? a.sg : a.su) : a.sd);
         const __amdgpu_buffer_rsrc_t wsrc = make_rsrc(wmatp + t.e * wbytes, (uint32_t)wbytes);
-        const __amdgpu_buffer_rsrc_t ssrc = make_rsrc(smatp + t.e * sbytes, (uint32_t)sbytes);
-        uint32_t aoff[4];
+        // activation rows and bf16 weight rows this lane loads (rows past the
+        // M-tile repeat its last row; their results are never stored)
+        uint32_t aoff[4], boff[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            const int r = min(lrow + 16 * q, t.rows - 1);
+            const int row = lrow + 16 * q;
+            const int r = min(row, t.rows - 1);
             const uint32_t src = PHASE == 1 ? (uint32_t)(a.sorted_pair[t.row0 + r] / a.k) : (uint32_t)(t.row0 + r);
             aoff[q] = src * (uint32_t)K * 2u + lch16;
+            const uint32_t wrow = PHASE == 1 ? (uint32_t)(nt * 128 + (row & 127)) : (uint32_t)(nt * 256 + row);
+            boff[q] = wrow * (uint32_t)K * 2u + lch16;
         }
-        // this lane loads the words and the scale of tile row 64 wave + lane
-        const int lr = 64 * wave + lane;
-        const uint32_t lgr = PHASE == 1 ? (uint32_t)(nt * 128 + (lr & 127)) : (uint32_t)(nt * 256 + lr);
-        const uint32_t roff = lgr * row_bytes;
-        const uint32_t sidx = lgr * (uint32_t)GR;
-        // scale parity of the decoded rows: the scale of group grp sits in the
-        // high half of its dword when (row * GR + grp) is odd
-        uint32_t spar[2];
+        // 3-bit: this lane loads the words and the scale of tile row 64 wave + lane
+        __amdgpu_buffer_rsrc_t ssrc = wsrc;
+        uint32_t roff = 0, sidx = 0, spar[2] = {0, 0};
+        if constexpr (WFMT == 1) {
+            const char* smatp = reinterpret_cast<const char*>(PHASE == 1 ? (wave < 2 ? a.sg : a.su) : a.sd);
+            ssrc = make_rsrc(smatp + t.e * sbytes, (uint32_t)sbytes);
+            const int lr = 64 * wave + lane;
+            const uint32_t lgr = PHASE == 1 ? (uint32_t)(nt * 128 + (lr & 127)) : (uint32_t)(nt * 256 + lr);
+            roff = lgr * q3_row_bytes;
+            sidx = lgr * (uint32_t)GR;
+            // the scale of group grp sits in the high half of its dword when (row * GR + grp) is odd
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
-            const uint32_t gr = PHASE == 1 ? (uint32_t)(nt * 128 + (brow[c] & 127)) : (uint32_t)(nt * 256 + brow[c]);
-            spar[c] = (gr * (uint32_t)GR) & 1u;
+            for (int c = 0; c < 2; ++c) {
+                const uint32_t gr = PHASE == 1 ? (uint32_t)(nt * 128 + (brow[c] & 127)) : (uint32_t)(nt * 256 + brow[c]);
+                spar[c] = (gr * (uint32_t)GR) & 1u;
+            }
         }
 
         f32x16 acc[8][2];
@@ -920,30 +511,45 @@ void ffn_fat_q3_kernel(FfnArgs a) {
             for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
 
         auto issue = [&](int kt, int slot) {
-            char* st = reinterpret_cast<char*>(smem) + slot * Q3_STAGE;
+            char* st = reinterpret_cast<char*>(smem) + slot * Stage::BYTES;
 #pragma unroll
             for (int q = 0; q < 4; ++q)
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(asrc, (lds_ptr_t)(st + (4 * wave + q) * 1024), 16, aoff[q],
                                                          kt * DMA_ROW, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(wsrc, (lds_ptr_t)(st + DMA_OPER + wave * 1024), 16, roff,
-                                                     (kt >> 2) * (Q3_WORDS * 4) + (kt & 3) * 12, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(ssrc, (lds_ptr_t)(st + DMA_OPER + Q3_RAW + wave * 256), 4,
-                                                     ((sidx + (uint32_t)(kt >> 2)) >> 1) * 4u, 0, 0, 0);
+            if constexpr (WFMT == 0) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(wsrc, (lds_ptr_t)(st + DMA_OPER + (4 * wave + q) * 1024),
+                                                             16, boff[q], kt * DMA_ROW, 0, 0);
+            } else {
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(wsrc, (lds_ptr_t)(st + DMA_OPER + wave * 1024), 16, roff,
+                                                         (kt >> 2) * (Q3_WORDS * 4) + (kt & 3) * 12, 0, 0);
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(ssrc, (lds_ptr_t)(st + DMA_OPER + Stage::RAW + wave * 256), 4,
+                                                         ((sidx + (uint32_t)(kt >> 2)) >> 1) * 4u, 0, 0, 0);
+            }
         };
-        // A fragments of 16-k step s (row tiles 0..RT-1)
-        auto areads = [&](auto rt_c, int slot, int s, u32x4 (&af)[8]) {
+        // activation fragments of 16-k step s (row tiles 0..RT-1) and, for
+        // bf16 weights, the two weight fragments
+        auto reads = [&](auto rt_c, int slot, int s, u32x4 (&af)[8], u32x4 (&bf)[2]) {
             constexpr int RT = decltype(rt_c)::value;
-            const uint32_t aa = sbase + slot * Q3_STAGE + aoffs[s];
+            const uint32_t st = sbase + slot * Stage::BYTES;
+            const uint32_t aa = st + aoffs[s];
             static_for<RT>([&](auto r_c) {
                 constexpr int R = decltype(r_c)::value;
                 af[R] = ds_read16<R * 32 * DMA_ROW>(aa);
             });
+            if constexpr (WFMT == 0) {
+#pragma unroll
+                for (int c = 0; c < 2; ++c)
+                    bf[c] = ds_read16<0>(st + DMA_OPER + (uint32_t)brow[c] * DMA_ROW +
+                                         (uint32_t)(((2 * s + g) ^ ((n >> 2) & 3)) * 16));
+            }
         };
-        // packed words and scales of stage kt (in `slot`) for this lane; a
-        // `hi` word past the row's four (never used: its fields land above
+        // 3-bit: packed words and scales of stage kt (in `slot`) for this lane;
+        // a `hi` word past the row's four (never used: its fields land above
         // bit 23) is the next row's first word
         auto rreads = [&](int slot, int kt, Q3Raw& rw) {
-            const uint32_t rb = sbase + slot * Q3_STAGE + DMA_OPER;
+            const uint32_t rb = sbase + slot * Stage::BYTES + DMA_OPER;
             const int j = kt & 3;
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
@@ -956,7 +562,7 @@ void ffn_fat_q3_kernel(FfnArgs a) {
                 }
             }
 #pragma unroll
-            for (int c = 0; c < 2; ++c) rw.sc[c] = ds_read4(rb + Q3_RAW + (uint32_t)brow[c] * 4u);
+            for (int c = 0; c < 2; ++c) rw.sc[c] = ds_read4(rb + FatStage<1>::RAW + (uint32_t)brow[c] * 4u);
         };
         auto rwait = [&](Q3Raw& rw) {
             asm volatile("s_waitcnt lgkmcnt(0)"
@@ -966,8 +572,9 @@ void ffn_fat_q3_kernel(FfnArgs a) {
                          :
                          : "memory");
         };
-        // decode piece P of stage kt: chunk C = P / 4 (step C / 2, column tile
-        // C % 2), weights 2 Q and 2 Q + 1 of its 8 (Q = P % 4)
+        // 3-bit decode piece P of stage kt: chunk C = P / 4 (step C / 2, column
+        // tile C % 2), weights 2 Q and 2 Q + 1 of its 8 (Q = P % 4); one
+        // bit-field extract, one conversion and one fma per weight
         auto piece = [&](auto p_c, int kt, const Q3Raw& rw, uint32_t (&bits)[4], float (&sf)[2], float (&m4)[2],
                          u32x4 (&bo)[2][2]) {
             constexpr int P = decltype(p_c)::value, C = P / 4, Q = P % 4, S = C / 2, CJ = C % 2;
@@ -983,7 +590,6 @@ void ffn_fat_q3_kernel(FfnArgs a) {
                 const int sh = 3 * ((32 * (kt & 3) + 16 * S + 8 * g) % 10);
                 bits[C] = ((rw.lo[S][CJ] & 0x3FFFFFFFu) >> sh) | (rw.hi[S][CJ] << (30 - sh));
             }
-            // one bit-field extract, one conversion and one fma per weight
             const float v0 = fmaf((float)field3<6 * Q>(bits[C]), sf[CJ], m4[CJ]);
             const float v1 = fmaf((float)field3<6 * Q + 3>(bits[C]), sf[CJ], m4[CJ]);
             if constexpr (PHASE == 2) {
@@ -995,13 +601,14 @@ void ffn_fat_q3_kernel(FfnArgs a) {
             }
         };
 
-        // prologue: the ring in flight; stages 0 and 1 landed; stage 0 decoded
+        // prologue: the whole ring in flight; stage 0 (and for 3-bit weights
+        // stage 1) landed; 3-bit: stage 0 decoded into B0
         const int pro = min(NS, KT);
         for (int s = 0; s < pro; ++s) issue(s, s);
-        vm_wait_stages<Q3_LOADS>(pro - 2);
+        vm_wait_stages<Stage::LOADS>(pro - Stage::AHEAD);
         __builtin_amdgcn_s_barrier();
         u32x4 B0[2][2], B1[2][2];
-        {
+        if constexpr (WFMT == 1) {
             Q3Raw rw;
             uint32_t bits[4];
             float sf[2], m4[2];
@@ -1013,67 +620,106 @@ void ffn_fat_q3_kernel(FfnArgs a) {
         auto kloop = [&](auto rt_c) {
             constexpr int RT = decltype(rt_c)::value, S = 2 * RT;
             constexpr int BAR = S / 4;                               // step-1 slot of the stage barrier
-            constexpr int DW = S >= 8 ? 3 : (S >= 4 ? 1 : 0);        // step-0 slot of the words' wait
-            constexpr int AV0 = S > DW + 1 ? S - DW - 1 : 0;         // decode slots in step 0
-            constexpr int AV = AV0 + BAR;                            // ... and in step 1
-            u32x4 x0[8], x1[8];
-            areads(rt_c, 0, 0, x0);
+            u32x4 x0[8], x1[8], y0[2], y1[2];
+            reads(rt_c, 0, 0, x0, y0);
             int slot = 0;
-            // stage kt computes with bc and decodes stage kt+1 into bn
-            auto stage = [&](int kt, auto more_c, u32x4 (&bc)[2][2], u32x4 (&bn)[2][2]) {
-                constexpr bool more = decltype(more_c)::value;
-                const int nslot = slot + 1 == NS ? 0 : slot + 1;
-                Q3Raw rw;
-                uint32_t bits[4];
-                float sf[2], m4[2];
-                auto pieces_at = [&](auto step_c, auto slot_c) {
-                    constexpr int STEP = decltype(step_c)::value, I = decltype(slot_c)::value;
-                    static_for<16>([&](auto p_c) {
-                        constexpr int P = decltype(p_c)::value;
-                        constexpr int G = AV > 0 ? P * AV / 16 : 0;
-                        constexpr int ST = (AV == 0 || G < AV0) ? 0 : 1;
-                        constexpr int SL = AV == 0 ? DW + 1 : (G < AV0 ? DW + 1 + G : G - AV0);
-                        if constexpr (more && ST == STEP && SL == I) piece(p_c, kt + 1, rw, bits, sf, m4, bn);
+            if constexpr (WFMT == 0) {
+                // per stage: step 0 issues step 1's fragment reads; step 1 waits
+                // for the next stage, passes the barrier (every wave is done with
+                // this stage), refills this stage's slot and reads the next
+                // stage's first step
+                auto stage = [&](int kt, auto more_c) {
+                    constexpr bool more = decltype(more_c)::value;
+                    const int nslot = slot + 1 == NS ? 0 : slot + 1;
+                    lds_wait_frag<0>(x0, y0);
+                    __builtin_amdgcn_sched_barrier(0);
+                    step_slots<PHASE, RT>(acc, x0, y0, [&](auto i) {
+                        constexpr int I = decltype(i)::value;
+                        if constexpr (PHASE == 2 && I < 2) y0[I] = bf16x8_to_f16x8(y0[I]);
+                        if constexpr (I == 0) reads(rt_c, slot, 1, x1, y1);
                     });
+                    lds_wait_frag<0>(x1, y1);
+                    __builtin_amdgcn_sched_barrier(0);
+                    step_slots<PHASE, RT>(acc, x1, y1, [&](auto i) {
+                        constexpr int I = decltype(i)::value;
+                        if constexpr (PHASE == 2 && I < 2) y1[I] = bf16x8_to_f16x8(y1[I]);
+                        if constexpr (I == BAR && more) {
+                            vm_wait_stages<Stage::LOADS>(min(NS - 2, KT - 2 - kt));   // stage kt+1 landed here
+                            __builtin_amdgcn_s_barrier();                              // ... and in every lane
+                        }
+                        if constexpr (I == BAR + 1) {
+                            if (kt + NS < KT) issue(kt + NS, slot);                     // refill this stage's slot
+                        }
+                        if constexpr (I == BAR + 2 && more) reads(rt_c, nslot, 0, x0, y0);
+                    });
+                    slot = nslot;
                 };
-                using St0 = std::integral_constant<int, 0>;
-                using St1 = std::integral_constant<int, 1>;
-                lds_wait_tied<0>(x0);
-                __builtin_amdgcn_sched_barrier(0);
-                step_slots_1x4<PHASE, RT>(acc, x0, bc[0], [&](auto i) {
-                    constexpr int I = decltype(i)::value;
-                    if constexpr (I == 0) {
-                        areads(rt_c, slot, 1, x1);
-                        if constexpr (more) rreads(nslot, kt + 1, rw);
-                    }
-                    if constexpr (I == DW && more) rwait(rw);
-                    pieces_at(St0{}, i);
-                });
-                lds_wait_tied<0>(x1);
-                __builtin_amdgcn_sched_barrier(0);
-                step_slots_1x4<PHASE, RT>(acc, x1, bc[1], [&](auto i) {
-                    constexpr int I = decltype(i)::value;
-                    pieces_at(St1{}, i);
-                    if constexpr (I == BAR && more) {
-                        // the stage after next must have landed: it is decoded during the next stage
-                        vm_wait_stages<Q3_LOADS>(max(0, min(NS - 3, KT - 3 - kt)));
-                        __builtin_amdgcn_s_barrier();
-                    }
-                    if constexpr (I == BAR + 1) {
-                        if (kt + NS < KT) issue(kt + NS, slot);
-                    }
-                    if constexpr (I == BAR + 2 && more) areads(rt_c, nslot, 0, x0);
-                });
-                slot = nslot;
-            };
-            for (int kt = 0; kt + 2 < KT; kt += 2) {
-                stage(kt, std::true_type{}, B0, B1);
-                stage(kt + 1, std::true_type{}, B1, B0);
+                for (int kt = 0; kt + 1 < KT; ++kt) stage(kt, std::true_type{});
+                stage(KT - 1, std::false_type{});
+            } else {
+                // per stage: step 0 issues step 1's activation reads and the next
+                // stage's packed words; the next stage's weights are decoded in 16
+                // pieces over the MFMA slots of step 0 and of step 1 up to the
+                // barrier; at the barrier this stage's slot is free and the stage
+                // after next has landed
+                constexpr int DW = S >= 8 ? 3 : (S >= 4 ? 1 : 0);    // step-0 slot of the words' wait
+                constexpr int AV0 = S > DW + 1 ? S - DW - 1 : 0;     // decode slots in step 0
+                constexpr int AV = AV0 + BAR;                        // ... and in step 1
+                // stage kt computes with bc and decodes stage kt+1 into bn
+                auto stage = [&](int kt, auto more_c, u32x4 (&bc)[2][2], u32x4 (&bn)[2][2]) {
+                    constexpr bool more = decltype(more_c)::value;
+                    const int nslot = slot + 1 == NS ? 0 : slot + 1;
+                    Q3Raw rw;
+                    uint32_t bits[4];
+                    float sf[2], m4[2];
+                    auto pieces_at = [&](auto step_c, auto slot_c) {
+                        constexpr int STEP = decltype(step_c)::value, I = decltype(slot_c)::value;
+                        static_for<16>([&](auto p_c) {
+                            constexpr int P = decltype(p_c)::value;
+                            constexpr int G = AV > 0 ? P * AV / 16 : 0;
+                            constexpr int ST = (AV == 0 || G < AV0) ? 0 : 1;
+                            constexpr int SL = AV == 0 ? DW + 1 : (G < AV0 ? DW + 1 + G : G - AV0);
+                            if constexpr (more && ST == STEP && SL == I) piece(p_c, kt + 1, rw, bits, sf, m4, bn);
+                        });
+                    };
+                    using St0 = std::integral_constant<int, 0>;
+                    using St1 = std::integral_constant<int, 1>;
+                    lds_wait_frag<0>(x0, y0);
+                    __builtin_amdgcn_sched_barrier(0);
+                    step_slots<PHASE, RT>(acc, x0, bc[0], [&](auto i) {
+                        constexpr int I = decltype(i)::value;
+                        if constexpr (I == 0) {
+                            reads(rt_c, slot, 1, x1, y1);
+                            if constexpr (more) rreads(nslot, kt + 1, rw);
+                        }
+                        if constexpr (I == DW && more) rwait(rw);
+                        pieces_at(St0{}, i);
+                    });
+                    lds_wait_frag<0>(x1, y1);
+                    __builtin_amdgcn_sched_barrier(0);
+                    step_slots<PHASE, RT>(acc, x1, bc[1], [&](auto i) {
+                        constexpr int I = decltype(i)::value;
+                        pieces_at(St1{}, i);
+                        if constexpr (I == BAR && more) {
+                            vm_wait_stages<Stage::LOADS>(max(0, min(NS - 3, KT - 3 - kt)));
+                            __builtin_amdgcn_s_barrier();
+                        }
+                        if constexpr (I == BAR + 1) {
+                            if (kt + NS < KT) issue(kt + NS, slot);
+                        }
+                        if constexpr (I == BAR + 2 && more) reads(rt_c, nslot, 0, x0, y0);
+                    });
+                    slot = nslot;
+                };
+                for (int kt = 0; kt + 2 < KT; kt += 2) {
+                    stage(kt, std::true_type{}, B0, B1);
+                    stage(kt + 1, std::true_type{}, B1, B0);
+                }
+                stage(KT - 2, std::true_type{}, B0, B1);
+                stage(KT - 1, std::false_type{}, B1, B0);
             }
-            stage(KT - 2, std::true_type{}, B0, B1);
-            stage(KT - 1, std::false_type{}, B1, B0);
             __syncthreads();
-            fat_epilogue_1x4<PHASE, RT>(a, acc, t, nt, smem);
+            fat_epilogue<PHASE, RT>(a, acc, t, nt, smem);
         };
         switch (rt) {
             case 8: kloop(std::integral_constant<int, 8>{}); break;
@@ -1198,8 +844,8 @@ FfnLayout ffn_layout(int T, int E, int k, int H, int I) {
 
 struct DevInfo {
     int cus = 0;
-    int ring = 4;                               // LDS stages of the bf16 fat kernels (4 or 5)
-    int q3ring = 5;                             // LDS stages of the 3-bit fat kernels (5 or 6)
+    int ring = 4;                               // LDS ring stages of the bf16 fat kernels (4 or 5)
+    int q3ring = 5;                             // ... of the 3-bit fat kernels (5 or 6)
     int thin_blocks[2][2][2] = {};              // [wfmt][phase-1][chunk width 2 / 4]
 };
 
@@ -1226,25 +872,25 @@ hipError_t dev_info(DevInfo& out) {
         int cus = 0;
         err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
         if (err != hipSuccess) return err;
-        // the fat kernels use 128 KB or more of dynamic LDS (above the default
-        // cap); the bf16 ones take a fifth 32 KB stage where a block may hold
-        // 160 KB
+        // the fat kernels use up to 160 KB of dynamic LDS (above the default
+        // cap): a fifth 32 KB bf16 stage and a sixth 21 KB 3-bit stage where a
+        // block may hold that much
         int lds_max = 0;
         err = hipDeviceGetAttribute(&lds_max, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
         if (err != hipSuccess) return err;
         const struct {
             const void* f;
             size_t bytes;
-        } fats[8] = {{(const void*)ffn_fat_dma_kernel<1, 4>, dma_lds_bytes<4>()},
-                     {(const void*)ffn_fat_dma_kernel<2, 4>, dma_lds_bytes<4>()},
-                     {(const void*)ffn_fat_dma_kernel<1, 5>, dma_lds_bytes<5>()},
-                     {(const void*)ffn_fat_dma_kernel<2, 5>, dma_lds_bytes<5>()},
-                     {(const void*)ffn_fat_q3_kernel<1, 5>, q3_lds_bytes<5>()},
-                     {(const void*)ffn_fat_q3_kernel<2, 5>, q3_lds_bytes<5>()},
-                     {(const void*)ffn_fat_q3_kernel<1, 6>, q3_lds_bytes<6>()},
-                     {(const void*)ffn_fat_q3_kernel<2, 6>, q3_lds_bytes<6>()}};
-        d.ring = (size_t)lds_max >= dma_lds_bytes<5>() ? 5 : 4;
-        d.q3ring = (size_t)lds_max >= q3_lds_bytes<6>() ? 6 : 5;
+        } fats[8] = {{(const void*)ffn_fat_kernel<1, 0, 4>, fat_lds_bytes<0, 4>()},
+                     {(const void*)ffn_fat_kernel<2, 0, 4>, fat_lds_bytes<0, 4>()},
+                     {(const void*)ffn_fat_kernel<1, 0, 5>, fat_lds_bytes<0, 5>()},
+                     {(const void*)ffn_fat_kernel<2, 0, 5>, fat_lds_bytes<0, 5>()},
+                     {(const void*)ffn_fat_kernel<1, 1, 5>, fat_lds_bytes<1, 5>()},
+                     {(const void*)ffn_fat_kernel<2, 1, 5>, fat_lds_bytes<1, 5>()},
+                     {(const void*)ffn_fat_kernel<1, 1, 6>, fat_lds_bytes<1, 6>()},
+                     {(const void*)ffn_fat_kernel<2, 1, 6>, fat_lds_bytes<1, 6>()}};
+        d.ring = (size_t)lds_max >= fat_lds_bytes<0, 5>() ? 5 : 4;
+        d.q3ring = (size_t)lds_max >= fat_lds_bytes<1, 6>() ? 6 : 5;
         for (const auto& f : fats) {
             if (f.bytes > (size_t)lds_max) continue;
             err = hipFuncSetAttribute(f.f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)f.bytes);
@@ -1289,13 +935,14 @@ void launch_phase_t(const FfnArgs& fa, const DevInfo& d, bool fat_possible, hipS
     if (fat_possible) {
         if constexpr (WFMT != 0) {
             if (d.q3ring == 6)
-                ffn_fat_q3_kernel<PHASE, 6><<<d.cus, FAT_THREADS, q3_lds_bytes<6>(), s>>>(fa);
+                ffn_fat_kernel<PHASE, 1, 6><<<d.cus, FAT_THREADS, fat_lds_bytes<1, 6>(), s>>>(fa);
             else
-                ffn_fat_q3_kernel<PHASE, 5><<<d.cus, FAT_THREADS, q3_lds_bytes<5>(), s>>>(fa);
-        } else if (d.ring == 5)
-            ffn_fat_dma_kernel<PHASE, 5><<<d.cus, FAT_THREADS, dma_lds_bytes<5>(), s>>>(fa);
-        else
-            ffn_fat_dma_kernel<PHASE, 4><<<d.cus, FAT_THREADS, dma_lds_bytes<4>(), s>>>(fa);
+                ffn_fat_kernel<PHASE, 1, 5><<<d.cus, FAT_THREADS, fat_lds_bytes<1, 5>(), s>>>(fa);
+        } else if (d.ring == 5) {
+            ffn_fat_kernel<PHASE, 0, 5><<<d.cus, FAT_THREADS, fat_lds_bytes<0, 5>(), s>>>(fa);
+        } else {
+            ffn_fat_kernel<PHASE, 0, 4><<<d.cus, FAT_THREADS, fat_lds_bytes<0, 4>(), s>>>(fa);
+        }
     }
     // whole 128-byte lines per row when each wave's quarter of K is a multiple of 64
     const int K = PHASE == 1 ? fa.H : fa.I;
