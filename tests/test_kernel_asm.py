@@ -1,0 +1,134 @@
+"""Static checks of the gfx950 assembly of the FFN kernels (CPU only: hipcc
+cross-compiles, nothing runs on a GPU).
+
+1. No instruction reads, copies, spills or overwrites the destination
+   registers of an LDS read before an ``s_waitcnt`` has retired it (the fat
+   kernels' operand reads are inline assembly, which the compiler takes as
+   complete at once; a register copy placed before the wait would hold stale
+   data and give wrong results only on some paths).
+2. The fat kernels' K-loops (the innermost loops) spill nothing to scratch.
+
+The checker itself is pinned on hand-written snippets with and without such
+a hazard.
+"""
+import hashlib
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+from tests.asm_check import kernel_bodies, stale_lds_uses
+from routed_expert_ffn_03_amd.build import BUILD, CSRC, HIPCC_FLAGS
+
+SOURCES = ["ffn.hip", "common.h", "kernels.h"]
+
+
+def _hipcc():
+    return shutil.which("hipcc") or ("/opt/rocm/bin/hipcc" if os.path.exists("/opt/rocm/bin/hipcc") else None)
+
+
+@pytest.fixture(scope="module")
+def ffn_asm():
+    hipcc = _hipcc()
+    if hipcc is None:
+        pytest.skip("hipcc not available")
+    h = hashlib.sha256(" ".join(HIPCC_FLAGS).encode())
+    for s in SOURCES:
+        with open(os.path.join(CSRC, s), "rb") as f:
+            h.update(f.read())
+    out = os.path.join(BUILD, f"ffn_device_{h.hexdigest()[:12]}.s")
+    if not os.path.exists(out):
+        os.makedirs(BUILD, exist_ok=True)
+        cmd = [hipcc, *HIPCC_FLAGS, "--cuda-device-only", "-S", os.path.join(CSRC, "ffn.hip"), "-o", out + ".tmp"]
+        res = subprocess.run(cmd, capture_output=True, text=True, timeout=900)
+        assert res.returncode == 0, res.stderr[-2000:]
+        os.replace(out + ".tmp", out)
+    with open(out) as f:
+        return f.read()
+
+
+def test_checker_flags_a_copy_before_the_wait():
+    bad = """
+    ds_read_b128 v[4:7], v1 offset:64
+    v_mov_b64_e32 v[10:11], v[4:5]
+    s_waitcnt lgkmcnt(0)
+    v_mfma_f32_32x32x16_bf16 a[0:15], v[4:7], v[20:23], a[0:15]
+    """.split("\n")
+    r = stale_lds_uses(bad)
+    assert len(r) == 1 and "v_mov_b64" in r[0][1]
+
+
+def test_checker_follows_branches_and_partial_waits():
+    # the read is in flight on the path through .LBB0_1 only
+    lines = """
+    s_cbranch_scc1 .LBB0_2
+.LBB0_1:
+    ds_read_b128 v[4:7], v1
+    ds_read_b128 v[8:11], v1 offset:16
+    s_waitcnt lgkmcnt(1)
+    v_mov_b32_e32 v30, v4
+.LBB0_2:
+    scratch_store_dwordx4 off, v[8:11], off offset:16
+    s_waitcnt lgkmcnt(0)
+    v_mov_b32_e32 v31, v8
+    s_endpgm
+    """.split("\n")
+    r = stale_lds_uses(lines)
+    assert [x[1].split()[0] for x in r] == ["scratch_store_dwordx4"]
+
+
+def test_checker_accepts_clean_code():
+    lines = """
+    ds_read_b128 v[4:7], v1
+    s_waitcnt lgkmcnt(0)
+    v_mov_b64_e32 v[10:11], v[4:5]
+    s_load_dword s4, s[0:1], 0x0
+    ds_read_b128 v[8:11], v1
+    s_waitcnt lgkmcnt(0)
+    v_add_u32_e32 v12, v8, v9
+    s_endpgm
+    """.split("\n")
+    assert stale_lds_uses(lines) == []
+
+
+def test_no_lds_result_used_before_its_wait(ffn_asm):
+    kernels = {k: v for k, v in kernel_bodies(ffn_asm).items() if "ffn_" in k}
+    assert any("ffn_fat_kernel" in k for k in kernels)
+    bad = {}
+    for name, lines in kernels.items():
+        r = stale_lds_uses(lines)
+        if r:
+            bad[name] = r[:3]
+    assert not bad, bad
+
+
+def _loops(lines):
+    """(label, body lines) of every loop: from the first block of the loop to
+    the last branch back to its header."""
+    out = []
+    for i, l in enumerate(lines):
+        if "Inner Loop Header" in l and i > 0:
+            lab = lines[i - 1].split(":")[0].strip()
+            if not lab.startswith(".LBB"):
+                continue
+            tag = "Header=" + lab[2:] + " "
+            ends = [j for j, x in enumerate(lines) if re.search(r"s_c?branch\w*\s+" + re.escape(lab) + r"\s*$", x)]
+            starts = [j for j, x in enumerate(lines) if tag in x]
+            if ends:
+                out.append((lab, lines[min(starts + [i - 1]):max(ends) + 1]))
+    return out
+
+
+def test_fat_k_loops_do_not_spill(ffn_asm):
+    kernels = {k: v for k, v in kernel_bodies(ffn_asm).items() if "ffn_fat_kernel" in k}
+    checked = 0
+    for name, lines in kernels.items():
+        for lab, body in _loops(lines):
+            if sum("v_mfma" in x for x in body) < 8:
+                continue
+            checked += 1
+            spills = [x.strip() for x in body if "scratch_" in x]
+            assert not spills, (name, lab, spills[:3])
+    assert checked > 0
