@@ -153,7 +153,8 @@ class Runner:
             per = f"{2 * s.I * s.H * 2} gate+up weight bytes per touched expert x {touched} experts"
         r["frac"] = r["achieved"] / r["peak"]
         r["traffic"] = measured_traffic(s.name)
-        fat_name = "ffn_fat_dma_kernel<1, ring>" if s.wfmt == "bf16" else "ffn_fat_q3_kernel<1, ring>"
+        # fat kernel template arguments: <phase, weight format, LDS ring stages>
+        fat_name = "ffn_fat_kernel<1, 0, 5>" if s.wfmt == "bf16" else "ffn_fat_kernel<1, 1, 6>"
         r["kernel"] = f"gate/up phase ({fat_name} + ffn_thin_kernel<1, {0 if s.wfmt == 'bf16' else 1}, w>)"
         r["kernel_ms"] = gate_up_ms
         r["algorithmic"] = per
