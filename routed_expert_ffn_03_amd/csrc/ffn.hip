@@ -510,32 +510,27 @@ void ffn_fat_kernel(FfnArgs a) {
 #pragma unroll
             for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
 
-        // bf16: load instruction q of stage kt into ring slot `slot` (q < 4:
-        // activation rows, else weight rows)
+        // load instruction q of stage kt into ring slot `slot`: q < 4 the
+        // activation rows; then bf16: the weight rows (q = 4..7); 3-bit: the
+        // packed words (q = 4) and the scale dwords (q = 5)
         auto issue_one = [&](int kt, int slot, int q) {
             char* st = reinterpret_cast<char*>(smem) + slot * Stage::BYTES;
             if (q < 4)
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(asrc, (lds_ptr_t)(st + (4 * wave + q) * 1024), 16, aoff[q],
                                                          kt * DMA_ROW, 0, 0);
-            else
+            else if constexpr (WFMT == 0)
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(wsrc, (lds_ptr_t)(st + DMA_OPER + (4 * wave + q - 4) * 1024),
                                                          16, boff[q - 4], kt * DMA_ROW, 0, 0);
-        };
-        auto issue = [&](int kt, int slot) {
-            if constexpr (WFMT == 0) {
-#pragma unroll
-                for (int q = 0; q < 8; ++q) issue_one(kt, slot, q);
-            } else {
-                char* st = reinterpret_cast<char*>(smem) + slot * Stage::BYTES;
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    __builtin_amdgcn_raw_ptr_buffer_load_lds(asrc, (lds_ptr_t)(st + (4 * wave + q) * 1024), 16, aoff[q],
-                                                             kt * DMA_ROW, 0, 0);
+            else if (q == 4)
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(wsrc, (lds_ptr_t)(st + DMA_OPER + wave * 1024), 16, roff,
                                                          (kt >> 2) * (Q3_WORDS * 4) + (kt & 3) * 12, 0, 0);
+            else
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(ssrc, (lds_ptr_t)(st + DMA_OPER + Stage::RAW + wave * 256), 4,
                                                          ((sidx + (uint32_t)(kt >> 2)) >> 1) * 4u, 0, 0, 0);
-            }
+        };
+        auto issue = [&](int kt, int slot) {
+#pragma unroll
+            for (int q = 0; q < Stage::LOADS; ++q) issue_one(kt, slot, q);
         };
         // activation fragments of 16-k step s (row tiles 0..RT-1) and, for
         // bf16 weights, the two weight fragments
@@ -629,7 +624,7 @@ void ffn_fat_kernel(FfnArgs a) {
         auto kloop = [&](auto rt_c) {
             constexpr int RT = decltype(rt_c)::value, S = 2 * RT;
             constexpr int BAR = S / 4;                               // step-1 slot of the stage barrier
-            static_assert(WFMT != 0 || BAR + 8 < 16, "the eight refill loads follow the barrier inside step 1");
+            static_assert(BAR + Stage::LOADS < 16, "the refill loads follow the barrier inside step 1");
             u32x4 x0[8], x1[8], y0[2], y1[2];
             reads(rt_c, 0, 0, x0, y0);
             int slot = 0;
@@ -659,7 +654,7 @@ void ffn_fat_kernel(FfnArgs a) {
                             vm_wait_stages<Stage::LOADS>(min(NS - 2, KT - 2 - kt));   // stage kt+1 landed here
                             __builtin_amdgcn_s_barrier();                              // ... and in every lane
                         }
-                        if constexpr (I > BAR && I <= BAR + 8) {
+                        if constexpr (I > BAR && I <= BAR + Stage::LOADS) {
                             if (kt + NS < KT) issue_one(kt + NS, slot, I - BAR - 1);    // refill this stage's slot
                         }
                         if constexpr (I == BAR + 2 && more) reads(rt_c, nslot, 0, x0, y0);
@@ -716,8 +711,8 @@ void ffn_fat_kernel(FfnArgs a) {
                             vm_wait_stages<Stage::LOADS>(max(0, min(NS - 3, KT - 3 - kt)));
                             __builtin_amdgcn_s_barrier();
                         }
-                        if constexpr (I == BAR + 1) {
-                            if (kt + NS < KT) issue(kt + NS, slot);
+                        if constexpr (I > BAR && I <= BAR + Stage::LOADS) {
+                            if (kt + NS < KT) issue_one(kt + NS, slot, I - BAR - 1);   // one load per MFMA slot
                         }
                         if constexpr (I == BAR + 2 && more) reads(rt_c, nslot, 0, x0, y0);
                     });
