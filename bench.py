@@ -5,7 +5,8 @@ One step = one full layer call (route -> permute -> plan -> gate/up -> down
 -> combine) over one batch of synthetic inputs already resident in HBM.
 The headline workload is the 16,384-token prefill chunk (bf16 experts,
 Zipf-skewed router); the 4-token decode step is measured in the same run on
-the same weights and reported under "decode".  The dominant kernel's time
+the same weights and reported under "decode" (with --workload prefill16k_q3:
+the decode step on the same 3-bit weights).  The dominant kernel's time
 (the gate/up phase) is taken live with HIP events on the library's stream.
 
 Prints ONE JSON line.  Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
@@ -61,7 +62,7 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", default="prefill16k",
-                   choices=["prefill16k", "decode", "prefill1k", "prefill16k_q3"])
+                   choices=["prefill16k", "decode", "prefill1k", "prefill16k_q3", "decode_q3"])
     p.add_argument("--decode-steps", type=int, default=200, help="steps of the secondary decode measurement")
     p.add_argument("--no-decode", action="store_true", help="skip the secondary decode measurement")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -135,22 +136,23 @@ class Runner:
         counts = self.b.expert_counts.cpu().numpy()
         touched = int((counts > 0).sum())
         P = s.T * s.k
-        if s.wfmt == "bf16":
-            wbytes_gate_up = touched * 2 * s.I * s.H * 2
-        else:
-            wbytes_gate_up = touched * 2 * s.I * (s.H // 128) * (13 * 4 + 2)
+        # gate+up weight bytes of one expert: bf16, or 13 words + one fp16 scale per 128 weights
+        per_expert = 2 * s.I * s.H * 2 if s.wfmt == "bf16" else 2 * s.I * (s.H // 128) * (13 * 4 + 2)
+        wbytes_gate_up = touched * per_expert
         flops_gate_up = 4.0 * s.H * s.I * P
         t = gate_up_ms * 1e-3
         fat = int((counts >= self.thr).sum())
-        # MFMA-bound when most pairs sit in experts past the ridge (~313 rows at
-        # 2.5 PFLOP/s vs 8 TB/s for bf16 experts)
-        if P / max(touched, 1) >= 313 or s.wfmt != "bf16":
+        # MFMA-bound when the pairs per touched expert pass the ridge: flops per
+        # pair / MFMA peak = expert bytes / HBM peak (about 313 rows for bf16
+        # experts, 66 for 3-bit ones)
+        ridge = (per_expert / (PEAK_HBM_GBS * 1e9)) / (4.0 * s.H * s.I / (PEAK_MFMA_TFLOPS["bf16"] * 1e12))
+        if P / max(touched, 1) >= ridge:
             r = {"bound": "mfma", "achieved": flops_gate_up / t / 1e12, "peak": PEAK_MFMA_TFLOPS["bf16"],
                  "unit": "TFLOP/s"}
             per = f"{4 * s.H * s.I} flop per (token, expert) pair x {P} pairs"
         else:
             r = {"bound": "hbm", "achieved": wbytes_gate_up / t / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s"}
-            per = f"{2 * s.I * s.H * 2} gate+up weight bytes per touched expert x {touched} experts"
+            per = f"{per_expert} gate+up weight bytes per touched expert x {touched} experts"
         r["frac"] = r["achieved"] / r["peak"]
         r["traffic"] = measured_traffic(s.name)
         # fat kernel template arguments: <phase, weight format, LDS ring stages>
@@ -236,8 +238,9 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": shape.wfmt, "data": "synthetic",
         "config": workload_desc(shape, args.fat_threshold), "roofline": roof,
     }
-    if not args.no_decode and args.workload != "decode" and shape.wfmt == "bf16":
-        dshape = SHAPES["decode"]
+    if not args.no_decode and not args.workload.startswith("decode"):
+        # the 4-token decode step on the same weights (same format, same layer)
+        dshape = SHAPES["decode" if shape.wfmt == "bf16" else "decode_q3"]
         drun = Runner(dshape, args.seed, dev_w, args.fat_threshold)
         dms, dgu = drun.measure(args.decode_steps, 20)
         droof = drun.roofline(dgu)

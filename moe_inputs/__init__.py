@@ -75,15 +75,17 @@ class LayerShape:
         return LayerShape(self.name, T, self.H, self.I, self.E, self.k, self.router, self.wfmt)
 
 
-# The five workloads: a tiny layer for exhaustive parity, a 4-token decode
-# step, 1k and 16k prefill chunks (Zipf-skewed router), and the 16k chunk with
-# 3-bit grouped weights under an unskewed router.
+# The workloads: a tiny layer for exhaustive parity, a 4-token decode step,
+# 1k and 16k prefill chunks (Zipf-skewed router), the 16k chunk with 3-bit
+# grouped weights under an unskewed router, and the 4-token decode step on the
+# same 3-bit weights (Zipf router as the bf16 decode step).
 SHAPES = {
     "tiny": LayerShape("tiny", 64, 256, 128, 16, 2, "normal", "bf16"),
     "decode": LayerShape("decode", 4, 4096, 2048, 384, 8, "zipf", "bf16"),
     "prefill1k": LayerShape("prefill1k", 1024, 4096, 2048, 384, 8, "zipf", "bf16"),
     "prefill16k": LayerShape("prefill16k", 16384, 4096, 2048, 384, 8, "zipf", "bf16"),
     "prefill16k_q3": LayerShape("prefill16k_q3", 16384, 4096, 2048, 384, 8, "normal", "q3"),
+    "decode_q3": LayerShape("decode_q3", 4, 4096, 2048, 384, 8, "zipf", "q3"),
 }
 
 

@@ -119,83 +119,6 @@ void build_tiles_kernel(const int32_t* __restrict__ offsets, int E, int thr, Ffn
     }
 }
 
-// ------------------------------------------------------------ weight loaders
-
-// 3-bit group decode: the 8 weights k..k+7 (k % 8 == 0) of one output row.
-// A group of 128 weights is 13 words; field f sits in word f/10 at bits
-// 3*(f%10).  Eight consecutive fields span at most two words; they are
-// gathered into one 24-bit run first.  weight = scale * (field - 4), computed
-// exactly in fp32 as fma(field, s, -4s) and rounded once to the MFMA type.
-// 8 consecutive 3-bit fields (bits 3q..3q+2 of `bits`, q = 0..7) to MFMA
-// operand values scale * (field - 4): exact in fp32 as fma(field, s, -4s),
-// rounded once to fp16 (TO_F16) or bf16 (nearest even).
-template <bool TO_F16>
-__device__ __forceinline__ u32x4 q3_decode8(uint32_t bits, uint32_t scale_bits) {
-    const float s = (float)__builtin_bit_cast(_Float16, (uint16_t)scale_bits);
-    const float m4 = -4.0f * s;
-    u32x4 r;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const float v0 = fmaf((float)((bits >> (6 * i)) & 7u), s, m4);
-        const float v1 = fmaf((float)((bits >> (6 * i + 3)) & 7u), s, m4);
-        if (TO_F16) {
-            const f16x2 h = {(_Float16)v0, (_Float16)v1};          // v_cvt_pk_f16_f32, nearest even
-            r[i] = __builtin_bit_cast(uint32_t, h);
-        } else {
-            const bf16x2 b = {(__bf16)v0, (__bf16)v1};             // v_cvt_pk_bf16_f32, nearest even
-            r[i] = __builtin_bit_cast(uint32_t, b);
-        }
-    }
-    return r;
-}
-
-// 3-bit group decode: the 8 weights k..k+7 (k % 8 == 0) of one output row.
-// A group of 128 weights is 13 words; field f sits in word f/10 at bits
-// 3*(f%10).  Eight consecutive fields span at most two words; they are
-// gathered into one 24-bit run first.
-template <bool TO_F16>
-__device__ __forceinline__ u32x4 q3_chunk(const uint32_t* __restrict__ wrow, const uint16_t* __restrict__ srow,
-                                          int k) {
-    const int g = k >> 7, f0 = k & 127;
-    const uint32_t* gw = wrow + g * Q3_WORDS;
-    const int wlo = f0 / 10, n0 = f0 - wlo * 10;
-    uint32_t bits = (gw[wlo] & 0x3FFFFFFFu) >> (3 * n0);   // bits 30-31 are not fields
-    if (n0 > 2) bits |= gw[wlo + 1] << (30 - 3 * n0);
-    return q3_decode8<TO_F16>(bits, srow[g]);
-}
-
-// One weight row as seen by a loader: bf16 row pointer, or 3-bit words + scales.
-struct WRow {
-    const void* w;
-    const uint16_t* s;
-};
-
-template <int WFMT>
-__device__ __forceinline__ WRow weight_row(const void* base, const uint16_t* sbase, size_t row, int K) {
-    WRow r;
-    if (WFMT == 0) {
-        r.w = reinterpret_cast<const uint16_t*>(base) + row * (size_t)K;
-        r.s = nullptr;
-    } else {
-        const size_t groups = (size_t)(K >> 7);
-        r.w = reinterpret_cast<const uint32_t*>(base) + row * groups * Q3_WORDS;
-        r.s = sbase + row * groups;
-    }
-    return r;
-}
-
-// 8 weights k..k+7 of a row as an MFMA operand chunk: bf16 for phase 1, fp16
-// for phase 2.
-template <int WFMT, int PHASE>
-__device__ __forceinline__ u32x4 load_w8(const WRow& r, int k) {
-    if (WFMT == 0) {
-        u32x4 v = ldg16(reinterpret_cast<const uint16_t*>(r.w) + k);
-        return PHASE == 2 ? bf16x8_to_f16x8(v) : v;
-    } else {
-        return q3_chunk<PHASE == 2>(reinterpret_cast<const uint32_t*>(r.w), r.s, k);
-    }
-}
-
 template <int PHASE>
 __device__ __forceinline__ f32x16 mma(u32x4 a, u32x4 b, f32x16 c) {
     return PHASE == 1 ? mfma_bf16(a, b, c) : mfma_f16(a, b, c);
@@ -532,6 +455,17 @@ void ffn_fat_kernel(FfnArgs a) {
 #pragma unroll
             for (int q = 0; q < Stage::LOADS; ++q) issue_one(kt, slot, q);
         };
+        // bf16: fragment j of 16-k step s in ring slot `slot` (j < RT: activation
+        // row tile j; RT + c: weight column tile c; larger j: nothing)
+        auto read_one = [&](auto rt_c, auto j_c, int slot, int s, u32x4 (&af)[8], u32x4 (&bf)[2]) {
+            constexpr int RT = decltype(rt_c)::value, J = decltype(j_c)::value;
+            const uint32_t st = sbase + slot * Stage::BYTES;
+            if constexpr (J < RT)
+                af[J] = ds_read16<J * 32 * DMA_ROW>(st + aoffs[s]);
+            else if constexpr (J < RT + 2)
+                bf[J - RT] = ds_read16<0>(st + DMA_OPER + (uint32_t)brow[J - RT] * DMA_ROW +
+                                          (uint32_t)(((2 * s + g) ^ ((n >> 2) & 3)) * 16));
+        };
         // activation fragments of 16-k step s (row tiles 0..RT-1) and, for
         // bf16 weights, the two weight fragments
         auto reads = [&](auto rt_c, int slot, int s, u32x4 (&af)[8], u32x4 (&bf)[2]) {
@@ -625,25 +559,37 @@ void ffn_fat_kernel(FfnArgs a) {
             constexpr int RT = decltype(rt_c)::value, S = 2 * RT;
             constexpr int BAR = S / 4;                               // step-1 slot of the stage barrier
             static_assert(BAR + Stage::LOADS < 16, "the refill loads follow the barrier inside step 1");
+            static_assert(WFMT != 0 || (Stage::LOADS == 8 && 2 * (15 - BAR) >= RT + 2),
+                          "bf16: eight refill loads in the odd slots of step 0, next-step reads after the barrier");
             u32x4 x0[8], x1[8], y0[2], y1[2];
             reads(rt_c, 0, 0, x0, y0);
             int slot = 0;
             if constexpr (WFMT == 0) {
-                // per stage: step 0 issues step 1's fragment reads; step 1 waits
-                // for the next stage, passes the barrier (every wave is done with
-                // this stage), refills this stage's slot -- one load instruction
-                // per MFMA slot after the barrier, so that no burst of loads
-                // holds the wave while its MFMA pipe drains -- and reads the next
-                // stage's first step
+                // per stage kt: the even slots of step 0 read step 1's fragments
+                // (two per slot) and the odd slots refill the slot that stage kt-1
+                // used with stage kt-1+NS (one load per slot; every wave finished
+                // reading it before the previous barrier); step 1 waits for stage
+                // kt+1, passes the barrier and reads stage kt+1's first step, two
+                // fragments per slot.  No slot issues a burst of loads or reads
+                // that would hold the wave while its MFMA pipe drains (the four
+                // waves leave a barrier together and would queue all their
+                // loads at once).
                 auto stage = [&](int kt, auto more_c) {
                     constexpr bool more = decltype(more_c)::value;
                     const int nslot = slot + 1 == NS ? 0 : slot + 1;
+                    const int pslot = slot == 0 ? NS - 1 : slot - 1;
+                    const bool refill = kt >= 1 && kt - 1 + NS < KT;
                     lds_wait_frag<0>(x0, y0);
                     __builtin_amdgcn_sched_barrier(0);
                     step_slots<PHASE, RT>(acc, x0, y0, [&](auto i) {
                         constexpr int I = decltype(i)::value;
                         if constexpr (PHASE == 2 && I < 2) y0[I] = bf16x8_to_f16x8(y0[I]);
-                        if constexpr (I == 0) reads(rt_c, slot, 1, x1, y1);
+                        if constexpr (I % 2 == 0) {
+                            read_one(rt_c, std::integral_constant<int, I>{}, slot, 1, x1, y1);
+                            read_one(rt_c, std::integral_constant<int, I + 1>{}, slot, 1, x1, y1);
+                        } else {
+                            if (refill) issue_one(kt - 1 + NS, pslot, I / 2);
+                        }
                     });
                     lds_wait_frag<0>(x1, y1);
                     __builtin_amdgcn_sched_barrier(0);
@@ -654,10 +600,10 @@ void ffn_fat_kernel(FfnArgs a) {
                             vm_wait_stages<Stage::LOADS>(min(NS - 2, KT - 2 - kt));   // stage kt+1 landed here
                             __builtin_amdgcn_s_barrier();                              // ... and in every lane
                         }
-                        if constexpr (I > BAR && I <= BAR + Stage::LOADS) {
-                            if (kt + NS < KT) issue_one(kt + NS, slot, I - BAR - 1);    // refill this stage's slot
+                        if constexpr (I > BAR && more) {
+                            read_one(rt_c, std::integral_constant<int, 2 * (I - BAR - 1)>{}, nslot, 0, x0, y0);
+                            read_one(rt_c, std::integral_constant<int, 2 * (I - BAR - 1) + 1>{}, nslot, 0, x0, y0);
                         }
-                        if constexpr (I == BAR + 2 && more) reads(rt_c, nslot, 0, x0, y0);
                     });
                     slot = nslot;
                 };
@@ -741,12 +687,39 @@ void ffn_fat_kernel(FfnArgs a) {
     }
 }
 
-// ------------------------------------------------------------ thin kernel
+// ------------------------------------------------------------ thin kernels
+
+// The four waves' partial 32 x 32 tiles of one thin item are summed through
+// LDS; wave 0 stores the result: phase 1 silu(gate) * up for the 16 gate
+// columns (the up partner sits 16 lanes over), phase 2 the 32 y columns.
+template <int PHASE>
+__device__ __forceinline__ void thin_reduce_store(const FfnArgs& a, const f32x16& acc, const MTile& t, int nt,
+                                                  float (&red)[4][16][64], int wave, int lane) {
+    const int m = lane & 31, g = lane >> 5;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) red[wave][r][lane] = acc[r];
+    __syncthreads();
+    if (wave == 0) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const float v = red[0][r][lane] + red[1][r][lane] + red[2][r][lane] + red[3][r][lane];
+            const int row = 8 * (r >> 2) + 4 * g + (r & 3);
+            if (PHASE == 1) {
+                const float u = __shfl(v, (lane + 16) & 63, 64);
+                if (m < 16 && row < t.rows)
+                    a.act[(size_t)(t.row0 + row) * a.I + nt * 16 + m] = f32_to_f16_bits(silu_mul(v, u));
+            } else {
+                if (row < t.rows) a.y[(size_t)(t.row0 + row) * a.H + nt * 32 + m] = f32_to_f16_bits(v);
+            }
+        }
+    }
+    __syncthreads();
+}
 
 // CW: 16-byte pieces per lane and row per chunk; lane half g covers 8*CW
 // consecutive k of a 16*CW-wide chunk, so with CW = 4 every row is read in
 // whole 128-byte lines.  D: chunks in the register ring (D - 1 in flight).
-template <int PHASE, int WFMT, int CW>
+template <int PHASE, int CW>
 __global__ __launch_bounds__(THIN_THREADS)
 void ffn_thin_kernel(FfnArgs a) {
     constexpr int D = CW == 4 ? 3 : 4;
@@ -770,12 +743,14 @@ void ffn_thin_kernel(FfnArgs a) {
             if (PHASE == 1) arow = a.x + (size_t)(a.sorted_pair[t.row0 + m] / a.k) * a.H;
             else arow = a.act + (size_t)(t.row0 + m) * a.I;
         }
-        WRow brow;
+        // this lane's weight row (bf16): phase 1 gate rows nt*16.. (m < 16)
+        // and the matching up rows, phase 2 down rows nt*32 + m
+        const uint16_t* brow;
         if (PHASE == 1) {
             const size_t n = (size_t)t.e * a.I + nt * 16 + (m & 15);
-            brow = m < 16 ? weight_row<WFMT>(a.wg, a.sg, n, K) : weight_row<WFMT>(a.wu, a.su, n, K);
+            brow = reinterpret_cast<const uint16_t*>(m < 16 ? a.wg : a.wu) + n * (size_t)K;
         } else {
-            brow = weight_row<WFMT>(a.wd, a.sd, (size_t)t.e * a.H + nt * 32 + m, K);
+            brow = reinterpret_cast<const uint16_t*>(a.wd) + ((size_t)t.e * a.H + nt * 32 + m) * (size_t)K;
         }
 
         u32x4 ra[D][CW], rw[D][CW];
@@ -787,7 +762,10 @@ void ffn_thin_kernel(FfnArgs a) {
                 if (arow) xa[c] = ldg16(arow + k0 + 8 * c);
             }
 #pragma unroll
-            for (int c = 0; c < CW; ++c) xw[c] = load_w8<WFMT, PHASE>(brow, k0 + 8 * c);
+            for (int c = 0; c < CW; ++c) {
+                const u32x4 v = ldg16(brow + k0 + 8 * c);
+                xw[c] = PHASE == 2 ? bf16x8_to_f16x8(v) : v;       // fp16 MFMA for the down projection
+            }
         };
         f32x16 acc = f32x16{};
 #pragma unroll
@@ -804,24 +782,91 @@ void ffn_thin_kernel(FfnArgs a) {
                 }
             }
         }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) red[wave][r][lane] = acc[r];
-        __syncthreads();
-        if (wave == 0) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float v = red[0][r][lane] + red[1][r][lane] + red[2][r][lane] + red[3][r][lane];
-                const int row = 8 * (r >> 2) + 4 * g + (r & 3);
-                if (PHASE == 1) {
-                    const float u = __shfl(v, (lane + 16) & 63, 64);
-                    if (m < 16 && row < t.rows)
-                        a.act[(size_t)(t.row0 + row) * a.I + nt * 16 + m] = f32_to_f16_bits(silu_mul(v, u));
-                } else {
-                    if (row < t.rows) a.y[(size_t)(t.row0 + row) * a.H + nt * 32 + m] = f32_to_f16_bits(v);
-                }
-            }
+        thin_reduce_store<PHASE>(a, acc, t, nt, red, wave, lane);
+    }
+}
+
+// 3-bit thin kernel: the same items, waves and reduction as the bf16 thin
+// kernel, with the reduction index walked a group pair at a time.  For MFMA
+// step j (0..15) of pair p, lane half g holds fields 8j..8j+7 of group 2p+g
+// of its weight row, and the activation lanes hold the matching 8 k of their
+// row (the MFMA sums over k in any order, so both operands only have to agree
+// on which k each lane holds).  Every field then sits at a compile-time word
+// and bit: one v_bfe_u32, one convert and one fma per weight, no index
+// arithmetic.  Each lane loads its group's 13 words with three 16-byte loads
+// and one 4-byte load (52-byte groups are 4-byte aligned; a buffer load needs
+// no more), instead of re-reading words per 8 fields.
+template <int PHASE>
+__global__ __launch_bounds__(THIN_THREADS)
+void ffn_thin_q3_kernel(FfnArgs a) {
+    __shared__ float red[4][16][64];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform (SGPR)
+    const int m = lane & 31, g = lane >> 5;
+    const int K = PHASE == 1 ? a.H : a.I;
+    const int N = PHASE == 1 ? a.I : a.H;            // rows of one expert matrix
+    const int NT = PHASE == 1 ? a.I / 16 : a.H / 32;
+    const int NG = K >> 7;                           // groups of 128 per row
+    const int NP = (NG + 1) >> 1;                    // group pairs
+    const int n_mt = a.hdr->n_thin;
+    const int n_items = n_mt * NT;
+    const size_t mat_words = (size_t)N * NG * Q3_WORDS;
+    const size_t mat_scales = (size_t)N * NG;
+
+    for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
+        const int nt = item / n_mt, mt = item % n_mt;
+        const MTile t = a.thin[mt];
+        const uint16_t* arow = nullptr;
+        if (m < t.rows) {
+            if (PHASE == 1) arow = a.x + (size_t)(a.sorted_pair[t.row0 + m] / a.k) * a.H;
+            else arow = a.act + (size_t)(t.row0 + m) * a.I;
         }
-        __syncthreads();
+        // this lane's weight row: phase 1 gate rows nt*16.. (m < 16) and the
+        // matching up rows (m >= 16); phase 2 down rows nt*32 + m
+        const void* wm = PHASE == 1 ? (m < 16 ? a.wg : a.wu) : a.wd;
+        const uint16_t* sm = PHASE == 1 ? (m < 16 ? a.sg : a.su) : a.sd;
+        const int row = PHASE == 1 ? nt * 16 + (m & 15) : nt * 32 + m;
+        const __amdgpu_buffer_rsrc_t wsrc =
+            make_rsrc(reinterpret_cast<const uint32_t*>(wm) + (size_t)t.e * mat_words, (uint32_t)(mat_words * 4));
+        const uint16_t* srow = sm + (size_t)t.e * mat_scales + (size_t)row * NG;
+
+        f32x16 acc = f32x16{};
+        for (int p = wave; p < NP; p += 4) {
+            const int G = 2 * p + g;
+            const bool valid = G < NG;                // an odd group count leaves the last half empty
+            const uint32_t off = (uint32_t)(row * NG + G) * (uint32_t)(Q3_WORDS * 4);
+            const u32x4 q0 = __builtin_amdgcn_raw_buffer_load_b128(wsrc, off, 0, 0);
+            const u32x4 q1 = __builtin_amdgcn_raw_buffer_load_b128(wsrc, off + 16, 0, 0);
+            const u32x4 q2 = __builtin_amdgcn_raw_buffer_load_b128(wsrc, off + 32, 0, 0);
+            const uint32_t q3w = __builtin_amdgcn_raw_buffer_load_b32(wsrc, off + 48, 0, 0);
+            const uint32_t W[Q3_WORDS] = {q0[0], q0[1], q0[2], q0[3], q1[0], q1[1], q1[2],
+                                          q1[3], q2[0], q2[1], q2[2], q2[3], q3w};
+            const uint16_t sbits = srow[valid ? G : 0];   // never past the row's scales
+            const float sc = valid ? (float)__builtin_bit_cast(_Float16, sbits) : 0.0f;
+            const float m4 = -4.0f * sc;
+            const uint16_t* ak = (arow && valid) ? arow + G * 128 : nullptr;
+            static_for<16>([&](auto j_c) {
+                constexpr int J = decltype(j_c)::value;
+                u32x4 av = u32x4{0, 0, 0, 0};
+                if (ak) av = ldg16(ak + 8 * J);
+                u32x4 bv;
+                static_for<4>([&](auto q_c) {
+                    constexpr int Q = decltype(q_c)::value;
+                    constexpr int F0 = 8 * J + 2 * Q, F1 = F0 + 1;
+                    const float v0 = fmaf((float)field3<3 * (F0 % 10)>(W[F0 / 10]), sc, m4);
+                    const float v1 = fmaf((float)field3<3 * (F1 % 10)>(W[F1 / 10]), sc, m4);
+                    if constexpr (PHASE == 2) {
+                        const f16x2 h = {(_Float16)v0, (_Float16)v1};
+                        bv[Q] = __builtin_bit_cast(uint32_t, h);
+                    } else {
+                        const bf16x2 h = {(__bf16)v0, (__bf16)v1};
+                        bv[Q] = __builtin_bit_cast(uint32_t, h);
+                    }
+                });
+                acc = mma<PHASE>(av, bv, acc);
+            });
+        }
+        thin_reduce_store<PHASE>(a, acc, t, nt, red, wave, lane);
     }
 }
 
@@ -859,12 +904,9 @@ struct DevInfo {
 std::mutex g_dev_mu;
 DevInfo g_dev[64];
 
-template <int PHASE, int WFMT, int CW>
-int thin_occupancy() {
+int occupancy_of(const void* f) {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, ffn_thin_kernel<PHASE, WFMT, CW>, THIN_THREADS, 0) !=
-        hipSuccess || n < 1)
-        n = 1;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, f, THIN_THREADS, 0) != hipSuccess || n < 1) n = 1;
     return n;
 }
 
@@ -903,14 +945,12 @@ hipError_t dev_info(DevInfo& out) {
             err = hipFuncSetAttribute(f.f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)f.bytes);
             if (err != hipSuccess) return err;
         }
-        d.thin_blocks[0][0][0] = thin_occupancy<1, 0, 2>();
-        d.thin_blocks[0][0][1] = thin_occupancy<1, 0, 4>();
-        d.thin_blocks[0][1][0] = thin_occupancy<2, 0, 2>();
-        d.thin_blocks[0][1][1] = thin_occupancy<2, 0, 4>();
-        d.thin_blocks[1][0][0] = thin_occupancy<1, 1, 2>();
-        d.thin_blocks[1][0][1] = thin_occupancy<1, 1, 4>();
-        d.thin_blocks[1][1][0] = thin_occupancy<2, 1, 2>();
-        d.thin_blocks[1][1][1] = thin_occupancy<2, 1, 4>();
+        d.thin_blocks[0][0][0] = occupancy_of((const void*)ffn_thin_kernel<1, 2>);
+        d.thin_blocks[0][0][1] = occupancy_of((const void*)ffn_thin_kernel<1, 4>);
+        d.thin_blocks[0][1][0] = occupancy_of((const void*)ffn_thin_kernel<2, 2>);
+        d.thin_blocks[0][1][1] = occupancy_of((const void*)ffn_thin_kernel<2, 4>);
+        d.thin_blocks[1][0][0] = d.thin_blocks[1][0][1] = occupancy_of((const void*)ffn_thin_q3_kernel<1>);
+        d.thin_blocks[1][1][0] = d.thin_blocks[1][1][1] = occupancy_of((const void*)ffn_thin_q3_kernel<2>);
         d.cus = cus;
     }
     out = d;
@@ -951,12 +991,16 @@ void launch_phase_t(const FfnArgs& fa, const DevInfo& d, bool fat_possible, hipS
             ffn_fat_kernel<PHASE, 0, 4><<<d.cus, FAT_THREADS, fat_lds_bytes<0, 4>(), s>>>(fa);
         }
     }
-    // whole 128-byte lines per row when each wave's quarter of K is a multiple of 64
-    const int K = PHASE == 1 ? fa.H : fa.I;
-    if ((K / 4) % 64 == 0)
-        ffn_thin_kernel<PHASE, WFMT, 4><<<d.cus * d.thin_blocks[WFMT][PHASE - 1][1], THIN_THREADS, 0, s>>>(fa);
-    else
-        ffn_thin_kernel<PHASE, WFMT, 2><<<d.cus * d.thin_blocks[WFMT][PHASE - 1][0], THIN_THREADS, 0, s>>>(fa);
+    if constexpr (WFMT != 0) {
+        ffn_thin_q3_kernel<PHASE><<<d.cus * d.thin_blocks[1][PHASE - 1][0], THIN_THREADS, 0, s>>>(fa);
+    } else {
+        // whole 128-byte lines per row when each wave's quarter of K is a multiple of 64
+        const int K = PHASE == 1 ? fa.H : fa.I;
+        if ((K / 4) % 64 == 0)
+            ffn_thin_kernel<PHASE, 4><<<d.cus * d.thin_blocks[0][PHASE - 1][1], THIN_THREADS, 0, s>>>(fa);
+        else
+            ffn_thin_kernel<PHASE, 2><<<d.cus * d.thin_blocks[0][PHASE - 1][0], THIN_THREADS, 0, s>>>(fa);
+    }
 }
 
 }  // namespace

@@ -94,7 +94,7 @@ def test_route_ties_and_shapes(T, E, k):
     np.testing.assert_allclose(w.cpu().numpy(), w_ref, rtol=0, atol=2e-6)
 
 
-@pytest.mark.parametrize("name", ["decode", "prefill1k", "prefill16k", "prefill16k_q3"])
+@pytest.mark.parametrize("name", ["decode", "prefill1k", "prefill16k", "prefill16k_q3", "decode_q3"])
 def test_route_and_permute_full_batch(name):
     shape = SHAPES[name]
     for seed in (0, 1, 2):
@@ -205,7 +205,7 @@ def full_layer_case(shape, seed, n_sample):
 
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("name,n_sample", [("decode", 4), ("prefill1k", 12), ("prefill16k", 10),
-                                           ("prefill16k_q3", 10)])
+                                           ("prefill16k_q3", 10), ("decode_q3", 4)])
 def test_layer_full_shape(name, n_sample):
     shape = SHAPES[name]
     say(f"[full layer] {name} T={shape.T} wfmt={shape.wfmt}")
