@@ -812,14 +812,21 @@ void ffn_thin_q3_kernel(FfnArgs a) {
     const int n_items = n_mt * NT;
     const size_t mat_words = (size_t)N * NG * Q3_WORDS;
     const size_t mat_scales = (size_t)N * NG;
+    // activation rows through a bounded buffer: a lane without a row (or past
+    // an odd group count) gets an offset beyond the buffer, which loads zeros
+    const __amdgpu_buffer_rsrc_t asrc = PHASE == 1
+        ? make_rsrc(a.x, (uint32_t)((size_t)a.T * a.H * 2))
+        : make_rsrc(a.act, (uint32_t)((size_t)a.T * a.k * a.I * 2));
+    constexpr uint32_t NOWHERE = 0xFFFFFF00u;
 
     for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
         const int nt = item / n_mt, mt = item % n_mt;
         const MTile t = a.thin[mt];
-        const uint16_t* arow = nullptr;
-        if (m < t.rows) {
-            if (PHASE == 1) arow = a.x + (size_t)(a.sorted_pair[t.row0 + m] / a.k) * a.H;
-            else arow = a.act + (size_t)(t.row0 + m) * a.I;
+        const bool has_row = m < t.rows;
+        uint32_t aoff = 0;
+        if (has_row) {
+            const uint32_t r = PHASE == 1 ? (uint32_t)(a.sorted_pair[t.row0 + m] / a.k) : (uint32_t)(t.row0 + m);
+            aoff = r * (uint32_t)K * 2u;
         }
         // this lane's weight row: phase 1 gate rows nt*16.. (m < 16) and the
         // matching up rows (m >= 16); phase 2 down rows nt*32 + m
@@ -830,31 +837,46 @@ void ffn_thin_q3_kernel(FfnArgs a) {
             make_rsrc(reinterpret_cast<const uint32_t*>(wm) + (size_t)t.e * mat_words, (uint32_t)(mat_words * 4));
         const uint16_t* srow = sm + (size_t)t.e * mat_scales + (size_t)row * NG;
 
-        f32x16 acc = f32x16{};
-        for (int p = wave; p < NP; p += 4) {
-            const int G = 2 * p + g;
-            const bool valid = G < NG;                // an odd group count leaves the last half empty
+        // the 13 words and the scale of group 2p+g of this lane's row
+        struct Group {
+            uint32_t w[Q3_WORDS];
+            uint16_t s;
+        };
+        auto load_group = [&](int p, Group& q) {
+            const int G = min(2 * p + g, NG - 1);     // past an odd count: a real group, scaled by 0 below
             const uint32_t off = (uint32_t)(row * NG + G) * (uint32_t)(Q3_WORDS * 4);
             const u32x4 q0 = __builtin_amdgcn_raw_buffer_load_b128(wsrc, off, 0, 0);
             const u32x4 q1 = __builtin_amdgcn_raw_buffer_load_b128(wsrc, off + 16, 0, 0);
             const u32x4 q2 = __builtin_amdgcn_raw_buffer_load_b128(wsrc, off + 32, 0, 0);
-            const uint32_t q3w = __builtin_amdgcn_raw_buffer_load_b32(wsrc, off + 48, 0, 0);
-            const uint32_t W[Q3_WORDS] = {q0[0], q0[1], q0[2], q0[3], q1[0], q1[1], q1[2],
-                                          q1[3], q2[0], q2[1], q2[2], q2[3], q3w};
-            const uint16_t sbits = srow[valid ? G : 0];   // never past the row's scales
-            const float sc = valid ? (float)__builtin_bit_cast(_Float16, sbits) : 0.0f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                q.w[i] = q0[i];
+                q.w[4 + i] = q1[i];
+                q.w[8 + i] = q2[i];
+            }
+            q.w[12] = __builtin_amdgcn_raw_buffer_load_b32(wsrc, off + 48, 0, 0);
+            q.s = srow[G];
+        };
+
+        f32x16 acc = f32x16{};
+        Group cur, nxt;
+        if (wave < NP) load_group(wave, cur);
+        for (int p = wave; p < NP; p += 4) {
+            if (p + 4 < NP) load_group(p + 4, nxt);  // next pair of this wave in flight during the decode
+            const int G = 2 * p + g;
+            const bool valid = G < NG;
+            const float sc = valid ? (float)__builtin_bit_cast(_Float16, cur.s) : 0.0f;
             const float m4 = -4.0f * sc;
-            const uint16_t* ak = (arow && valid) ? arow + G * 128 : nullptr;
+            const uint32_t ao = (has_row && valid) ? aoff + (uint32_t)G * 256u : NOWHERE;
             static_for<16>([&](auto j_c) {
                 constexpr int J = decltype(j_c)::value;
-                u32x4 av = u32x4{0, 0, 0, 0};
-                if (ak) av = ldg16(ak + 8 * J);
+                const u32x4 av = __builtin_amdgcn_raw_buffer_load_b128(asrc, ao, 16 * J, 0);
                 u32x4 bv;
                 static_for<4>([&](auto q_c) {
                     constexpr int Q = decltype(q_c)::value;
                     constexpr int F0 = 8 * J + 2 * Q, F1 = F0 + 1;
-                    const float v0 = fmaf((float)field3<3 * (F0 % 10)>(W[F0 / 10]), sc, m4);
-                    const float v1 = fmaf((float)field3<3 * (F1 % 10)>(W[F1 / 10]), sc, m4);
+                    const float v0 = fmaf((float)field3<3 * (F0 % 10)>(cur.w[F0 / 10]), sc, m4);
+                    const float v1 = fmaf((float)field3<3 * (F1 % 10)>(cur.w[F1 / 10]), sc, m4);
                     if constexpr (PHASE == 2) {
                         const f16x2 h = {(_Float16)v0, (_Float16)v1};
                         bv[Q] = __builtin_bit_cast(uint32_t, h);
@@ -865,6 +887,7 @@ void ffn_thin_q3_kernel(FfnArgs a) {
                 });
                 acc = mma<PHASE>(av, bv, acc);
             });
+            cur = nxt;
         }
         thin_reduce_store<PHASE>(a, acc, t, nt, red, wave, lane);
     }
