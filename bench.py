@@ -71,6 +71,13 @@ def parse():
     p.add_argument("--fat-threshold", type=int, default=32)
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 1 GiB device copy (HBM counter calibration)")
+    p.add_argument("--sweep", default=None,
+                   help="comma-separated token counts: time the bf16 Zipf layer at each chunk size "
+                        "(one JSON line per size) instead of the headline measurement")
+    p.add_argument("--multilayer-decode", type=int, default=0, metavar="LAYERS",
+                   help="decode through LAYERS layers of 3-bit experts, eager and as one captured graph, "
+                        "at the batch sizes of --batches (one JSON line) instead of the headline measurement")
+    p.add_argument("--batches", default="1,4,8,16,24", help="decode batch sizes of --multilayer-decode")
     return p.parse_args()
 
 
@@ -189,6 +196,126 @@ def cpu_baseline(shape, seed, n_tokens):
                       f"{dt:.1f} s"}
 
 
+def chunk_sweep(sizes, seed, thr):
+    """The bf16 layer (Zipf router) at several chunk sizes: where the step turns
+    from weight streaming (HBM) to MFMA bound.  One JSON line per size."""
+    import torch
+
+    from moe_inputs import SHAPES, LayerShape
+    from moe_inputs.device import upload_weights
+
+    base = SHAPES["prefill16k"]
+    dev_w = upload_weights(base, seed)
+    for T in sizes:
+        shape = LayerShape(f"chunk{T}", T, base.H, base.I, base.E, base.k, base.router, base.wfmt)
+        run = Runner(shape, seed, dev_w, thr)
+        steps = max(3, min(50, int(2e5 / T)))
+        ms, gu = run.measure(steps, 2)
+        roof = run.roofline(gu)
+        line = {"mode": "chunk_sweep", "tokens": T, "ms_per_step": ms, "tokens_per_s": T / (ms * 1e-3),
+                "gate_up_ms": gu, "gate_up_roofline": roof, "steps": steps, "config": workload_desc(shape, thr)}
+        log(f"[sweep] T={T}: {ms:.3f} ms/step, {T / ms * 1e3:.0f} tok/s, gate/up {gu:.3f} ms "
+            f"({roof['bound']}, {100 * roof['frac']:.1f}% of peak)")
+        print(json.dumps(line), flush=True)
+        del run
+        torch.cuda.empty_cache()
+
+
+def multilayer_decode(n_layers, batches, steps, seed, thr):
+    """Decode through n_layers independent layers of 3-bit experts (weights
+    generated on the device: random codes with the unused bits cleared, fp16
+    scales in [0.001, 0.01]), eager and as one captured graph per batch size.
+    Each layer has its own router logits (Zipf-biased) and input rows; the
+    layers are not chained (the MoE part is timed, not the rest of a block)."""
+    import numpy as np
+    import torch
+
+    import routed_expert_ffn_03_amd as moe
+    from moe_inputs import LayerShape, routing_inputs
+
+    H, I, E, k = 4096, 2048, 384, 8
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(seed)
+    # unused bits: 30-31 of words 0..11, 24-31 of word 12
+    mask = torch.tensor([0x3FFFFFFF] * 12 + [0x00FFFFFF], dtype=torch.int32, device="cuda")
+
+    def q3_matrix(n_out, n_in):
+        w = torch.randint(-2 ** 31, 2 ** 31 - 1, (E, n_out, n_in // 128, 13), dtype=torch.int32, device="cuda",
+                          generator=gen)
+        w &= mask
+        s = (torch.rand((E, n_out, n_in // 128), device="cuda", generator=gen) * 0.009 + 0.001).half()
+        return w, s.view(torch.int16)
+
+    t0 = time.perf_counter()
+    layers = []
+    for _ in range(n_layers):
+        (gw, gs), (uw, us), (dw, ds) = q3_matrix(I, H), q3_matrix(I, H), q3_matrix(H, I)
+        layers.append({"gate": gw, "up": uw, "down": dw, "gate_scale": gs, "up_scale": us, "down_scale": ds})
+    torch.cuda.synchronize()
+    wbytes = sum(t.numel() * t.element_size() for L in layers for t in L.values())
+    log(f"[multilayer] {n_layers} layers of 3-bit experts ({wbytes / 1e9:.1f} GB) generated in "
+        f"{time.perf_counter() - t0:.1f} s")
+    per_expert = 2 * I * (H // 128) * (13 * 4 + 2) + H * (I // 128) * (13 * 4 + 2)
+    results = []
+    for T in batches:
+        shape = LayerShape(f"decode{T}_q3", T, H, I, E, k, "zipf", "q3")
+        bufs, ins, touched = [], [], 0
+        for li in range(n_layers):
+            lg, x = routing_inputs(shape, seed * 1000 + li)
+            ins.append((torch.from_numpy(lg).cuda(), torch.from_numpy(x.view(np.int16)).cuda()))
+            bufs.append(moe.MoELayerBuffers(T, E, k, H, I, moe.MOE_WFMT_Q3G128))
+
+        def step():
+            for li in range(n_layers):
+                bufs[li].forward(ins[li][0], ins[li][1], layers[li], fat_threshold=thr)
+
+        for _ in range(3):
+            step()
+        torch.cuda.synchronize()
+        touched = sum(int((b.expert_counts > 0).sum().item()) for b in bufs)
+        a, b2 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(steps):
+            step()
+        b2.record()
+        torch.cuda.synchronize()
+        eager_ms = a.elapsed_time(b2) / steps
+        eager_out = [b.out.clone() for b in bufs]
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        for _ in range(3):
+            graph.replay()
+        torch.cuda.synchronize()
+        same = all(torch.equal(b.out, o) for b, o in zip(bufs, eager_out))
+        a.record()
+        for _ in range(steps):
+            graph.replay()
+        b2.record()
+        torch.cuda.synchronize()
+        graph_ms = a.elapsed_time(b2) / steps
+        gbs = touched * per_expert / (graph_ms * 1e-3) / 1e9
+        r = {"batch": T, "eager_ms": eager_ms, "graph_ms": graph_ms, "graph_us_per_layer": graph_ms * 1e3 / n_layers,
+             "launch_overhead_us_per_layer": (eager_ms - graph_ms) * 1e3 / n_layers,
+             "tokens_per_s_graph": T / (graph_ms * 1e-3), "touched_experts_per_layer": touched / n_layers,
+             "touched_weight_GBps": gbs, "hbm_frac": gbs / PEAK_HBM_GBS, "graph_equals_eager": same}
+        log(f"[multilayer] T={T}: eager {eager_ms:.3f} ms, graph {graph_ms:.3f} ms for {n_layers} layers "
+            f"({r['graph_us_per_layer']:.1f} us/layer, {touched / n_layers:.1f} experts/layer, "
+            f"{gbs:.0f} GB/s of touched weights), replay == eager: {same}")
+        results.append(r)
+        del graph, bufs
+        torch.cuda.empty_cache()
+    print(json.dumps({"mode": "multilayer_decode", "layers": n_layers, "expert_weights": "q3",
+                      "weights_GB": wbytes / 1e9, "steps": steps, "data": "synthetic (device-generated codes)",
+                      "results": results}), flush=True)
+
+
 def copy_calibration():
     import torch
     n = 1 << 30
@@ -200,6 +327,11 @@ def copy_calibration():
         b.copy_(a)
     torch.cuda.synchronize()
     print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 3}), flush=True)
+
+
+def moe_lib_check():
+    import routed_expert_ffn_03_amd as moe
+    moe.lib()
 
 
 def main():
@@ -215,6 +347,15 @@ def main():
     torch.cuda.set_device(0)
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.sweep:
+        moe_lib_check()
+        chunk_sweep([int(v) for v in args.sweep.split(",")], args.seed, args.fat_threshold)
+        return
+    if args.multilayer_decode:
+        moe_lib_check()
+        multilayer_decode(args.multilayer_decode, [int(v) for v in args.batches.split(",")], args.steps,
+                          args.seed, args.fat_threshold)
         return
 
     import routed_expert_ffn_03_amd as moe
