@@ -164,7 +164,8 @@ class Runner:
         r["traffic"] = measured_traffic(s.name)
         # fat kernel template arguments: <phase, weight format, LDS ring stages>
         fat_name = "ffn_fat_kernel<1, 0, 5>" if s.wfmt == "bf16" else "ffn_fat_kernel<1, 1, 6>"
-        r["kernel"] = f"gate/up phase ({fat_name} + ffn_thin_kernel<1, {0 if s.wfmt == 'bf16' else 1}, w>)"
+        thin_name = "ffn_thin_kernel<1, 4>" if s.wfmt == "bf16" else "ffn_thin_q3_kernel<1>"
+        r["kernel"] = f"gate/up phase ({fat_name} + {thin_name})"
         r["kernel_ms"] = gate_up_ms
         r["algorithmic"] = per
         r["experts_touched"] = touched
