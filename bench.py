@@ -78,6 +78,9 @@ def parse():
                    help="decode through LAYERS layers of 3-bit experts, eager and as one captured graph, "
                         "at the batch sizes of --batches (one JSON line) instead of the headline measurement")
     p.add_argument("--batches", default="1,4,8,16,24", help="decode batch sizes of --multilayer-decode")
+    p.add_argument("--router", action="store_true",
+                   help="time the fused router GEMM + top-k (moe_router_topk) on the 16k and decode batches "
+                        "(one JSON line) instead of the headline measurement")
     return p.parse_args()
 
 
@@ -317,6 +320,53 @@ def multilayer_decode(n_layers, batches, steps, seed, thr):
                       "results": results}), flush=True)
 
 
+def router_bench(seed, steps):
+    """The fused router (x . W_router^T on MFMA, then the top-k gate) on the
+    hidden states of the 16k and decode workloads, 384 experts, top-8; the
+    time of the gate alone on given logits (moe_route_topk) beside it."""
+    import numpy as np
+    import torch
+
+    import routed_expert_ffn_03_amd as moe
+    from moe_inputs import SHAPES, router_weights, routing_inputs
+
+    res = []
+    for name in ("prefill16k", "decode"):
+        s = SHAPES[name]
+        _, x = routing_inputs(s, seed)
+        dx = torch.from_numpy(x.view(np.int16)).cuda()
+        dw = torch.from_numpy(router_weights(s.E, s.H, seed).view(np.int16)).cuda()
+        ids = torch.empty((s.T, s.k), dtype=torch.int32, device="cuda")
+        tw = torch.empty((s.T, s.k), dtype=torch.float32, device="cuda")
+        cnt = torch.empty((s.E,), dtype=torch.int32, device="cuda")
+        lg = torch.empty((s.T, s.E), dtype=torch.float32, device="cuda")
+        n = steps if s.T > 64 else 10 * steps
+
+        def timed(fn):
+            for _ in range(3):
+                fn()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for _ in range(n):
+                fn()
+            b.record()
+            torch.cuda.synchronize()
+            return a.elapsed_time(b) / n
+
+        fused = timed(lambda: moe.moe_router_topk(dx, dw, s.k, ids, tw, cnt))
+        with_logits = timed(lambda: moe.moe_router_topk(dx, dw, s.k, ids, tw, cnt, logits=lg))
+        gate_only = timed(lambda: moe.moe_route_topk(lg, s.k, ids, tw, cnt))
+        flops = 2.0 * s.T * s.E * s.H
+        r = {"workload": name, "tokens": s.T, "experts": s.E, "hidden": s.H, "top_k": s.k,
+             "fused_ms": fused, "with_logits_ms": with_logits, "gate_on_given_logits_ms": gate_only,
+             "fused_tflops": flops / (fused * 1e-3) / 1e12,
+             "fused_mfma_frac": flops / (fused * 1e-3) / 1e12 / PEAK_MFMA_TFLOPS["bf16"]}
+        log(f"[router] {name}: fused {fused * 1e3:.1f} us ({r['fused_tflops']:.0f} TFLOP/s), with logits out "
+            f"{with_logits * 1e3:.1f} us, gate alone on given logits {gate_only * 1e3:.1f} us")
+        res.append(r)
+    print(json.dumps({"mode": "router", "data": "synthetic", "results": res}), flush=True)
+
+
 def copy_calibration():
     import torch
     n = 1 << 30
@@ -352,6 +402,10 @@ def main():
     if args.sweep:
         moe_lib_check()
         chunk_sweep([int(v) for v in args.sweep.split(",")], args.seed, args.fat_threshold)
+        return
+    if args.router:
+        moe_lib_check()
+        router_bench(args.seed, args.steps)
         return
     if args.multilayer_decode:
         moe_lib_check()

@@ -106,6 +106,31 @@ moe_status moe_route_topk(const float* logits, int T, int E, int k,
                           void* stream);
 
 /*
+ * moe_router_topk -- the router GEMM fused with moe_route_topk.
+ *
+ * logits[t, e] = x[t, :] . w_router[e, :] (bf16 products, fp32 accumulation
+ * on MFMA), then for every token exactly the selection, gate weights and
+ * histogram of moe_route_topk applied to these fp32 logits.  The logits stay
+ * on chip unless `logits` is non-NULL, in which case they are also written
+ * there (fp32 [T, E], row-major).  Reading of the pages (routing over the
+ * layer's routed experts: dsv41-flash-offload wiki, opening paragraph; the
+ * router itself is not written there): a bias-free linear router over the
+ * hidden state, the expert's rows stored [E, H] like the expert matrices.
+ *
+ * x          bf16 [T, H];   w_router  bf16 [E, H]
+ * topk_ids int32 [T, k], topk_w fp32 [T, k], expert_counts int32 [E]: as
+ *            moe_route_topk.
+ * Shapes: E a multiple of 128 with 128 <= E <= 512, H a multiple of 32, and
+ * T*H*2 and E*H*2 below 4 GiB, else MOE_ERR_UNSUPPORTED (moe_route_topk takes
+ * any E <= 1024 from given logits).  Errors: NULL x, w_router, topk_ids,
+ * topk_w or expert_counts, T < 1, k outside [1, min(E, 32)], T*k >= 2^31 ->
+ * MOE_ERR_INVALID_ARG.
+ */
+moe_status moe_router_topk(const uint16_t* x, const uint16_t* w_router, int T, int E, int H, int k,
+                           int32_t* topk_ids, float* topk_w, int32_t* expert_counts, float* logits,
+                           void* stream);
+
+/*
  * moe_permute -- per-expert route lists (a stable counting sort of the
  * T*k pairs p = t*k + j by expert id).
  *

@@ -152,6 +152,13 @@ def expert_weight_q3(shape: LayerShape, seed: int, which: str, e: int):
     return words, scales
 
 
+def router_weights(E: int, H: int, seed: int) -> np.ndarray:
+    """Router matrix [E, H] as bf16 bits: bf16_rne(0.02 * N(0,1)) from its own
+    generator, so that with x ~ N(0,1) the logits have a spread near 0.02 * sqrt(H)."""
+    rng = np.random.default_rng([seed, 0x7207, E, H])
+    return float32_to_bf16_bits((0.02 * rng.standard_normal((E, H))).astype(np.float32))
+
+
 def expert_weights(shape: LayerShape, seed: int, e: int) -> dict:
     """All weight arrays of expert ``e`` keyed like :func:`layer_weights`."""
     out = {}

@@ -5,6 +5,6 @@ leg of ``bench.py``; never by the library.
 """
 from .moe_oracle import (  # noqa: F401
     bf16_to_f64, f16_to_f64, q3_fields, q3_pack, q3_dequant, expert_matrices,
-    route_topk, expert_histogram, permute, silu, expert_ffn, grouped_ffn,
+    router_logits, route_topk, expert_histogram, permute, silu, expert_ffn, grouped_ffn,
     combine, moe_layer, dense_layer, rel_max_err,
 )

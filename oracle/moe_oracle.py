@@ -106,6 +106,18 @@ def expert_matrices(raw: dict) -> tuple:
 
 # ------------------------------------------------------------------- route
 
+def router_logits(x_bits: np.ndarray, w_router_bits: np.ndarray) -> np.ndarray:
+    """Router logits logits[t, e] = x[t] . w_router[e], float64 over the exact
+    bf16 values (x [T, H], w_router [E, H]).
+
+    Source: dsv41-flash-offload wiki, opening paragraph -- tokens are routed to
+    a few of the layer's routed experts; the router itself is not written on
+    the pages.  Reading used: a bias-free linear layer over the hidden state,
+    its rows stored [E, H] like the expert matrices.
+    """
+    return bf16_to_f64(x_bits) @ bf16_to_f64(w_router_bits).T
+
+
 def route_topk(logits: np.ndarray, k: int):
     """Top-k expert selection and gate weights for every token.
 

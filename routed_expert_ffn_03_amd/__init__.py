@@ -2,6 +2,7 @@
 (``libmoe_mi355x.so``) with a thin ctypes binding.
 
     moe_route_topk   top-k gate, gate weights, load histogram
+    moe_router_topk  the router GEMM fused with the same top-k gate
     moe_permute      per-expert route lists
     moe_grouped_ffn  every expert's SwiGLU FFN (MFMA tiles for busy experts,
                      HBM-streaming tiles for the rest)
@@ -10,7 +11,7 @@
 from .binding import (  # noqa: F401
     MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP,
     MOE_WFMT_BF16, MOE_WFMT_Q3G128, DEFAULT_FAT_THRESHOLD, EXPORTS, MoEError, lib,
-    moe_workspace_size, moe_route_topk, moe_permute, moe_grouped_ffn, moe_ffn_plan, moe_ffn_gate_up,
+    moe_workspace_size, moe_route_topk, moe_router_topk, moe_permute, moe_grouped_ffn, moe_ffn_plan, moe_ffn_gate_up,
     moe_ffn_down, moe_combine,
 )
 from .layer import MoELayerBuffers  # noqa: F401

@@ -21,7 +21,7 @@ MOE_WFMT_Q3G128 = 1
 
 DEFAULT_FAT_THRESHOLD = 32
 
-EXPORTS = ("moe_status_string", "moe_version", "moe_workspace_size", "moe_route_topk",
+EXPORTS = ("moe_status_string", "moe_version", "moe_workspace_size", "moe_route_topk", "moe_router_topk",
            "moe_permute", "moe_grouped_ffn", "moe_ffn_plan", "moe_ffn_gate_up", "moe_ffn_down",
            "moe_combine")
 
@@ -50,6 +50,8 @@ def lib() -> ctypes.CDLL:
         L.moe_workspace_size.argtypes = [i32] * 6
         L.moe_route_topk.restype = i32
         L.moe_route_topk.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp]
+        L.moe_router_topk.restype = i32
+        L.moe_router_topk.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp]
         L.moe_permute.restype = i32
         L.moe_permute.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp, sz, vp]
         L.moe_grouped_ffn.restype = i32
@@ -105,6 +107,27 @@ def moe_route_topk(logits, k, topk_ids, topk_w, expert_counts, stream=None):
             raise ValueError(f"{n}: shape {tuple(t.shape)} != {shp}")
     _check(lib().moe_route_topk(_ptr(logits), T, E, k, _ptr(topk_ids), _ptr(topk_w), _ptr(expert_counts),
                                 _stream(stream)), "moe_route_topk")
+
+
+def moe_router_topk(x, w_router, k, topk_ids, topk_w, expert_counts, logits=None, stream=None):
+    """Router GEMM (x [T, H] bf16 bits . w_router [E, H] bf16 bits) fused with the top-k gate;
+    ``logits`` (fp32 [T, E]) is written only when given."""
+    T, H = x.shape
+    E = w_router.shape[0]
+    if x.dtype not in (torch.int16, torch.bfloat16) or w_router.dtype not in (torch.int16, torch.bfloat16):
+        raise ValueError("x and w_router: bf16 bit patterns (int16 or bfloat16 tensors)")
+    for t, name in ((x, "x"), (w_router, "w_router")):
+        if not (t.is_cuda and t.is_contiguous()):
+            raise ValueError(f"{name}: expected a contiguous tensor on the GPU")
+    if w_router.shape[1] != H:
+        raise ValueError("w_router must be [E, H]")
+    _dev(topk_ids, torch.int32, "topk_ids")
+    _dev(topk_w, torch.float32, "topk_w")
+    _dev(expert_counts, torch.int32, "expert_counts")
+    if logits is not None:
+        _dev(logits, torch.float32, "logits")
+    _check(lib().moe_router_topk(_ptr(x), _ptr(w_router), T, E, H, k, _ptr(topk_ids), _ptr(topk_w),
+                                 _ptr(expert_counts), _ptr(logits), _stream(stream)), "moe_router_topk")
 
 
 def moe_permute(topk_ids, E, expert_offsets, sorted_pair, pair_to_sorted, workspace, stream=None):

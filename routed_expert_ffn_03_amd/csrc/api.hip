@@ -59,6 +59,15 @@ moe_status moe_route_topk(const float* logits, int T, int E, int k, int32_t* top
                                              reinterpret_cast<hipStream_t>(stream)));
 }
 
+moe_status moe_router_topk(const uint16_t* x, const uint16_t* w_router, int T, int E, int H, int k,
+                           int32_t* topk_ids, float* topk_w, int32_t* expert_counts, float* logits, void* stream) {
+    if (!x || !w_router || !topk_ids || !topk_w || !expert_counts) return MOE_ERR_INVALID_ARG;
+    if (bad_tek(T, E, k) || H < 1) return MOE_ERR_INVALID_ARG;
+    if (!moe::router_shape_ok(T, E, H)) return MOE_ERR_UNSUPPORTED;
+    return hip_status(moe::launch_router_topk(x, w_router, T, E, H, k, topk_ids, topk_w, expert_counts, logits,
+                                              reinterpret_cast<hipStream_t>(stream)));
+}
+
 moe_status moe_permute(const int32_t* topk_ids, int T, int E, int k, int32_t* expert_offsets,
                        int32_t* sorted_pair, int32_t* pair_to_sorted, void* workspace, size_t workspace_bytes,
                        void* stream) {

@@ -38,6 +38,7 @@
 // to bf16 (phase 1) or fp16 (phase 2) as they are staged.
 #include "common.h"
 #include "kernels.h"
+#include "lds_dma.h"
 
 #include <mutex>
 #include <type_traits>
@@ -131,10 +132,6 @@ __device__ __forceinline__ int logical_block() {
 
 // ------------------------------------------------------------ fat kernel
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
-
 // Fat work item -> (M-tile, N-tile).  The items of one expert (count M-tiles
 // x NT N-tiles) are contiguous and walked in super-tiles of gm M-tiles x gn
 // N-tiles (gm * gn = 32, gm <= 8): blocks on one XCD take 32 consecutive
@@ -155,26 +152,6 @@ __device__ __forceinline__ void fat_item(const MTile* __restrict__ fat, int item
     nt = nb * gn + r % gnr;
 }
 
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
-
-__device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)p; }
-
-// LDS reads issued as inline asm: the operand reads of the fat tile must not
-// wait on the direct-to-LDS loads of later stages that are still in flight
-// (the compiler would make every LDS read wait for all of them).
-template <int OFF>
-__device__ __forceinline__ u32x4 ds_read16(uint32_t addr) {
-    u32x4 v;
-    asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "i"(OFF));
-    return v;
-}
-
-__device__ __forceinline__ uint32_t ds_read4(uint32_t addr) {
-    uint32_t v;
-    asm volatile("ds_read_b32 %0, %1" : "=v"(v) : "v"(addr));
-    return v;
-}
-
 // Wait until at most N of this wave's LDS reads are outstanding; the operand
 // registers the wait is for are tied to it, so no use of them is scheduled
 // before it.
@@ -185,11 +162,6 @@ __device__ __forceinline__ void lds_wait_frag(u32x4 (&x)[8], u32x4 (&y)[2]) {
                    "+v"(y[0]), "+v"(y[1])
                  : "n"(N)
                  : "memory");
-}
-
-template <int N>
-__device__ __forceinline__ void vm_wait() {
-    asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
 }
 
 // Wait until at most `stages` stages of this wave's loads are outstanding
@@ -204,16 +176,6 @@ __device__ __forceinline__ void vm_wait_stages(int stages) {
         case 4: vm_wait<4 * L>(); break;
         default: vm_wait<5 * L>(); break;
     }
-}
-
-template <class F, int... I>
-__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
-    (f(std::integral_constant<int, I>{}), ...);
-}
-
-template <int N, class F>
-__device__ __forceinline__ void static_for(F&& f) {
-    static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
 // 3-bit field at bit OFF as one v_bfe_u32 (left to the compiler, a constant

@@ -13,6 +13,9 @@
 // butterfly max, owner clears the winner) give the ordered top-k.
 #include "common.h"
 #include "kernels.h"
+#include "lds_dma.h"
+
+#include <mutex>
 
 namespace moe {
 namespace {
@@ -129,7 +132,219 @@ void route_launch(const float* logits, int T, int E, int k, int32_t* topk_ids, f
     route_topk_kernel<NV><<<blocks, ROUTE_THREADS, 0, s>>>(logits, T, E, k, tpb, 0, topk_ids, topk_w, counts);
 }
 
+// ------------------------------------------------------------ fused router
+
+// Router GEMM + top-k: logits[t, e] = x[t] . W_router[e] (bf16 products, fp32
+// accumulate on MFMA) for a block of RB tokens against all E experts, kept in
+// registers and then in LDS, followed by the same top-k, softmax and histogram
+// as route_topk_kernel (so the choice is exactly route_topk's on these fp32
+// logits).  The logits reach HBM only when the caller asks for them.
+//
+// Tile: RB = 64 tokens x E experts; the four waves side by side, wave w owning
+// experts [w E/4, (w+1) E/4) as CT = E/128 column tiles of 32 against both
+// 32-token row tiles.  Operands stream through a ring of RNS stages of 32 k
+// (activation rows 64 x 64 B, router rows E x 64 B) filled by direct-to-LDS
+// loads, 64-byte LDS rows with the 16-byte chunk c of row r at c ^ ((r >> 2) & 3).
+constexpr int RB = 64;                    // tokens per block
+constexpr int RNS = 4;                    // ring stages
+constexpr int R_THREADS = 256;
+constexpr uint32_t R_ROW = 64;            // bytes of one row per 32-k stage
+
+__host__ __device__ constexpr uint32_t router_stage_bytes(int E) { return (uint32_t)(RB + E) * R_ROW; }
+__host__ __device__ constexpr uint32_t router_lds_bytes(int E) {
+    return router_stage_bytes(E) * RNS > (uint32_t)RB * (E + 8) * 4 ? router_stage_bytes(E) * RNS
+                                                                    : (uint32_t)RB * (E + 8) * 4;
+}
+
+template <int CT>
+__global__ __launch_bounds__(R_THREADS, 1)
+void router_topk_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr, int T, int H, int k,
+                        int32_t* __restrict__ topk_ids, float* __restrict__ topk_w, int32_t* __restrict__ counts,
+                        float* __restrict__ logits_out) {
+    constexpr int E = 128 * CT;
+    constexpr int LW = 1 + 2 * CT;                       // load instructions per wave per stage
+    constexpr uint32_t SB = router_stage_bytes(E);
+    constexpr int LD = E + 8;                            // staged logit row (floats): conflict-free stores
+    extern __shared__ u32x4 smem[];
+    __shared__ int hist[E];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n = lane & 31, g = lane >> 5;
+    const int t0 = blockIdx.x * RB;
+    const int KT = H / 32;
+    for (int e = tid; e < E; e += R_THREADS) hist[e] = 0;
+
+    const __amdgpu_buffer_rsrc_t xsrc = make_rsrc(x, (uint32_t)((size_t)T * H * 2));
+    const __amdgpu_buffer_rsrc_t wsrc = make_rsrc(wr, (uint32_t)((size_t)E * H * 2));
+    // load roles: instruction q of a wave fills 16 rows (4 lanes per 64-byte row),
+    // the chunk landing at position L % 4 being (L % 4) ^ ((row >> 2) & 3)
+    const uint32_t lch16 = (uint32_t)(((lane & 3) ^ ((lane >> 4) & 3)) * 16);
+    const int xr = min(t0 + 16 * wave + (lane >> 2), T - 1);          // rows past T repeat the last one
+    const uint32_t xoff = (uint32_t)xr * (uint32_t)H * 2u + lch16;
+    uint32_t woff[2 * CT];
+#pragma unroll
+    for (int q = 0; q < 2 * CT; ++q) woff[q] = (uint32_t)(wave * (E / 4) + 16 * q + (lane >> 2)) * (uint32_t)H * 2u + lch16;
+    const uint32_t sbase = lds_addr(smem);
+
+    auto issue = [&](int kt, int slot) {
+        char* st = reinterpret_cast<char*>(smem) + slot * SB;
+        dma16(xsrc, st + wave * 1024, xoff, kt * R_ROW);
+#pragma unroll
+        for (int q = 0; q < 2 * CT; ++q) dma16(wsrc, st + RB * R_ROW + (wave * 2 * CT + q) * 1024, woff[q], kt * R_ROW);
+    };
+
+    f32x16 acc[2][CT];
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+        for (int c = 0; c < CT; ++c) acc[r][c] = f32x16{};
+
+    const int pro = min(RNS, KT);
+    for (int s = 0; s < pro; ++s) issue(s, s);
+    for (int kt = 0; kt < KT; ++kt) {
+        const int slot = kt % RNS;
+        switch (min(RNS - 1, KT - 1 - kt)) {                      // stage kt landed (this wave's part) ...
+            case 0: vm_wait<0>(); break;
+            case 1: vm_wait<LW>(); break;
+            case 2: vm_wait<2 * LW>(); break;
+            default: vm_wait<3 * LW>(); break;
+        }
+        __syncthreads();                                          // ... and every wave's
+        const uint32_t st = sbase + slot * SB;
+        u32x4 af[2][2], bf[2][CT];
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            const uint32_t ch = (uint32_t)(((2 * s + g) ^ ((n >> 2) & 3)) * 16);
+            af[s][0] = ds_read16<0>(st + (uint32_t)n * R_ROW + ch);
+            af[s][1] = ds_read16<32 * R_ROW>(st + (uint32_t)n * R_ROW + ch);
+#pragma unroll
+            for (int c = 0; c < CT; ++c)
+                bf[s][c] = ds_read16<0>(st + RB * R_ROW + (uint32_t)(wave * (E / 4) + 32 * c + n) * R_ROW + ch);
+        }
+        lds_wait_all();
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            tie_after_wait(af[s][0]);
+            tie_after_wait(af[s][1]);
+#pragma unroll
+            for (int c = 0; c < CT; ++c) tie_after_wait(bf[s][c]);
+        }
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int r = 0; r < 2; ++r)
+#pragma unroll
+                for (int c = 0; c < CT; ++c) acc[r][c] = mfma_bf16(af[s][r], bf[s][c], acc[r][c]);
+        __syncthreads();                                          // every wave is done with this slot
+        if (kt + RNS < KT) issue(kt + RNS, slot);
+    }
+
+    // logits to LDS: lane holds expert column n of its tile, tokens 8 (i >> 2) + 4 g + (i & 3)
+    float* lg = reinterpret_cast<float*>(smem);
+#pragma unroll
+    for (int r = 0; r < 2; ++r)
+#pragma unroll
+        for (int c = 0; c < CT; ++c)
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                lg[(32 * r + 8 * (i >> 2) + 4 * g + (i & 3)) * LD + wave * (E / 4) + 32 * c + n] = acc[r][c][i];
+    __syncthreads();
+    const int rows = min(RB, T - t0);
+    if (logits_out) {
+        for (int i = tid; i < rows * (E / 4); i += R_THREADS) {
+            const int r = i / (E / 4), c4 = i % (E / 4);
+            const float* src = lg + r * LD + 4 * c4;
+            *reinterpret_cast<float4*>(logits_out + (size_t)(t0 + r) * E + 4 * c4) =
+                make_float4(src[0], src[1], src[2], src[3]);
+        }
+    }
+    // top-k per token, one wave per token: the selection of route_topk_kernel
+    constexpr int NV = E / 64;
+    for (int r = wave; r < rows; r += R_THREADS / 64) {
+        const float* row = lg + r * LD;
+        uint64_t key[NV];
+#pragma unroll
+        for (int i = 0; i < NV; ++i) {
+            const int e = lane + 64 * i;
+            key[i] = ((uint64_t)ordered_bits(row[e]) << 32) | (uint32_t)(~e);
+        }
+        int my_e = 0;
+        float my_v = 0.0f;
+        for (int j = 0; j < k; ++j) {
+            uint64_t m = 0;
+#pragma unroll
+            for (int i = 0; i < NV; ++i) m = key[i] > m ? key[i] : m;
+            m = wave_max_u64(m);
+            const int win = (int)(~(uint32_t)m);
+            if ((win & 63) == lane) {
+#pragma unroll
+                for (int i = 0; i < NV; ++i)
+                    if (i == (win >> 6)) key[i] = 0;
+            }
+            if (lane == j) {
+                my_e = win;
+                my_v = from_ordered((uint32_t)(m >> 32));
+            }
+        }
+        const float v0 = __shfl(my_v, 0, 64);
+        const float z = lane < k ? expf(my_v - v0) : 0.0f;
+        const float sum = wave_sum(z);
+        if (lane < k) {
+            const size_t t = (size_t)(t0 + r);
+            topk_ids[t * k + lane] = my_e;
+            topk_w[t * k + lane] = z / sum;
+            atomicAdd(&hist[my_e], 1);
+        }
+    }
+    __syncthreads();
+    for (int e = tid; e < E; e += R_THREADS)
+        if (hist[e]) atomicAdd(&counts[e], hist[e]);
+}
+
+// the router kernels use more dynamic LDS than the default cap: raised once
+// per device (and kernel) before its first launch there
+std::mutex g_router_mu;
+bool g_router_lds_set[64][4] = {};
+
+template <int CT>
+hipError_t router_launch(const uint16_t* x, const uint16_t* wr, int T, int H, int k, int32_t* ids, float* w,
+                         int32_t* counts, float* logits, hipStream_t s) {
+    constexpr int E = 128 * CT;
+    int dev = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess) return err;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    {
+        std::lock_guard<std::mutex> lock(g_router_mu);
+        if (!g_router_lds_set[dev][CT - 1]) {
+            err = hipFuncSetAttribute((const void*)router_topk_kernel<CT>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                      (int)router_lds_bytes(E));
+            if (err != hipSuccess) return err;
+            g_router_lds_set[dev][CT - 1] = true;
+        }
+    }
+    zero_i32_kernel<<<(E + 255) / 256, 256, 0, s>>>(counts, E);
+    router_topk_kernel<CT><<<(T + RB - 1) / RB, R_THREADS, router_lds_bytes(E), s>>>(x, wr, T, H, k, ids, w,
+                                                                                      counts, logits);
+    return hipGetLastError();
+}
+
 }  // namespace
+
+bool router_shape_ok(int T, int E, int H) {
+    return E % 128 == 0 && E >= 128 && E <= 512 && H % 32 == 0 && H >= 32 && (size_t)T * H * 2 < (1ull << 32) &&
+           (size_t)E * H * 2 < (1ull << 32);
+}
+
+hipError_t launch_router_topk(const uint16_t* x, const uint16_t* w_router, int T, int E, int H, int k,
+                              int32_t* topk_ids, float* topk_w, int32_t* counts, float* logits, hipStream_t s) {
+    switch (E / 128) {
+        case 1: return router_launch<1>(x, w_router, T, H, k, topk_ids, topk_w, counts, logits, s);
+        case 2: return router_launch<2>(x, w_router, T, H, k, topk_ids, topk_w, counts, logits, s);
+        case 3: return router_launch<3>(x, w_router, T, H, k, topk_ids, topk_w, counts, logits, s);
+        default: return router_launch<4>(x, w_router, T, H, k, topk_ids, topk_w, counts, logits, s);
+    }
+}
 
 hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* topk_ids,
                              float* topk_w, int32_t* counts, hipStream_t s) {

@@ -68,6 +68,22 @@ def test_route_rejects(L):
         assert L.moe_route_topk(FAKE, T, E, k, FAKE, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
 
 
+def test_router_rejects(L):
+    ok = dict(x=FAKE, w=FAKE, T=64, E=384, H=4096, k=8, ids=FAKE, tw=FAKE, cnt=FAKE, lg=None)
+    call = lambda **kw: L.moe_router_topk(*[{**ok, **kw}[n] for n in ("x", "w", "T", "E", "H", "k", "ids", "tw",
+                                                                         "cnt", "lg")], None)
+    for key in ("x", "w", "ids", "tw", "cnt"):
+        assert call(**{key: None}) == moe.MOE_ERR_INVALID_ARG, key
+    assert call(T=0) == moe.MOE_ERR_INVALID_ARG
+    assert call(k=0) == moe.MOE_ERR_INVALID_ARG
+    assert call(k=33) == moe.MOE_ERR_INVALID_ARG
+    assert call(E=2048) == moe.MOE_ERR_INVALID_ARG
+    for E in (16, 200, 640, 1024):
+        assert call(E=E, k=2) == moe.MOE_ERR_UNSUPPORTED, E
+    assert call(H=4080) == moe.MOE_ERR_UNSUPPORTED                      # not a multiple of 32
+    assert call(T=1 << 19, H=4096, k=1) == moe.MOE_ERR_UNSUPPORTED      # x = 4 GiB
+
+
 def test_permute_rejects(L):
     assert L.moe_permute(None, 64, 16, 2, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == moe.MOE_ERR_INVALID_ARG
     assert L.moe_permute(FAKE, 64, 16, 0, FAKE, FAKE, FAKE, FAKE, 1 << 20, None) == moe.MOE_ERR_INVALID_ARG

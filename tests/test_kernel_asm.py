@@ -1,4 +1,4 @@
-"""Static checks of the gfx950 assembly of the FFN kernels (CPU only: hipcc
+"""Static checks of the gfx950 assembly of the FFN and router kernels (CPU only: hipcc
 cross-compiles, nothing runs on a GPU).
 
 1. No instruction reads, copies, spills or overwrites the destination
@@ -22,7 +22,9 @@ import pytest
 from tests.asm_check import kernel_bodies, stale_lds_uses
 from routed_expert_ffn_03_amd.build import BUILD, CSRC, HIPCC_FLAGS
 
-SOURCES = ["ffn.hip", "common.h", "kernels.h"]
+# sources compiled to assembly, and every file their hash covers
+UNITS = ["ffn.hip", "route.hip"]
+SOURCES = UNITS + ["common.h", "kernels.h", "lds_dma.h"]
 
 
 def _hipcc():
@@ -38,15 +40,18 @@ def ffn_asm():
     for s in SOURCES:
         with open(os.path.join(CSRC, s), "rb") as f:
             h.update(f.read())
-    out = os.path.join(BUILD, f"ffn_device_{h.hexdigest()[:12]}.s")
-    if not os.path.exists(out):
-        os.makedirs(BUILD, exist_ok=True)
-        cmd = [hipcc, *HIPCC_FLAGS, "--cuda-device-only", "-S", os.path.join(CSRC, "ffn.hip"), "-o", out + ".tmp"]
-        res = subprocess.run(cmd, capture_output=True, text=True, timeout=900)
-        assert res.returncode == 0, res.stderr[-2000:]
-        os.replace(out + ".tmp", out)
-    with open(out) as f:
-        return f.read()
+    text = []
+    for unit in UNITS:
+        out = os.path.join(BUILD, f"{unit.split('.')[0]}_device_{h.hexdigest()[:12]}.s")
+        if not os.path.exists(out):
+            os.makedirs(BUILD, exist_ok=True)
+            cmd = [hipcc, *HIPCC_FLAGS, "--cuda-device-only", "-S", os.path.join(CSRC, unit), "-o", out + ".tmp"]
+            res = subprocess.run(cmd, capture_output=True, text=True, timeout=900)
+            assert res.returncode == 0, res.stderr[-2000:]
+            os.replace(out + ".tmp", out)
+        with open(out) as f:
+            text.append(f.read())
+    return "\n".join(text)
 
 
 def test_checker_flags_a_copy_before_the_wait():
@@ -94,8 +99,8 @@ def test_checker_accepts_clean_code():
 
 
 def test_no_lds_result_used_before_its_wait(ffn_asm):
-    kernels = {k: v for k, v in kernel_bodies(ffn_asm).items() if "ffn_" in k}
-    assert any("ffn_fat_kernel" in k for k in kernels)
+    kernels = {k: v for k, v in kernel_bodies(ffn_asm).items() if "ffn_" in k or "router_topk_kernel" in k}
+    assert any("ffn_fat_kernel" in k for k in kernels) and any("router_topk_kernel" in k for k in kernels)
     bad = {}
     for name, lines in kernels.items():
         r = stale_lds_uses(lines)

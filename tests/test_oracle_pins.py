@@ -265,3 +265,31 @@ def test_q3_pack_round_trip_and_bitwise_decode():
     deq = oracle.q3_dequant(words, scales)
     ref = (fields.astype(np.float64) - 4) * scales.view(np.float16).astype(np.float64)[..., None]
     assert np.array_equal(deq, ref.reshape(3, 512))
+
+
+def test_router_logits_closed_forms():
+    """Router logits: a one-hot hidden state picks one column of W_router; the
+    map is linear in x; a hand-worked 2 x 3 case."""
+    rng = np.random.default_rng(5)
+    E, H = 8, 16
+    w = float32_to_bf16_bits((rng.standard_normal((E, H)) * 0.25).astype(np.float32))
+    wv = oracle.bf16_to_f64(w)
+    for h in (0, 7, 15):
+        x = np.zeros((1, H), dtype=np.float32)
+        x[0, h] = 1.0
+        got = oracle.router_logits(float32_to_bf16_bits(x), w)
+        assert np.array_equal(got[0], wv[:, h])
+    a = float32_to_bf16_bits(rng.standard_normal((3, H)).astype(np.float32))
+    b = float32_to_bf16_bits(rng.standard_normal((3, H)).astype(np.float32))
+    la, lb = oracle.router_logits(a, w), oracle.router_logits(b, w)
+    # x values are bf16-exact; 2 * a is exact too
+    a2 = float32_to_bf16_bits((2 * oracle.bf16_to_f64(a)).astype(np.float32))
+    assert np.allclose(oracle.router_logits(a2, w), 2 * la, rtol=0, atol=1e-12)
+    assert la.shape == (3, E) and lb.shape == (3, E)
+    # hand-worked: x = [1, 2], W = [[1, 0], [0.5, -1], [-2, 0.25]] -> [1, -1.5, -1.5]
+    x = float32_to_bf16_bits(np.array([[1.0, 2.0]], dtype=np.float32))
+    W = float32_to_bf16_bits(np.array([[1.0, 0.0], [0.5, -1.0], [-2.0, 0.25]], dtype=np.float32))
+    assert np.array_equal(oracle.router_logits(x, W), np.array([[1.0, -1.5, -1.5]]))
+    # and the gate on top of it breaks the tie between experts 1 and 2 by index
+    ids, _ = oracle.route_topk(oracle.router_logits(x, W).astype(np.float32), 2)
+    assert ids.tolist() == [[0, 1]]
