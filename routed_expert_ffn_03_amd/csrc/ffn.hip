@@ -133,23 +133,29 @@ __device__ __forceinline__ int logical_block() {
 // ------------------------------------------------------------ fat kernel
 
 // Fat work item -> (M-tile, N-tile).  The items of one expert (count M-tiles
-// x NT N-tiles) are contiguous and walked in super-tiles of gm M-tiles x gn
-// N-tiles (gm * gn = 32, gm <= 8): blocks on one XCD take 32 consecutive
-// items, so the activation rows of gm M-tiles and the weight tiles of gn
-// N-tiles are each fetched once into that XCD's L2 and shared.
+// x NT N-tiles) are contiguous: its M-tiles are split into ceil(count / 8)
+// blocks of near-equal size s (at most 8), and within a block the items run
+// N-tile by N-tile with the s M-tiles of each N-tile next to each other.  The
+// 32 consecutive items that the blocks of one XCD take at a time then cover s
+// activation tiles and about 32 / s weight tiles, each fetched once into that
+// XCD's L2 and shared.
 __device__ __forceinline__ void fat_item(const MTile* __restrict__ fat, int item, int NT, MTile& t, int& nt) {
-    const int q = item / NT;
-    const MTile t0 = fat[q];
+    const int q0 = item / NT;
+    const MTile t0 = fat[q0];
     const int me = t0.count, local = item - t0.first * NT;
-    int gm = 1;
-    while (gm * 2 <= min(me, 8)) gm *= 2;
-    const int gn = min(NT, 32 / gm);
-    const int mb = local / (gm * NT), rem = local - mb * gm * NT;
-    const int gmr = min(gm, me - mb * gm);
-    const int nb = rem / (gmr * gn), r = rem - nb * gmr * gn;
-    const int gnr = min(gn, NT - nb * gn);
-    t = fat[t0.first + mb * gm + r / gnr];
-    nt = nb * gn + r % gnr;
+    const int nblk = (me + 7) >> 3;
+    const int q = me / nblk, r = me - q * nblk;              // r blocks of q + 1 M-tiles, then blocks of q
+    const int big = (q + 1) * NT;
+    int s, m0, off;
+    if (local < r * big) {
+        const int b = local / big;
+        s = q + 1; m0 = b * s; off = local - b * big;
+    } else {
+        const int l2 = local - r * big, b = l2 / (q * NT);
+        s = q; m0 = r * (q + 1) + b * q; off = l2 - b * q * NT;
+    }
+    nt = off / s;
+    t = fat[t0.first + m0 + (off - nt * s)];
 }
 
 // Wait until at most N of this wave's LDS reads are outstanding; the operand
