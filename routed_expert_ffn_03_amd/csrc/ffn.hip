@@ -343,8 +343,10 @@ void ffn_fat_kernel(FfnArgs a) {
     const size_t sbytes = wmat / 128 * 2;
     const int GR = K >> 7;                                    // 3-bit scale groups per weight row
     const uint32_t q3_row_bytes = (uint32_t)GR * (Q3_WORDS * 4);
-    // load roles: instruction q of this wave fills rows 64 wave + 16 q + L/4 of
-    // an operand; the chunk landing at position L%4 is (L%4) ^ ((row >> 2) & 3)
+    // load roles: activation instruction q of this wave fills rows 64 q + 16
+    // wave + L/4 (so the first (RT + 1) / 2 instructions cover the RT row tiles
+    // of a tile, on every wave alike), weight instruction q rows 64 wave + 16 q
+    // + L/4; the chunk landing at position L%4 is (L%4) ^ ((row >> 2) & 3)
     const int lrow = 64 * wave + (lane >> 2);
     const uint32_t lch16 = (uint32_t)(((lane & 3) ^ ((lane >> 4) & 3)) * 16);
     const uint32_t sbase = lds_addr(smem);
@@ -371,7 +373,7 @@ void ffn_fat_kernel(FfnArgs a) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int row = lrow + 16 * q;
-            const int r = min(row, t.rows - 1);
+            const int r = min(64 * q + 16 * wave + (lane >> 2), t.rows - 1);
             const uint32_t src = PHASE == 1 ? (uint32_t)(a.sorted_pair[t.row0 + r] / a.k) : (uint32_t)(t.row0 + r);
             aoff[q] = src * (uint32_t)K * 2u + lch16;
             const uint32_t wrow = PHASE == 1 ? (uint32_t)(nt * 128 + (row & 127)) : (uint32_t)(nt * 256 + row);
@@ -407,7 +409,7 @@ void ffn_fat_kernel(FfnArgs a) {
         auto issue_one = [&](int kt, int slot, int q) {
             char* st = reinterpret_cast<char*>(smem) + slot * Stage::BYTES;
             if (q < 4)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(asrc, (lds_ptr_t)(st + (4 * wave + q) * 1024), 16, aoff[q],
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(asrc, (lds_ptr_t)(st + (4 * q + wave) * 1024), 16, aoff[q],
                                                          kt * DMA_ROW, 0, 0);
             else if constexpr (WFMT == 0)
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(wsrc, (lds_ptr_t)(st + DMA_OPER + (4 * wave + q - 4) * 1024),
@@ -418,10 +420,6 @@ void ffn_fat_kernel(FfnArgs a) {
             else
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(ssrc, (lds_ptr_t)(st + DMA_OPER + Stage::RAW + wave * 256), 4,
                                                          ((sidx + (uint32_t)(kt >> 2)) >> 1) * 4u, 0, 0, 0);
-        };
-        auto issue = [&](int kt, int slot) {
-#pragma unroll
-            for (int q = 0; q < Stage::LOADS; ++q) issue_one(kt, slot, q);
         };
         // bf16: fragment j of 16-k step s in ring slot `slot` (j < RT: activation
         // row tile j; RT + c: weight column tile c; larger j: nothing)
@@ -507,28 +505,37 @@ void ffn_fat_kernel(FfnArgs a) {
             }
         };
 
-        // prologue: the whole ring in flight; stage 0 (and for 3-bit weights
-        // stage 1) landed; 3-bit: stage 0 decoded into B0
-        const int pro = min(NS, KT);
-        for (int s = 0; s < pro; ++s) issue(s, s);
-        vm_wait_stages<Stage::LOADS>(pro - Stage::AHEAD);
-        __builtin_amdgcn_s_barrier();
         u32x4 B0[2][2], B1[2][2];
-        if constexpr (WFMT == 1) {
-            Q3Raw rw;
-            uint32_t bits[4];
-            float sf[2], m4[2];
-            rreads(0, 0, rw);
-            rwait(rw);
-            static_for<16>([&](auto p) { piece(p, 0, rw, bits, sf, m4, B0); });
-        }
-
         auto kloop = [&](auto rt_c) {
             constexpr int RT = decltype(rt_c)::value, S = 2 * RT;
             constexpr int BAR = S / 4;                               // step-1 slot of the stage barrier
-            static_assert(BAR + Stage::LOADS < 16, "the refill loads follow the barrier inside step 1");
-            static_assert(WFMT != 0 || (Stage::LOADS == 8 && 2 * (15 - BAR) >= RT + 2),
-                          "bf16: eight refill loads in the odd slots of step 0, next-step reads after the barrier");
+            // loads per stage: the activation instructions that reach the RT
+            // row tiles, then the weight (or packed word and scale) instructions
+            constexpr int LA = (RT + 1) / 2;
+            constexpr int LOADS = LA + Stage::LOADS - 4;
+            auto issue_i = [&](int kt, int slot, int i) { issue_one(kt, slot, i < LA ? i : i - LA + 4); };
+            auto issue_all = [&](int kt, int slot) {
+#pragma unroll
+                for (int i = 0; i < LOADS; ++i) issue_i(kt, slot, i);
+            };
+            // prologue: the whole ring in flight; stage 0 (and for 3-bit weights
+            // stage 1) landed; 3-bit: stage 0 decoded into B0
+            const int pro = min(NS, KT);
+            for (int s = 0; s < pro; ++s) issue_all(s, s);
+            vm_wait_stages<LOADS>(pro - Stage::AHEAD);
+            __builtin_amdgcn_s_barrier();
+            if constexpr (WFMT == 1) {
+                Q3Raw rw;
+                uint32_t bits[4];
+                float sf[2], m4[2];
+                rreads(0, 0, rw);
+                rwait(rw);
+                static_for<16>([&](auto p) { piece(p, 0, rw, bits, sf, m4, B0); });
+            }
+
+            static_assert(BAR + LOADS < 16, "the refill loads follow the barrier inside step 1");
+            static_assert(WFMT != 0 || (LOADS <= 8 && 2 * (15 - BAR) >= RT + 2),
+                          "bf16: one refill load per odd slot of step 0, next-step reads after the barrier");
             u32x4 x0[8], x1[8], y0[2], y1[2];
             reads(rt_c, 0, 0, x0, y0);
             int slot = 0;
@@ -556,7 +563,8 @@ void ffn_fat_kernel(FfnArgs a) {
                             read_one(rt_c, std::integral_constant<int, I>{}, slot, 1, x1, y1);
                             read_one(rt_c, std::integral_constant<int, I + 1>{}, slot, 1, x1, y1);
                         } else {
-                            if (refill) issue_one(kt - 1 + NS, pslot, I / 2);
+                            if constexpr (I / 2 < LOADS)
+                                if (refill) issue_i(kt - 1 + NS, pslot, I / 2);
                         }
                     });
                     lds_wait_frag<0>(x1, y1);
@@ -565,7 +573,7 @@ void ffn_fat_kernel(FfnArgs a) {
                         constexpr int I = decltype(i)::value;
                         if constexpr (PHASE == 2 && I < 2) y1[I] = bf16x8_to_f16x8(y1[I]);
                         if constexpr (I == BAR && more) {
-                            vm_wait_stages<Stage::LOADS>(min(NS - 2, KT - 2 - kt));   // stage kt+1 landed here
+                            vm_wait_stages<LOADS>(min(NS - 2, KT - 2 - kt));   // stage kt+1 landed here
                             __builtin_amdgcn_s_barrier();                              // ... and in every lane
                         }
                         if constexpr (I > BAR && more) {
@@ -622,11 +630,11 @@ void ffn_fat_kernel(FfnArgs a) {
                         constexpr int I = decltype(i)::value;
                         pieces_at(St1{}, i);
                         if constexpr (I == BAR && more) {
-                            vm_wait_stages<Stage::LOADS>(max(0, min(NS - 3, KT - 3 - kt)));
+                            vm_wait_stages<LOADS>(max(0, min(NS - 3, KT - 3 - kt)));
                             __builtin_amdgcn_s_barrier();
                         }
-                        if constexpr (I > BAR && I <= BAR + Stage::LOADS) {
-                            if (kt + NS < KT) issue_one(kt + NS, slot, I - BAR - 1);   // one load per MFMA slot
+                        if constexpr (I > BAR && I <= BAR + LOADS) {
+                            if (kt + NS < KT) issue_i(kt + NS, slot, I - BAR - 1);     // one load per MFMA slot
                         }
                         if constexpr (I == BAR + 2 && more) reads(rt_c, nslot, 0, x0, y0);
                     });
