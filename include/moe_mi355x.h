@@ -79,8 +79,11 @@ const char* moe_version(void);
  * Bytes of workspace needed by moe_permute and moe_grouped_ffn for a layer
  * of T tokens, E experts, top-k, hidden H, expert intermediate I and the
  * weight format `wfmt`.  One buffer of this size serves both calls (they
- * use it in stream order).  Returns 0 for arguments that are invalid or
- * unsupported.  Alignment: 256 bytes (any hipMalloc pointer).
+ * use it in stream order).  MOE_WFMT_Q3G128 needs T*H*2 + T*(H/128)*4 more
+ * bytes (rounded up to 256 each) than MOE_WFMT_BF16: a reordered copy of the
+ * thin experts' activation rows and their 128-group sums.  Returns 0 for
+ * arguments that are invalid or unsupported.  Alignment: 256 bytes (any
+ * hipMalloc pointer).
  */
 size_t moe_workspace_size(int T, int E, int k, int H, int I, int wfmt);
 

@@ -48,7 +48,7 @@ const char* moe_version(void) { return "0.1.0"; }
 size_t moe_workspace_size(int T, int E, int k, int H, int I, int wfmt) {
     if (bad_tek(T, E, k) || !ffn_shape_ok(T, k, H, I)) return 0;
     if (wfmt != MOE_WFMT_BF16 && wfmt != MOE_WFMT_Q3G128) return 0;
-    return align256(moe::permute_ws_bytes(T, E)) + moe::ffn_ws_bytes(T, E, k, H, I);
+    return align256(moe::permute_ws_bytes(T, E)) + moe::ffn_ws_bytes(T, E, k, H, I, wfmt);
 }
 
 moe_status moe_route_topk(const float* logits, int T, int E, int k, int32_t* topk_ids, float* topk_w,

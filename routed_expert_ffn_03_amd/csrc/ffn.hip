@@ -76,6 +76,8 @@ struct FfnArgs {
     int T, k, H, I;
     uint16_t* act;
     uint16_t* y;
+    uint16_t* xq;                 // 3-bit thin path: x rows in pair-slot order per 128-group
+    uint32_t* xs;                 // ... and each (token, group) sum of x as a bf16 hi, lo pair
     const FfnHeader* hdr;
     const MTile* fat;
     const MTile* thin;
@@ -663,6 +665,89 @@ void ffn_fat_kernel(FfnArgs a) {
     }
 }
 
+// ------------------------------------------------------------ 3-bit pair slots
+//
+// The gate/up thin path for tiles of at most 16 rows feeds the MFMA with the
+// 3-bit codes themselves: the bf16 number 128 + u (bits 0x4300 | u) is exact,
+// and two of them come out of one packed 16-bit shift and one and-or when the
+// pair is fields i and i + 5 of a word (bits 3i and 3i + 15).  Slot 2P and
+// 2P + 1 of a 128-group hold pair P: fields 10w + i and 10w + i + 5 for
+// P = 5w + i < 60, fields 120 + i and 125 + i for P = 60 + i < 63, and fields
+// 123, 124 for P = 63.  The activations are stored in the same slot order
+// (the MFMA sums over k in any order), and
+//   sum_k x_k (u_k - 4) = sum_k x_k (128 + u_k) - 132 sum_k x_k,
+// the last term through one more MFMA step against the group sum of x.
+__host__ __device__ constexpr int pair_field(int slot) {
+    const int P = slot >> 1, hi = slot & 1;
+    if (P == 63) return 123 + hi;
+    const int a = P < 60 ? 10 * (P / 5) + P % 5 : 120 + (P - 60);
+    return a + 5 * hi;
+}
+
+typedef __attribute__((ext_vector_type(2))) unsigned short u16x2;
+
+// bf16 pair (128 + u_a, 128 + u_b) of pair P from the group's 13 words;
+// `magic` holds 0x43004300 in a VGPR, so the mask and the or are one
+// v_and_or_b32 (a VOP3 instruction reads at most one SGPR or constant here)
+template <int P>
+__device__ __forceinline__ uint32_t magic_pair(const uint32_t (&w)[Q3_WORDS], uint32_t magic) {
+    if constexpr (P == 63) {
+        return ((w[12] >> 9) & 7u) | (((w[12] >> 12) & 7u) << 16) | magic;
+    } else {
+        constexpr int W = P < 60 ? P / 5 : 12, I = P < 60 ? P % 5 : P - 60;
+        const u16x2 v = __builtin_bit_cast(u16x2, w[W] << 1);
+        const u16x2 sh = {(unsigned short)(3 * I + 1), (unsigned short)(3 * I)};
+        return (__builtin_bit_cast(uint32_t, v >> sh) & 0x00070007u) | magic;
+    }
+}
+
+typedef __attribute__((ext_vector_type(4), aligned(4))) uint32_t u32x4a4;   // 4-byte aligned 16-byte load
+
+// For every token of a thin tile of at most 16 rows: its x row in pair-slot
+// order per 128-group (xq) and each group sum of x, summed in fp64 and stored
+// as bf16 hi + lo (xs).  A token in several thin tiles is written with the
+// same values each time.
+__global__ __launch_bounds__(256)
+void q3_xprep_kernel(FfnArgs a) {
+    const int NG = a.H >> 7;
+    const int per_tile = 16 * NG;
+    const int n_tasks = a.hdr->n_thin * per_tile;
+    for (int task = blockIdx.x * 256 + threadIdx.x; task < n_tasks; task += gridDim.x * 256) {
+        const int mt = task / per_tile, rem = task - mt * per_tile;
+        const int m = rem / NG, G = rem - m * NG;
+        const MTile t = a.thin[mt];
+        if (t.rows > 16 || m >= t.rows) continue;
+        const size_t tok = (size_t)(a.sorted_pair[t.row0 + m] / a.k);
+        const u32x4* src = reinterpret_cast<const u32x4*>(a.x + tok * a.H + (size_t)G * 128);
+        u32x4* dst = reinterpret_cast<u32x4*>(a.xq + tok * a.H + (size_t)G * 128);
+        uint32_t v[64];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const u32x4 q = src[i];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) v[4 * i + j] = q[j];
+        }
+        auto half = [&](int f) -> uint32_t { return (v[f >> 1] >> (16 * (f & 1))) & 0xFFFFu; };
+        double sum = 0.0;
+#pragma unroll
+        for (int f = 0; f < 128; ++f) sum += (double)__uint_as_float(half(f) << 16);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            u32x4 o;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int d = 4 * i + j;
+                o[j] = half(pair_field(2 * d)) | (half(pair_field(2 * d + 1)) << 16);
+            }
+            dst[i] = o;
+        }
+        const __bf16 hi = (__bf16)(float)sum;
+        const __bf16 lo = (__bf16)(float)(sum - (double)(float)hi);
+        a.xs[tok * NG + G] = (uint32_t)__builtin_bit_cast(uint16_t, hi) |
+                             ((uint32_t)__builtin_bit_cast(uint16_t, lo) << 16);
+    }
+}
+
 // ------------------------------------------------------------ thin kernels
 
 // The four waves' partial 32 x 32 tiles of one thin item are summed through
@@ -762,6 +847,106 @@ void ffn_thin_kernel(FfnArgs a) {
     }
 }
 
+// One gate/up item of the 3-bit thin kernel for a tile of at most 16 rows,
+// on the pair-slot operands (see q3_xprep_kernel): lanes m < 16 carry the
+// activations of group 2p in k-half 0 and lanes m >= 16 those of group 2p + 1
+// in k-half 1, so accumulator rows 0..15 collect the first group's sums and
+// rows 16..31 the second's for the same tokens; each pair ends with the
+// 132 x group-sum step, and the two groups' fp16 scales are applied in fp32.
+__device__ __forceinline__ void thin_q3_pairs(const FfnArgs& a, const MTile& t, int nt,
+                                              __amdgpu_buffer_rsrc_t xqsrc, __amdgpu_buffer_rsrc_t xssrc,
+                                              float (&red)[4][16][64], int wave, int lane) {
+    constexpr uint32_t NOWHERE = 0xFFFFFF00u;
+    const int m = lane & 31, g = lane >> 5, mm = m & 15;
+    const int NG = a.H >> 7, NP = (NG + 1) >> 1;
+    const size_t mat_words = (size_t)a.I * NG * Q3_WORDS;
+    const bool act_lane = (m >> 4) == g && mm < t.rows;
+    uint32_t xo = 0, so = 0;
+    if (act_lane) {
+        const uint32_t tok = (uint32_t)(a.sorted_pair[t.row0 + mm] / a.k);
+        xo = tok * (uint32_t)a.H * 2u;
+        so = tok * (uint32_t)NG * 4u;
+    }
+    // this lane's weight row: gate rows nt*16.. (m < 16), then the matching up
+    // rows; plain global loads (the two matrices would make a buffer resource
+    // lane-dependent)
+    const int row = nt * 16 + mm;
+    const uint32_t* wrow = reinterpret_cast<const uint32_t*>(m < 16 ? a.wg : a.wu) + (size_t)t.e * mat_words +
+                           (size_t)row * NG * Q3_WORDS;
+    const uint16_t* srow = (m < 16 ? a.sg : a.su) + ((size_t)t.e * a.I + row) * NG;
+    uint32_t magic;
+    asm volatile("v_mov_b32 %0, 0x43004300" : "=v"(magic));
+
+    // the 13 words of group 2p+g of this lane's row, and the row's scales of groups 2p and 2p+1
+    struct Pair {
+        uint32_t w[Q3_WORDS];
+        uint16_t s0, s1;
+    };
+    auto load_pair = [&](int p, Pair& q) {
+        const int G = min(2 * p + g, NG - 1);     // past an odd count: a real group whose sums are zero
+        const uint32_t* gw = wrow + G * Q3_WORDS;
+        const u32x4a4 q0 = *reinterpret_cast<const u32x4a4*>(gw);
+        const u32x4a4 q1 = *reinterpret_cast<const u32x4a4*>(gw + 4);
+        const u32x4a4 q2 = *reinterpret_cast<const u32x4a4*>(gw + 8);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            q.w[i] = q0[i];
+            q.w[4 + i] = q1[i];
+            q.w[8 + i] = q2[i];
+        }
+        q.w[12] = gw[12];
+        q.s0 = srow[2 * p];
+        q.s1 = srow[min(2 * p + 1, NG - 1)];
+    };
+
+    // offsets of the activation slots and of the group sum of pair p for this
+    // lane (past the buffers -- zeros -- off its half, past the groups or p)
+    auto act_off = [&](int p) { return act_lane && 2 * p + g < NG ? xo + (uint32_t)(2 * p + g) * 256u : NOWHERE; };
+    auto sum_off = [&](int p) { return act_lane && 2 * p + g < NG ? so + (uint32_t)(2 * p + g) * 4u : NOWHERE; };
+
+    float fin[8] = {};
+    Pair cur, nxt;
+    u32x4 av[16];
+    uint32_t xsum = 0;
+    if (wave < NP) {
+        load_pair(wave, cur);
+        const uint32_t ao = act_off(wave);
+#pragma unroll
+        for (int j = 0; j < 16; ++j) av[j] = __builtin_amdgcn_raw_buffer_load_b128(xqsrc, ao, 16 * j, 0);
+        xsum = __builtin_amdgcn_raw_buffer_load_b32(xssrc, sum_off(wave), 0, 0);
+    }
+    for (int p = wave; p < NP; p += 4) {
+        const bool more = p + 4 < NP;
+        if (more) load_pair(p + 4, nxt);         // next pair's words in flight during this one
+        // each activation register is refilled with the next pair's slots
+        // right after its MFMA has read it
+        const uint32_t aon = more ? act_off(p + 4) : NOWHERE;
+        f32x16 c = f32x16{};
+        static_for<16>([&](auto j_c) {
+            constexpr int J = decltype(j_c)::value;
+            u32x4 bv;
+            static_for<4>([&](auto q_c) {
+                constexpr int Q = decltype(q_c)::value;
+                bv[Q] = magic_pair<4 * J + Q>(cur.w, magic);
+            });
+            c = mfma_bf16(av[J], bv, c);
+            av[J] = __builtin_amdgcn_raw_buffer_load_b128(xqsrc, aon, 16 * J, 0);
+        });
+        // minus 132 x (group sum, as bf16 hi + lo): exact bf16 weights -132 in k-slots 0 and 1 of each half
+        c = mfma_bf16(u32x4{xsum, 0u, 0u, 0u}, u32x4{0xC304C304u, 0u, 0u, 0u}, c);
+        xsum = __builtin_amdgcn_raw_buffer_load_b32(xssrc, more ? sum_off(p + 4) : NOWHERE, 0, 0);
+        const float s0 = (float)__builtin_bit_cast(_Float16, cur.s0);
+        const float s1 = 2 * p + 1 < NG ? (float)__builtin_bit_cast(_Float16, cur.s1) : 0.0f;
+#pragma unroll
+        for (int r = 0; r < 8; ++r) fin[r] = fmaf(s1, c[r + 8], fmaf(s0, c[r], fin[r]));
+        cur = nxt;
+    }
+    f32x16 acc = f32x16{};
+#pragma unroll
+    for (int r = 0; r < 8; ++r) acc[r] = fin[r];
+    thin_reduce_store<1>(a, acc, t, nt, red, wave, lane);
+}
+
 // 3-bit thin kernel: the same items, waves and reduction as the bf16 thin
 // kernel, with the reduction index walked a group pair at a time.  For MFMA
 // step j (0..15) of pair p, lane half g holds fields 8j..8j+7 of group 2p+g
@@ -794,10 +979,18 @@ void ffn_thin_q3_kernel(FfnArgs a) {
         ? make_rsrc(a.x, (uint32_t)((size_t)a.T * a.H * 2))
         : make_rsrc(a.act, (uint32_t)((size_t)a.T * a.k * a.I * 2));
     constexpr uint32_t NOWHERE = 0xFFFFFF00u;
+    const __amdgpu_buffer_rsrc_t xqsrc = make_rsrc(a.xq, PHASE == 1 ? (uint32_t)((size_t)a.T * a.H * 2) : 0u);
+    const __amdgpu_buffer_rsrc_t xssrc = make_rsrc(a.xs, PHASE == 1 ? (uint32_t)((size_t)a.T * NG * 4) : 0u);
 
     for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
         const int nt = item / n_mt, mt = item % n_mt;
         const MTile t = a.thin[mt];
+        if constexpr (PHASE == 1) {
+            if (t.rows <= 16) {
+                thin_q3_pairs(a, t, nt, xqsrc, xssrc, red, wave, lane);
+                continue;
+            }
+        }
         const bool has_row = m < t.rows;
         uint32_t aoff = 0;
         if (has_row) {
@@ -874,12 +1067,11 @@ void ffn_thin_q3_kernel(FfnArgs a) {
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct FfnLayout {
-    size_t hdr, fat, thin, act, total;
+    size_t hdr, fat, thin, act, xq, xs, total;
     size_t max_fat, max_thin;
 };
 
-FfnLayout ffn_layout(int T, int E, int k, int H, int I) {
-    (void)H;
+FfnLayout ffn_layout(int T, int E, int k, int H, int I, int wfmt) {
     const size_t P = (size_t)T * k;
     const size_t nz = P < (size_t)E ? P : (size_t)E;        // experts that can be non-empty
     FfnLayout L;
@@ -889,7 +1081,11 @@ FfnLayout ffn_layout(int T, int E, int k, int H, int I) {
     L.fat = align256(sizeof(FfnHeader));
     L.thin = L.fat + align256(L.max_fat * sizeof(MTile));
     L.act = L.thin + align256(L.max_thin * sizeof(MTile));
-    L.total = L.act + align256(P * (size_t)I * sizeof(uint16_t));
+    L.xq = L.act + align256(P * (size_t)I * sizeof(uint16_t));
+    // 3-bit weights: reordered x rows and group sums for the thin gate/up path
+    const size_t xq_bytes = wfmt == 1 ? align256((size_t)T * H * sizeof(uint16_t)) : 0;
+    L.xs = L.xq + xq_bytes;
+    L.total = L.xs + (wfmt == 1 ? align256((size_t)T * (H / 128) * sizeof(uint32_t)) : 0);
     return L;
 }
 
@@ -957,7 +1153,7 @@ hipError_t dev_info(DevInfo& out) {
 }
 
 FfnArgs make_args(const FfnLaunch& a) {
-    const FfnLayout L = ffn_layout(a.T, a.E, a.k, a.H, a.I);
+    const FfnLayout L = ffn_layout(a.T, a.E, a.k, a.H, a.I, a.wfmt);
     char* ws = reinterpret_cast<char*>(a.ws);
     FfnArgs fa;
     fa.x = a.x;
@@ -966,6 +1162,8 @@ FfnArgs make_args(const FfnLaunch& a) {
     fa.sorted_pair = a.sorted_pair;
     fa.T = a.T; fa.k = a.k; fa.H = a.H; fa.I = a.I;
     fa.act = reinterpret_cast<uint16_t*>(ws + L.act);
+    fa.xq = a.wfmt == 1 ? reinterpret_cast<uint16_t*>(ws + L.xq) : nullptr;
+    fa.xs = a.wfmt == 1 ? reinterpret_cast<uint32_t*>(ws + L.xs) : nullptr;
     fa.y = a.y;
     fa.hdr = reinterpret_cast<FfnHeader*>(ws + L.hdr);
     fa.fat = reinterpret_cast<MTile*>(ws + L.fat);
@@ -991,6 +1189,7 @@ void launch_phase_t(const FfnArgs& fa, const DevInfo& d, bool fat_possible, hipS
         }
     }
     if constexpr (WFMT != 0) {
+        if constexpr (PHASE == 1) q3_xprep_kernel<<<d.cus, 256, 0, s>>>(fa);
         ffn_thin_q3_kernel<PHASE><<<d.cus * d.thin_blocks[1][PHASE - 1][0], THIN_THREADS, 0, s>>>(fa);
     } else {
         // whole 128-byte lines per row when each wave's quarter of K is a multiple of 64
@@ -1004,10 +1203,10 @@ void launch_phase_t(const FfnArgs& fa, const DevInfo& d, bool fat_possible, hipS
 
 }  // namespace
 
-size_t ffn_ws_bytes(int T, int E, int k, int H, int I) { return ffn_layout(T, E, k, H, I).total; }
+size_t ffn_ws_bytes(int T, int E, int k, int H, int I, int wfmt) { return ffn_layout(T, E, k, H, I, wfmt).total; }
 
 hipError_t launch_ffn_plan(const FfnLaunch& a, hipStream_t s) {
-    const FfnLayout L = ffn_layout(a.T, a.E, a.k, a.H, a.I);
+    const FfnLayout L = ffn_layout(a.T, a.E, a.k, a.H, a.I, a.wfmt);
     char* ws = reinterpret_cast<char*>(a.ws);
     build_tiles_kernel<<<1, 1024, 0, s>>>(a.offsets, a.E, a.fat_threshold,
                                           reinterpret_cast<FfnHeader*>(ws + L.hdr),

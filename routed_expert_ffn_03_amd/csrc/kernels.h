@@ -38,7 +38,7 @@ struct FfnLaunch {
     void* ws;                       // FFN part of the workspace
 };
 
-size_t ffn_ws_bytes(int T, int E, int k, int H, int I);
+size_t ffn_ws_bytes(int T, int E, int k, int H, int I, int wfmt);
 hipError_t launch_ffn_plan(const FfnLaunch& a, hipStream_t s);
 hipError_t launch_ffn_phase(const FfnLaunch& a, int phase, hipStream_t s);   // 1 = gate/up, 2 = down
 

@@ -48,7 +48,9 @@ def test_status_strings(L):
 def test_workspace_size(L):
     ws = L.moe_workspace_size(16384, 384, 8, 4096, 2048, 0)
     assert ws >= 16384 * 8 * 2048 * 2             # the fp16 activation dominates
-    assert L.moe_workspace_size(16384, 384, 8, 4096, 2048, 1) == ws
+    r256 = lambda v: (v + 255) // 256 * 256
+    # 3-bit: plus the reordered thin activation rows and their 128-group sums
+    assert L.moe_workspace_size(16384, 384, 8, 4096, 2048, 1) == ws + r256(16384 * 4096 * 2) + r256(16384 * 32 * 4)
     assert L.moe_workspace_size(4, 384, 8, 4096, 2048, 0) > 0
     for bad in [(0, 384, 8, 4096, 2048, 0), (4, 2000, 8, 4096, 2048, 0), (4, 384, 0, 4096, 2048, 0),
                 (4, 384, 33, 4096, 2048, 0), (4, 4, 5, 4096, 2048, 0), (4, 384, 8, 4000, 2048, 0),
