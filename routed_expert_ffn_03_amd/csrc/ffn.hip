@@ -796,42 +796,65 @@ void ffn_thin_kernel(FfnArgs a) {
     const int nch = Kw / (16 * CW);         // chunks: lane half g covers 8 CW k of each
     const int kbase = wave * Kw + g * 8 * CW;
 
-    for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
-        const int nt = item / n_mt, mt = item % n_mt;
-        const MTile t = a.thin[mt];
-        const uint16_t* arow = nullptr;
-        if (m < t.rows) {
-            if (PHASE == 1) arow = a.x + (size_t)(a.sorted_pair[t.row0 + m] / a.k) * a.H;
-            else arow = a.act + (size_t)(t.row0 + m) * a.I;
-        }
-        // this lane's weight row (bf16): phase 1 gate rows nt*16.. (m < 16)
-        // and the matching up rows, phase 2 down rows nt*32 + m
-        const uint16_t* brow;
+    // an item's operand rows: the activation row of lane m (null past the
+    // tile) and the weight row (phase 1: gate rows nt*16.. for m < 16 and the
+    // matching up rows, phase 2: down rows nt*32 + m)
+    auto rows_of = [&](const MTile& t, int nt, int src, const uint16_t*& arow, const uint16_t*& brow) {
+        arow = nullptr;
+        if (m < t.rows) arow = PHASE == 1 ? a.x + (size_t)src * a.H : a.act + (size_t)(t.row0 + m) * a.I;
         if (PHASE == 1) {
             const size_t n = (size_t)t.e * a.I + nt * 16 + (m & 15);
             brow = reinterpret_cast<const uint16_t*>(m < 16 ? a.wg : a.wu) + n * (size_t)K;
         } else {
             brow = reinterpret_cast<const uint16_t*>(a.wd) + ((size_t)t.e * a.H + nt * 32 + m) * (size_t)K;
         }
+    };
+    // phase 1: the token of lane m's row (loaded one item ahead)
+    auto token_of = [&](const MTile& t) { return PHASE == 1 && m < t.rows ? a.sorted_pair[t.row0 + m] / a.k : 0; };
 
-        u32x4 ra[D][CW], rw[D][CW];
-        auto load = [&](int ch, u32x4 (&xa)[CW], u32x4 (&xw)[CW]) {
-            const int k0 = kbase + ch * 16 * CW;
+    u32x4 ra[D][CW], rw[D][CW];
+    const uint16_t* arow;
+    const uint16_t* brow;
+    auto load = [&](int ch, u32x4 (&xa)[CW], u32x4 (&xw)[CW]) {
+        const int k0 = kbase + ch * 16 * CW;
 #pragma unroll
-            for (int c = 0; c < CW; ++c) {
-                xa[c] = u32x4{0, 0, 0, 0};
-                if (arow) xa[c] = ldg16(arow + k0 + 8 * c);
-            }
+        for (int c = 0; c < CW; ++c) {
+            xa[c] = u32x4{0, 0, 0, 0};
+            if (arow) xa[c] = ldg16(arow + k0 + 8 * c);
+        }
 #pragma unroll
-            for (int c = 0; c < CW; ++c) {
-                const u32x4 v = ldg16(brow + k0 + 8 * c);
-                xw[c] = PHASE == 2 ? bf16x8_to_f16x8(v) : v;       // fp16 MFMA for the down projection
-            }
-        };
-        f32x16 acc = f32x16{};
+        for (int c = 0; c < CW; ++c) {
+            const u32x4 v = ldg16(brow + k0 + 8 * c);
+            xw[c] = PHASE == 2 ? bf16x8_to_f16x8(v) : v;       // fp16 MFMA for the down projection
+        }
+    };
+    // the first D - 1 chunks of an item go out before the previous item's
+    // reduction, so a block's loads do not drain between items
+    auto prologue = [&]() {
 #pragma unroll
         for (int d = 0; d < D - 1; ++d)
             if (d < nch) load(d, ra[d], rw[d]);
+    };
+
+    int item = blockIdx.x;
+    MTile t{};
+    int nt = 0;
+    if (item < n_items) {
+        nt = item / n_mt;
+        t = a.thin[item % n_mt];
+        rows_of(t, nt, token_of(t), arow, brow);
+        prologue();
+    }
+    while (item < n_items) {
+        const int next = item + (int)gridDim.x;
+        MTile tn{};
+        int ntn = 0, srcn = 0;
+        if (next < n_items) {
+            ntn = next / n_mt;
+            tn = a.thin[next % n_mt];
+            srcn = token_of(tn);
+        }
+        f32x16 acc = f32x16{};
         for (int c0 = 0; c0 < nch; c0 += D) {
 #pragma unroll
             for (int d = 0; d < D; ++d) {
@@ -843,7 +866,14 @@ void ffn_thin_kernel(FfnArgs a) {
                 }
             }
         }
+        if (next < n_items) {
+            rows_of(tn, ntn, srcn, arow, brow);
+            prologue();
+        }
         thin_reduce_store<PHASE>(a, acc, t, nt, red, wave, lane);
+        item = next;
+        t = tn;
+        nt = ntn;
     }
 }
 
