@@ -80,3 +80,47 @@ def test_layer_graph_replay_matches_eager(shape):
                               got, refs[i]):
             assert torch.equal(g, r), f"replay {rep} (inputs {i}): {name} differs from eager"
         say(f"   replay {rep} on inputs {i}: identical to eager")
+
+
+# More fat items than one round of blocks, so the gate/up phase runs both its
+# static rounds and its counter-driven tail; and a layer with fewer items than
+# blocks (all of them from the counter).
+REPEAT_CASES = [
+    LayerShape("mid", 700, 512, 384, 6, 2, "normal", "bf16"),
+    LayerShape("many", 8192, 256, 1024, 64, 8, "normal", "bf16"),
+    LayerShape("many_q3", 8192, 256, 1024, 64, 8, "normal", "q3"),
+]
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("shape", REPEAT_CASES, ids=[s.name for s in REPEAT_CASES])
+def test_ffn_phases_repeat_on_one_plan(shape):
+    """The fat gate/up kernel hands out its last rounds of items from a
+    counter in the workspace; the last block of each launch re-zeroes it.
+    Gate/up and down run again and again on one plan (no re-plan in between),
+    alternating two activation inputs with the same routing, must reproduce
+    each input's y bit for bit: an item skipped because the counter was left
+    high would keep the other input's activations."""
+    say(f"[repeat] {shape.name} T={shape.T} E={shape.E} k={shape.k} H={shape.H} I={shape.I} wfmt={shape.wfmt}")
+    lg, x0 = routing_inputs(shape, 0)
+    _, x1 = routing_inputs(shape, 1)
+    w = to_dev_weights(layer_weights(shape, 0))
+    b = moe.MoELayerBuffers(shape.T, shape.E, shape.k, shape.H, shape.I, wfmt_id(shape))
+    logits = torch.from_numpy(lg).cuda()
+    xs = [torch.from_numpy(xx.view(np.int16)).cuda() for xx in (x0, x1)]
+    refs = []
+    for x in xs:
+        b.forward(logits, x, w)
+        torch.cuda.synchronize()
+        refs.append(b.y_sorted.clone())
+    assert not torch.equal(refs[0], refs[1])
+    for rep in range(4):
+        i = rep % 2
+        b.y_sorted.zero_()
+        moe.moe_ffn_gate_up(xs[i], w["gate"], w["up"], b.sorted_pair, shape.E, shape.k, b.workspace,
+                            s_gate=w.get("gate_scale"), s_up=w.get("up_scale"), wfmt=wfmt_id(shape))
+        moe.moe_ffn_down(w["down"], shape.T, shape.E, shape.k, shape.I, b.y_sorted, b.workspace,
+                         s_down=w.get("down_scale"), wfmt=wfmt_id(shape))
+        torch.cuda.synchronize()
+        assert torch.equal(b.y_sorted, refs[i]), f"repeat {rep} (input {i}): y differs"
+        say(f"   repeat {rep} on input {i}: identical")
