@@ -69,6 +69,37 @@ def test_layer_small(shape, thresholds):
     assert np.array_equal(got["out"], outs[-1])
 
 
+# Route-list lengths that put thin tiles of exactly 1, 15, 16 and 17 rows
+# next to full 32-row tiles: the 3-bit gate/up kernel takes tiles of at most
+# 16 rows through its pair-slot path and longer ones through the per-weight
+# decode, so both sides of that boundary are compared with the oracle.
+THIN_COUNTS = [16, 17, 1, 15, 32, 48, 49, 31]
+
+
+@pytest.mark.parametrize("wfmt", ["q3", "bf16"])
+def test_thin_tile_boundaries(wfmt):
+    E, k = len(THIN_COUNTS), 1
+    T = sum(THIN_COUNTS)
+    shape = LayerShape(f"thin_edges_{wfmt}", T, 256, 256, E, k, "normal", wfmt)
+    _, x = routing_inputs(shape, 0)
+    rng = np.random.default_rng([7, T])
+    owner = np.repeat(np.arange(E), THIN_COUNTS)
+    rng.shuffle(owner)
+    logits = (0.1 * rng.standard_normal((T, E))).astype(np.float32)
+    logits[np.arange(T), owner] += np.float32(5.0)          # each token's one expert, by a wide margin
+    W = layer_weights(shape, 0)
+    ref = oracle.moe_layer(logits, x, host_raw(W), k)
+    assert np.array_equal(np.bincount(ref["ids"].ravel(), minlength=E), THIN_COUNTS)
+    bufs = moe.MoELayerBuffers(T, E, k, shape.H, shape.I, wfmt_id(shape))
+    say(f"[thin edges] {wfmt} T={T} counts={THIN_COUNTS}")
+    got = run_layer(bufs, logits, x, to_dev_weights(W), fat_threshold=10**6)
+    check_indices(got, ref)
+    ey = oracle.rel_max_err(got["Y"], ref["Y"])
+    eo = oracle.rel_max_err(got["out"], ref["out"])
+    say(f"   Y err {ey:.3e}  out err {eo:.3e}")
+    assert ey <= tol(shape) and eo <= tol(shape)
+
+
 def _tie_logits(T, E, seed):
     rng = np.random.default_rng(seed)
     lg = (np.round(rng.standard_normal((T, E)) * 2) / 2).astype(np.float32)
