@@ -217,7 +217,12 @@ moe_status moe_ffn_plan(const int32_t* expert_offsets, int T, int E, int k, int 
  * stored fp16 in the workspace (row i of a belongs to sorted row i).
  * fat_threshold must equal the value given to moe_ffn_plan; with
  * T < fat_threshold no route list can be fat, so the MFMA-tile kernel is not
- * launched at all. */
+ * launched at all.  The MFMA-tile kernel hands out its last batches through
+ * a counter in the workspace: moe_ffn_plan zeroes it and each launch leaves
+ * it zeroed, so gate_up may run any number of times on one plan, in stream
+ * order (two launches on one workspace must not overlap).  The 3-bit format
+ * also writes the reordered activation rows of the short lists into the
+ * workspace before its streaming kernel. */
 moe_status moe_ffn_gate_up(const uint16_t* x, int wfmt, const void* w_gate, const void* w_up,
                            const uint16_t* s_gate, const uint16_t* s_up, const int32_t* sorted_pair,
                            int T, int E, int k, int H, int I, int fat_threshold, void* workspace,
