@@ -115,7 +115,11 @@ moe_status moe_route_topk(const float* logits, int T, int E, int k,
  * on MFMA), then for every token exactly the selection, gate weights and
  * histogram of moe_route_topk applied to these fp32 logits.  The logits stay
  * on chip unless `logits` is non-NULL, in which case they are also written
- * there (fp32 [T, E], row-major).  Reading of the pages (routing over the
+ * there (fp32 [T, E], row-major).  With `logits` non-NULL and T <= 32 the
+ * GEMM is spread over E / 32 blocks that write the logits, and the gate then
+ * runs on them; every logit goes through the same MFMA accumulation chain as
+ * on chip, so ids, weights and histogram are bit-identical to the call
+ * without `logits`.  Reading of the pages (routing over the
  * layer's routed experts: dsv41-flash-offload wiki, opening paragraph; the
  * router itself is not written there): a bias-free linear router over the
  * hidden state, the expert's rows stored [E, H] like the expert matrices.

@@ -301,10 +301,153 @@ void router_topk_kernel(const uint16_t* __restrict__ x, const uint16_t* __restri
         if (hist[e]) atomicAdd(&counts[e], hist[e]);
 }
 
+// Router logits for a few tokens (T <= 32), split over the experts: block j
+// computes logits[t, 32 j .. 32 j + 31] for every token and writes them out.
+// The fused kernel has one block stream the whole router matrix; here E / 32
+// blocks each stream their 32 rows.  Every logit goes through exactly the MFMA
+// chain of router_topk_kernel (bf16 32x32x16, acc starting at zero, the 16-k
+// steps of the reduction in ascending order, lane half g holding k 8 g .. 8 g
+// + 7 of a step), so both kernels produce the same logits bit for bit, and
+// the gate applied to them afterwards makes the same choice.
+//
+// The four waves fill a two-slot LDS ring of 512-k batches by direct-to-LDS
+// loads (one 1 KB row per instruction: rows 0..31 the block's router rows,
+// rows 32..63 the tokens, zeros past T read from past the buffer end); wave 0
+// runs the MFMAs of one batch while the next one lands.  Position p of a row
+// holds its 16-byte chunk p ^ (r & 15), so each 16-lane fragment read covers
+// 16 distinct bank groups.
+constexpr int RS_BK = 512;                           // k per batch
+constexpr uint32_t RS_ROW = RS_BK * 2;               // bytes of one row per batch
+constexpr uint32_t RS_SLOT = 64 * RS_ROW;            // 32 router rows + 32 token rows
+constexpr uint32_t RS_LDS = 2 * RS_SLOT;
+constexpr int RS_TMAX = 32;
+
+// wait until at most N of this wave's LDS reads are outstanding, the four
+// operand registers of one two-step group tied to the wait
+template <int N>
+__device__ __forceinline__ void lds_wait_group(u32x4 (&a)[2], u32x4 (&w)[2]) {
+    asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(a[0]), "+v"(a[1]), "+v"(w[0]), "+v"(w[1]) : "n"(N) : "memory");
+}
+
+__global__ __launch_bounds__(R_THREADS, 1)
+void router_logits_split_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr, int T, int E,
+                                int H, float* __restrict__ logits) {
+    extern __shared__ u32x4 smem[];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n = lane & 31, g = lane >> 5;
+    const int e0 = blockIdx.x * 32;
+    const int NB = (H + RS_BK - 1) / RS_BK;
+    const uint32_t xbytes = (uint32_t)((size_t)T * H * 2);
+    const __amdgpu_buffer_rsrc_t src = wave < 2 ? make_rsrc(wr, (uint32_t)((size_t)E * H * 2)) : make_rsrc(x, xbytes);
+    // load instruction i of wave w fills row r = 16 w + i of a slot
+    uint32_t voff[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int r = 16 * wave + i;
+        const uint32_t ch = (uint32_t)((lane ^ (r & 15)) * 16);
+        if (r < 32) voff[i] = (uint32_t)(e0 + r) * (uint32_t)H * 2u + ch;
+        else voff[i] = r - 32 < T ? (uint32_t)(r - 32) * (uint32_t)H * 2u + ch : xbytes;
+    }
+    auto issue = [&](int b, int slot) {
+        char* st = reinterpret_cast<char*>(smem) + slot * RS_SLOT;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) dma16(src, st + (16 * wave + i) * RS_ROW, voff[i], (uint32_t)b * RS_ROW);
+    };
+
+    f32x16 acc = f32x16{};
+    issue(0, 0);
+    if (NB > 1) issue(1, 1);
+    for (int b = 0; b < NB; ++b) {
+        const int slot = b & 1;
+        if (b + 1 < NB) vm_wait<16>();                      // batch b landed (this wave's rows) ...
+        else vm_wait<0>();
+        __syncthreads();                                    // ... and every wave's
+        if (wave == 0) {
+            const uint32_t st = lds_addr(smem) + slot * RS_SLOT;
+            const uint32_t wb = st + (uint32_t)n * RS_ROW, xb = st + (uint32_t)(32 + n) * RS_ROW;
+            const uint32_t sw = (uint32_t)(n & 15);
+            const int nq = min(RS_BK, H - b * RS_BK) / 32;  // groups of two 16-k steps (H % 32 == 0)
+            auto rd = [&](int q, u32x4 (&a)[2], u32x4 (&w)[2]) {
+#pragma unroll
+                for (int s = 0; s < 2; ++s) {
+                    const uint32_t off = ((uint32_t)(4 * q + 2 * s + g) ^ sw) * 16u;
+                    a[s] = ds_read16<0>(xb + off);
+                    w[s] = ds_read16<0>(wb + off);
+                }
+            };
+            auto mfma2 = [&](const u32x4 (&a)[2], const u32x4 (&w)[2]) {
+                acc = mfma_bf16(a[0], w[0], acc);
+                acc = mfma_bf16(a[1], w[1], acc);
+            };
+            if (nq == RS_BK / 32) {
+                // a full batch, unrolled: the next group's reads are in flight
+                // during this group's MFMAs (no register set carried round a
+                // loop, which would let the compiler copy a read's destination
+                // before its wait)
+                u32x4 a0[2], w0[2], a1[2], w1[2];
+                rd(0, a0, w0);
+                static_for<RS_BK / 64>([&](auto h_c) {
+                    constexpr int Q = 2 * decltype(h_c)::value;
+                    rd(Q + 1, a1, w1);
+                    lds_wait_group<4>(a0, w0);
+                    mfma2(a0, w0);
+                    if constexpr (Q + 2 < RS_BK / 32) {
+                        rd(Q + 2, a0, w0);
+                        lds_wait_group<4>(a1, w1);
+                    } else {
+                        lds_wait_group<0>(a1, w1);
+                    }
+                    mfma2(a1, w1);
+                });
+            } else {
+                for (int q = 0; q < nq; ++q) {                // the last, partial batch
+                    u32x4 a[2], w[2];
+                    rd(q, a, w);
+                    lds_wait_group<0>(a, w);
+                    mfma2(a, w);
+                }
+            }
+        }
+        __syncthreads();                                    // slot free
+        if (b + 2 < NB) issue(b + 2, slot);
+    }
+    // lane holds expert e0 + n, tokens 8 (i >> 2) + 4 g + (i & 3)
+    if (wave == 0) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int m = 8 * (i >> 2) + 4 * g + (i & 3);
+            if (m < T) logits[(size_t)m * E + e0 + n] = acc[i];
+        }
+    }
+}
+
 // the router kernels use more dynamic LDS than the default cap: raised once
 // per device (and kernel) before its first launch there
 std::mutex g_router_mu;
 bool g_router_lds_set[64][4] = {};
+bool g_split_lds_set[64] = {};
+
+hipError_t router_split_launch(const uint16_t* x, const uint16_t* wr, int T, int E, int H, int k, int32_t* ids,
+                               float* w, int32_t* counts, float* logits, hipStream_t s) {
+    int dev = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess) return err;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    {
+        std::lock_guard<std::mutex> lock(g_router_mu);
+        if (!g_split_lds_set[dev]) {
+            err = hipFuncSetAttribute((const void*)router_logits_split_kernel,
+                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)RS_LDS);
+            if (err != hipSuccess) return err;
+            g_split_lds_set[dev] = true;
+        }
+    }
+    router_logits_split_kernel<<<E / 32, R_THREADS, RS_LDS, s>>>(x, wr, T, E, H, logits);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    return launch_route_topk(logits, T, E, k, ids, w, counts, s);
+}
 
 template <int CT>
 hipError_t router_launch(const uint16_t* x, const uint16_t* wr, int T, int H, int k, int32_t* ids, float* w,
@@ -338,6 +481,9 @@ bool router_shape_ok(int T, int E, int H) {
 
 hipError_t launch_router_topk(const uint16_t* x, const uint16_t* w_router, int T, int E, int H, int k,
                               int32_t* topk_ids, float* topk_w, int32_t* counts, float* logits, hipStream_t s) {
+    // a few tokens with the logits wanted in memory: the GEMM over E / 32
+    // blocks, then the gate on the stored logits (the same logits and choice)
+    if (logits && T <= RS_TMAX) return router_split_launch(x, w_router, T, E, H, k, topk_ids, topk_w, counts, logits, s);
     switch (E / 128) {
         case 1: return router_launch<1>(x, w_router, T, H, k, topk_ids, topk_w, counts, logits, s);
         case 2: return router_launch<2>(x, w_router, T, H, k, topk_ids, topk_w, counts, logits, s);

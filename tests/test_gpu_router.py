@@ -7,7 +7,8 @@
   kernel's own fp32 logits -- the selection is decided in the kernel's
   precision on both sides, so indices must match bit for bit;
 * the fused call (no logits output) gives bit-identical ids, weights and
-  histogram;
+  histogram -- for a few tokens the call with logits runs the GEMM split over
+  the experts, so this also checks that both kernels compute the same logits;
 * every selected expert is a valid top-k choice for the float64 logits up to
   twice that bound (the sets can differ only between near-equal logits).
 """
@@ -22,9 +23,11 @@ from tests.gpu_util import TOL_W, say
 
 pytestmark = pytest.mark.gpu
 
-# (T, E, H, k): ragged token blocks, every supported expert count, decode and the 16k chunk
+# (T, E, H, k): ragged token blocks, every supported expert count, decode and the 16k chunk.  With the logits
+# asked for, T <= 32 splits the GEMM over the experts (512-k batches): T = 32 and 33 sit on either side of that
+# switch, H = 1056 and 4128 end in a partial batch.
 CASES = [(64, 128, 256, 2), (333, 256, 512, 4), (700, 384, 1024, 8), (1, 384, 4096, 8), (4, 512, 4096, 8),
-         (16384, 384, 4096, 8)]
+         (32, 256, 1056, 4), (17, 128, 4128, 8), (33, 128, 512, 2), (16384, 384, 4096, 8)]
 
 
 def _x(T, H, seed):

@@ -99,8 +99,9 @@ def test_checker_accepts_clean_code():
 
 
 def test_no_lds_result_used_before_its_wait(ffn_asm):
-    kernels = {k: v for k, v in kernel_bodies(ffn_asm).items() if "ffn_" in k or "router_topk_kernel" in k}
+    kernels = {k: v for k, v in kernel_bodies(ffn_asm).items() if "ffn_" in k or "router_" in k}
     assert any("ffn_fat_kernel" in k for k in kernels) and any("router_topk_kernel" in k for k in kernels)
+    assert any("router_logits_split_kernel" in k for k in kernels)
     bad = {}
     for name, lines in kernels.items():
         r = stale_lds_uses(lines)
