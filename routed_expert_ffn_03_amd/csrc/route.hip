@@ -335,17 +335,25 @@ void router_topk_kernel(const uint16_t* __restrict__ x, const uint16_t* __restri
 // + 7 of a step), so both kernels produce the same logits bit for bit, and
 // the gate applied to them afterwards makes the same choice.
 //
-// The four waves fill a two-slot LDS ring of 512-k batches by direct-to-LDS
-// loads (one 1 KB row per instruction: rows 0..31 the block's router rows,
-// rows 32..63 the tokens, zeros past T read from past the buffer end); wave 0
-// runs the MFMAs of one batch while the next one lands.  Position p of a row
-// holds its 16-byte chunk p ^ (r & 15), so each 16-lane fragment read covers
-// 16 distinct bank groups.
+// The four waves fill an LDS ring of 512-k batches by direct-to-LDS loads
+// (one 1 KB row per instruction: rows 0..31 the block's router rows, then XR
+// token rows, zeros past T read from past the buffer end); wave 0 runs the
+// MFMAs of one batch while the later ones land.  XR = 16 token rows (T <= 16)
+// leave room for three slots, so 96 KB of router rows are in flight per CU
+// instead of 64 KB; A-operand lanes past XR repeat a row (their results are
+// never stored).  Position p of a row holds its 16-byte chunk p ^ (r & 15),
+// so each 16-lane fragment read covers 16 distinct bank groups.
 constexpr int RS_BK = 512;                           // k per batch
 constexpr uint32_t RS_ROW = RS_BK * 2;               // bytes of one row per batch
-constexpr uint32_t RS_SLOT = 64 * RS_ROW;            // 32 router rows + 32 token rows
-constexpr uint32_t RS_LDS = 2 * RS_SLOT;
 constexpr int RS_TMAX = 32;
+template <int XR>
+struct SplitRing {
+    static constexpr int ROWS = 32 + XR;             // router rows + token rows per slot
+    static constexpr int LPW = ROWS / 4;             // load instructions per wave per batch
+    static constexpr int NSL = XR == 16 ? 3 : 2;     // slots
+    static constexpr uint32_t SLOT = ROWS * RS_ROW;
+    static constexpr uint32_t LDS = NSL * SLOT;
+};
 
 // wait until at most N of this wave's LDS reads are outstanding, the four
 // operand registers of one two-step group tied to the wait
@@ -354,9 +362,11 @@ __device__ __forceinline__ void lds_wait_group(u32x4 (&a)[2], u32x4 (&w)[2]) {
     asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(a[0]), "+v"(a[1]), "+v"(w[0]), "+v"(w[1]) : "n"(N) : "memory");
 }
 
+template <int XR>
 __global__ __launch_bounds__(R_THREADS, 1)
 void router_logits_split_kernel(const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr, int T, int E,
                                 int H, float* __restrict__ logits) {
+    using R = SplitRing<XR>;
     extern __shared__ u32x4 smem[];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -364,33 +374,39 @@ void router_logits_split_kernel(const uint16_t* __restrict__ x, const uint16_t* 
     const int e0 = blockIdx.x * 32;
     const int NB = (H + RS_BK - 1) / RS_BK;
     const uint32_t xbytes = (uint32_t)((size_t)T * H * 2);
-    const __amdgpu_buffer_rsrc_t src = wave < 2 ? make_rsrc(wr, (uint32_t)((size_t)E * H * 2)) : make_rsrc(x, xbytes);
-    // load instruction i of wave w fills row r = 16 w + i of a slot
-    uint32_t voff[16];
+    const __amdgpu_buffer_rsrc_t wsrc = make_rsrc(wr, (uint32_t)((size_t)E * H * 2));
+    const __amdgpu_buffer_rsrc_t xsrc = make_rsrc(x, xbytes);
+    // load instruction i of wave w fills row r = LPW w + i of a slot
+    uint32_t voff[R::LPW];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const int r = 16 * wave + i;
+    for (int i = 0; i < R::LPW; ++i) {
+        const int r = R::LPW * wave + i;
         const uint32_t ch = (uint32_t)((lane ^ (r & 15)) * 16);
         if (r < 32) voff[i] = (uint32_t)(e0 + r) * (uint32_t)H * 2u + ch;
         else voff[i] = r - 32 < T ? (uint32_t)(r - 32) * (uint32_t)H * 2u + ch : xbytes;
     }
     auto issue = [&](int b, int slot) {
-        char* st = reinterpret_cast<char*>(smem) + slot * RS_SLOT;
+        char* st = reinterpret_cast<char*>(smem) + slot * R::SLOT;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) dma16(src, st + (16 * wave + i) * RS_ROW, voff[i], (uint32_t)b * RS_ROW);
+        for (int i = 0; i < R::LPW; ++i) {
+            const int r = R::LPW * wave + i;                // wave-uniform: the resource stays scalar
+            dma16(r < 32 ? wsrc : xsrc, st + r * RS_ROW, voff[i], (uint32_t)b * RS_ROW);
+        }
     };
 
     f32x16 acc = f32x16{};
-    issue(0, 0);
-    if (NB > 1) issue(1, 1);
+    for (int b = 0; b < min(R::NSL, NB); ++b) issue(b, b);
+    int slot = 0;
     for (int b = 0; b < NB; ++b) {
-        const int slot = b & 1;
-        if (b + 1 < NB) vm_wait<16>();                      // batch b landed (this wave's rows) ...
-        else vm_wait<0>();
+        switch (min(R::NSL - 1, NB - 1 - b)) {              // batch b landed (this wave's rows) ...
+            case 0: vm_wait<0>(); break;
+            case 1: vm_wait<R::LPW>(); break;
+            default: vm_wait<2 * R::LPW>(); break;
+        }
         __syncthreads();                                    // ... and every wave's
         if (wave == 0) {
-            const uint32_t st = lds_addr(smem) + slot * RS_SLOT;
-            const uint32_t wb = st + (uint32_t)n * RS_ROW, xb = st + (uint32_t)(32 + n) * RS_ROW;
+            const uint32_t st = lds_addr(smem) + slot * R::SLOT;
+            const uint32_t wb = st + (uint32_t)n * RS_ROW, xb = st + (uint32_t)(32 + (n & (XR - 1))) * RS_ROW;
             const uint32_t sw = (uint32_t)(n & 15);
             const int nq = min(RS_BK, H - b * RS_BK) / 32;  // groups of two 16-k steps (H % 32 == 0)
             auto rd = [&](int q, u32x4 (&a)[2], u32x4 (&w)[2]) {
@@ -435,7 +451,8 @@ void router_logits_split_kernel(const uint16_t* __restrict__ x, const uint16_t* 
             }
         }
         __syncthreads();                                    // slot free
-        if (b + 2 < NB) issue(b + 2, slot);
+        if (b + R::NSL < NB) issue(b + R::NSL, slot);
+        slot = slot + 1 == R::NSL ? 0 : slot + 1;
     }
     // lane holds expert e0 + n, tokens 8 (i >> 2) + 4 g + (i & 3)
     if (wave == 0) {
@@ -451,24 +468,26 @@ void router_logits_split_kernel(const uint16_t* __restrict__ x, const uint16_t* 
 // per device (and kernel) before its first launch there
 std::mutex g_router_mu;
 bool g_router_lds_set[64][4] = {};
-bool g_split_lds_set[64] = {};
+bool g_split_lds_set[64][2] = {};
 
+template <int XR>
 hipError_t router_split_launch(const uint16_t* x, const uint16_t* wr, int T, int E, int H, int k, int32_t* ids,
                                float* w, int32_t* counts, float* logits, hipStream_t s) {
+    using R = SplitRing<XR>;
     int dev = 0;
     hipError_t err = hipGetDevice(&dev);
     if (err != hipSuccess) return err;
     if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
     {
         std::lock_guard<std::mutex> lock(g_router_mu);
-        if (!g_split_lds_set[dev]) {
-            err = hipFuncSetAttribute((const void*)router_logits_split_kernel,
-                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)RS_LDS);
+        if (!g_split_lds_set[dev][XR / 16 - 1]) {
+            err = hipFuncSetAttribute((const void*)router_logits_split_kernel<XR>,
+                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)R::LDS);
             if (err != hipSuccess) return err;
-            g_split_lds_set[dev] = true;
+            g_split_lds_set[dev][XR / 16 - 1] = true;
         }
     }
-    router_logits_split_kernel<<<E / 32, R_THREADS, RS_LDS, s>>>(x, wr, T, E, H, logits);
+    router_logits_split_kernel<XR><<<E / 32, R_THREADS, R::LDS, s>>>(x, wr, T, E, H, logits);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
     return launch_route_topk(logits, T, E, k, ids, w, counts, s);
@@ -508,7 +527,9 @@ hipError_t launch_router_topk(const uint16_t* x, const uint16_t* w_router, int T
                               int32_t* topk_ids, float* topk_w, int32_t* counts, float* logits, hipStream_t s) {
     // a few tokens with the logits wanted in memory: the GEMM over E / 32
     // blocks, then the gate on the stored logits (the same logits and choice)
-    if (logits && T <= RS_TMAX) return router_split_launch(x, w_router, T, E, H, k, topk_ids, topk_w, counts, logits, s);
+    if (logits && T <= 16) return router_split_launch<16>(x, w_router, T, E, H, k, topk_ids, topk_w, counts, logits, s);
+    if (logits && T <= RS_TMAX)
+        return router_split_launch<32>(x, w_router, T, E, H, k, topk_ids, topk_w, counts, logits, s);
     switch (E / 128) {
         case 1: return router_launch<1>(x, w_router, T, H, k, topk_ids, topk_w, counts, logits, s);
         case 2: return router_launch<2>(x, w_router, T, H, k, topk_ids, topk_w, counts, logits, s);
