@@ -353,6 +353,8 @@ struct SplitRing {
     static constexpr int NSL = XR == 16 ? 3 : 2;     // slots
     static constexpr uint32_t SLOT = ROWS * RS_ROW;
     static constexpr uint32_t LDS = NSL * SLOT;
+    static_assert(LDS <= 160 * 1024, "the ring exceeds the LDS");
+    static_assert(NSL * LPW <= 63 && NSL <= 3, "loads in flight beyond the wait counter or the wait table");
 };
 
 // wait until at most N of this wave's LDS reads are outstanding, the four
