@@ -546,6 +546,7 @@ hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* 
     if (nv <= 1) route_launch<1>(logits, T, E, k, topk_ids, topk_w, counts, s);
     else if (nv <= 2) route_launch<2>(logits, T, E, k, topk_ids, topk_w, counts, s);
     else if (nv <= 4) route_launch<4>(logits, T, E, k, topk_ids, topk_w, counts, s);
+    else if (nv <= 6) route_launch<6>(logits, T, E, k, topk_ids, topk_w, counts, s);    // E = 384
     else if (nv <= 8) route_launch<8>(logits, T, E, k, topk_ids, topk_w, counts, s);
     else route_launch<16>(logits, T, E, k, topk_ids, topk_w, counts, s);
     return hipGetLastError();
