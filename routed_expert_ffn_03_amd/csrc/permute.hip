@@ -42,20 +42,34 @@ void permute_hist_kernel(const int32_t* __restrict__ ids, int T, int E, int k,
 __global__ __launch_bounds__(1024)
 void permute_scan_kernel(int32_t* __restrict__ block_hist, int nblocks, int E, int P,
                          int32_t* __restrict__ offsets) {
+    // each thread walks its expert's column of block counts in chunks of CH
+    // loads issued together (a plain loop waits for every load in turn)
+    constexpr int CH = 16;
     __shared__ int scratch[16];
     const int e = threadIdx.x;
     int total = 0;
     if (e < E)
-        for (int b = 0; b < nblocks; ++b) total += block_hist[(size_t)b * E + e];
+        for (int b0 = 0; b0 < nblocks; b0 += CH) {
+            int v[CH];
+#pragma unroll
+            for (int i = 0; i < CH; ++i) v[i] = b0 + i < nblocks ? block_hist[(size_t)(b0 + i) * E + e] : 0;
+#pragma unroll
+            for (int i = 0; i < CH; ++i) total += v[i];
+        }
     const int incl = block_inclusive_scan(total, scratch);
     if (e < E) {
         int base = incl - total;
         offsets[e] = base;
-        for (int b = 0; b < nblocks; ++b) {
-            const size_t i = (size_t)b * E + e;
-            const int c = block_hist[i];
-            block_hist[i] = base;
-            base += c;
+        for (int b0 = 0; b0 < nblocks; b0 += CH) {
+            int v[CH];
+#pragma unroll
+            for (int i = 0; i < CH; ++i) v[i] = b0 + i < nblocks ? block_hist[(size_t)(b0 + i) * E + e] : 0;
+#pragma unroll
+            for (int i = 0; i < CH; ++i)
+                if (b0 + i < nblocks) {
+                    block_hist[(size_t)(b0 + i) * E + e] = base;
+                    base += v[i];
+                }
         }
     }
     if (e == 0) offsets[E] = P;
