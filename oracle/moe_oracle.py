@@ -150,7 +150,13 @@ def route_topk(logits: np.ndarray, k: int):
 
 
 def expert_histogram(ids: np.ndarray, E: int) -> np.ndarray:
-    """Number of (token, slot) pairs routed to each expert."""
+    """Number of (token, slot) pairs routed to each expert, one entry per
+    expert (experts no token picked count 0).
+
+    Source: dsv41-flash-offload wiki, repository file table, entry for the
+    staged cold-expert prefill patch (per-expert route lists and their
+    counts).  Pinned by hand-worked cases in tests/golden/metric_worked.txt.
+    """
     return np.bincount(np.asarray(ids).ravel(), minlength=E).astype(np.int32)
 
 
@@ -296,7 +302,13 @@ def dense_layer(logits, x_bits, expert_raw, k: int) -> np.ndarray:
 
 
 def rel_max_err(got, ref) -> float:
-    """max |got - ref| / rms(ref) over the whole tensor (the parity metric)."""
+    """max |got - ref| / rms(ref) over the whole tensor (the parity metric).
+
+    Reading of the pages' relative-error comparison of two implementations
+    (dsv41-flash-offload wiki, paragraph on the fidelity of the busy-expert GEMM path) as a bound on the
+    largest element error; an all-zero reference falls back to max |err|.
+    Pinned by hand-worked cases in tests/golden/metric_worked.txt.
+    """
     ref = np.asarray(ref, dtype=np.float64)
     got = np.asarray(got, dtype=np.float64)
     rms = float(np.sqrt(np.mean(ref * ref)))

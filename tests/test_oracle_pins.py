@@ -293,3 +293,45 @@ def test_router_logits_closed_forms():
     # and the gate on top of it breaks the tie between experts 1 and 2 by index
     ids, _ = oracle.route_topk(oracle.router_logits(x, W).astype(np.float32), 2)
     assert ids.tolist() == [[0, 1]]
+
+
+# ------------------------------------------------- parity metric, histogram
+
+def test_rel_max_err_worked_values():
+    n = 0
+    for key, val in lines("metric_worked.txt"):
+        if key != "metric":
+            continue
+        got, ref, shp, want = [s.strip() for s in val.split("|")]
+        shape = tuple(int(v) for v in shp.split())
+        g = np.array([float(v) for v in got.split()]).reshape(shape)
+        r = np.array([float(v) for v in ref.split()]).reshape(shape)
+        assert oracle.rel_max_err(g, r) == pytest.approx(float(want), rel=1e-15, abs=0)
+        # symmetric in the sign of the error, and scale-free
+        assert oracle.rel_max_err(2 * r - g, r) == pytest.approx(float(want), rel=1e-15, abs=0)
+        if np.any(r):
+            assert oracle.rel_max_err(8 * g, 8 * r) == pytest.approx(float(want), rel=1e-15, abs=0)
+        n += 1
+    assert n >= 4
+
+
+def test_expert_histogram_worked_values():
+    n = 0
+    for key, val in lines("metric_worked.txt"):
+        if key != "hist":
+            continue
+        E, ids, k, counts = [s.strip() for s in val.split("|")]
+        a = np.array(ints(ids), dtype=np.int32).reshape(-1, int(k))
+        got = oracle.expert_histogram(a, int(E))
+        assert got.dtype == np.int32 and got.shape == (int(E),)
+        assert got.tolist() == ints(counts)
+        n += 1
+    assert n >= 3
+    # against the permutation's own counts (an independent bucket walk is in
+    # test_permute_brute_force): same totals on a random routing
+    rng = np.random.default_rng(12)
+    ids = np.stack([rng.choice(9, size=3, replace=False) for _ in range(40)]).astype(np.int32)
+    buckets = [0] * 12
+    for e in ids.ravel():
+        buckets[int(e)] += 1
+    assert oracle.expert_histogram(ids, 12).tolist() == buckets
