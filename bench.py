@@ -6,8 +6,12 @@ One step = one full layer call (route -> permute -> plan -> gate/up -> down
 The headline workload is the 16,384-token prefill chunk (bf16 experts,
 Zipf-skewed router); the 4-token decode step is measured in the same run on
 the same weights and reported under "decode" (with --workload prefill16k_q3:
-the decode step on the same 3-bit weights).  The dominant kernel's time
-(the gate/up phase) is taken live with HIP events on the library's stream.
+the decode step on the same 3-bit weights).  Every timed step sits between
+its own pair of HIP events on the library's stream, and a 512 MiB scratch
+buffer is read between steps (outside the events) so that no step starts
+with the previous one's weights in the MALL; the line reports the
+mean (value, ms_per_step) and the median, p10 and p90.  The dominant
+kernel's time (the gate/up phase) is taken live the same way.
 
 Prints ONE JSON line.  Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -26,6 +30,8 @@ if ROOT not in sys.path:
 METRIC = "MoE-layer tokens/s at 16k-token prefill and 4-token decode; % MFMA/HBM peak"
 PEAK_MFMA_TFLOPS = {"bf16": 2500.0, "fp16": 2500.0}      # dense, MI355X published
 PEAK_HBM_GBS = 8000.0
+FLUSH_BYTES = 512 << 20                                   # > the 256 MB MALL
+FAT_GATE_UP_NAME = "ffn_fat_kernel<1, 0, 5>"
 
 
 def ffn_source_hash() -> str:
@@ -59,14 +65,16 @@ def log(*a):
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--steps", type=int, default=30)
+    p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="prefill16k",
                    choices=["prefill16k", "decode", "prefill1k", "prefill16k_q3", "decode_q3"])
     p.add_argument("--decode-steps", type=int, default=200, help="steps of the secondary decode measurement")
     p.add_argument("--no-decode", action="store_true", help="skip the secondary decode measurement")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-sample", type=int, default=128, help="tokens of the batch the oracle is timed on")
+    p.add_argument("--cpu-sample", type=int, default=1024, help="tokens of the batch the oracle is timed on")
+    p.add_argument("--no-flush", action="store_true",
+                   help="do not read the 512 MiB scratch buffer between timed steps")
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--fat-threshold", type=int, default=32)
     p.add_argument("--copy-calibration", action="store_true",
@@ -92,6 +100,31 @@ def workload_desc(shape, thr):
         "tokens": shape.T, "hidden": shape.H, "inter": shape.I, "experts": shape.E, "top_k": shape.k,
         "router": router, "expert_weights": shape.wfmt, "fat_threshold": thr,
     }
+
+
+class StepTimes:
+    """Per-step layer and gate/up-phase times (ms) of one timed run."""
+
+    def __init__(self, layer_ms, gate_up_ms, wall_ms):
+        import numpy as np
+        self.layer = np.asarray(layer_ms)
+        self.gate_up = np.asarray(gate_up_ms)
+        self.wall_ms = wall_ms                        # host clock per step, flush included
+
+    @property
+    def mean(self):
+        return float(self.layer.mean())
+
+    @property
+    def gate_up_mean(self):
+        return float(self.gate_up.mean())
+
+    def stats(self):
+        import numpy as np
+        q = lambda a, p: float(np.percentile(a, p))
+        return {"mean_ms": self.mean, "median_ms": q(self.layer, 50), "p10_ms": q(self.layer, 10),
+                "p90_ms": q(self.layer, 90), "gate_up_median_ms": q(self.gate_up, 50),
+                "wall_ms_per_step_incl_flush": self.wall_ms, "reps": int(self.layer.size)}
 
 
 class Runner:
@@ -126,19 +159,31 @@ class Runner:
                        fat_threshold=self.thr, wfmt=self.wfmt)
         m.moe_combine(b.y_sorted, b.topk_w, b.pair_to_sorted, b.out)
 
-    def measure(self, steps, warmup):
+    def measure(self, steps, warmup, flush=None):
+        """Time `steps` layer calls, each between its own pair of HIP events on
+        the library's stream.  With `flush` (a 512 MiB device buffer) the buffer
+        is read in full before every step, outside the events, so no step finds
+        the previous one's weights in the 256 MB MALL or the L2s.  A read leaves
+        only clean lines behind (a write would leave dirty ones that the timed
+        step would then have to write back)."""
         torch = self.torch
         for _ in range(warmup):
             self.step()
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        ev = lambda: torch.cuda.Event(enable_timing=True)
+        layer = [(ev(), ev()) for _ in range(steps)]
+        gu = [(ev(), ev()) for _ in range(steps)]
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in range(steps):
-            self.step(evs[i])
+            if flush is not None:
+                flush.sum()
+            layer[i][0].record()
+            self.step(gu[i])
+            layer[i][1].record()
         torch.cuda.synchronize()
         t1 = time.perf_counter()
-        gate_up_ms = sum(a.elapsed_time(b) for a, b in evs) / steps
-        return (t1 - t0) * 1e3 / steps, gate_up_ms
+        return StepTimes([a.elapsed_time(b) for a, b in layer], [a.elapsed_time(b) for a, b in gu],
+                         (t1 - t0) * 1e3 / steps)
 
     def roofline(self, gate_up_ms):
         import numpy as np
@@ -165,8 +210,10 @@ class Runner:
             per = f"{per_expert} gate+up weight bytes per touched expert x {touched} experts"
         r["frac"] = r["achieved"] / r["peak"]
         r["traffic"] = measured_traffic(s.name)
+        r["traffic_source"] = ("rocprofv3 FETCH_SIZE + WRITE_SIZE of this kernel source, profiles/hbm_traffic.md"
+                               if r["traffic"] is not None else "not measured for this kernel source")
         # fat kernel template arguments: <phase, weight format, LDS ring stages>
-        fat_name = "ffn_fat_kernel<1, 0, 5>" if s.wfmt == "bf16" else "ffn_fat_kernel<1, 1, 6>"
+        fat_name = FAT_GATE_UP_NAME if s.wfmt == "bf16" else "ffn_fat_kernel<1, 1, 6>"
         thin_name = "ffn_thin_kernel<1, 4>" if s.wfmt == "bf16" else "ffn_thin_q3_kernel<1>"
         r["kernel"] = f"gate/up phase ({fat_name} + {thin_name})"
         r["kernel_ms"] = gate_up_ms
@@ -175,11 +222,23 @@ class Runner:
         r["experts_fat"] = fat
         return r
 
+    def layer_hbm(self, layer_ms):
+        """Whole-layer weight streaming rate: every touched expert's gate, up and
+        down bytes over the layer step time (the decode bound)."""
+        s = self.shape
+        counts = self.b.expert_counts.cpu().numpy()
+        touched = int((counts > 0).sum())
+        per_expert = (3 * s.I * s.H * 2 if s.wfmt == "bf16"
+                      else 2 * s.I * (s.H // 128) * (13 * 4 + 2) + s.H * (s.I // 128) * (13 * 4 + 2))
+        gbs = touched * per_expert / (layer_ms * 1e-3) / 1e9
+        return {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
+                "algorithmic": f"{per_expert} gate+up+down weight bytes per touched expert x {touched} experts "
+                               f"over the whole layer step"}
 
-def cpu_baseline(shape, seed, n_tokens):
-    """The float64 oracle as it is, on the first n_tokens tokens of the same batch, 1 BLAS thread."""
+
+def _time_oracle(shape, seed, n_tokens, threads):
     import numpy as np
-    from threadpoolctl import threadpool_limits
+    from threadpoolctl import threadpool_info, threadpool_limits
 
     import oracle
     from moe_inputs import for_each_expert, routing_inputs
@@ -190,14 +249,33 @@ def cpu_baseline(shape, seed, n_tokens):
     need = sorted({int(e) for e in ids.ravel()})
     raw = {}
     for_each_expert(shape, seed, lambda e, a: raw.__setitem__(e, a), experts=need)
-    with threadpool_limits(limits=1):
+    with threadpool_limits(limits=threads):
+        blas = sorted({(i["internal_api"], i["num_threads"]) for i in threadpool_info()})
         t0 = time.perf_counter()
         oracle.moe_layer(logits, x, lambda e: raw[e], shape.k)
         dt = time.perf_counter() - t0
-    return {"value": n_tokens / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"first {n_tokens} tokens of the {shape.name} batch (seed {seed}): route, permute, "
-                      f"{len(need)} experts' SwiGLU FFN and combine in float64 numpy, 1 thread; "
-                      f"{dt:.1f} s"}
+    return n_tokens / dt, dt, len(need), blas
+
+
+def cpu_baseline(shape, seed, n_tokens):
+    """The float64 oracle as it is (numpy, BLAS per expert), timed on the host
+    cores available to this process: the first n_tokens tokens of the headline
+    batch with every core, plus 1-thread figures for the tiny layer and the
+    4-token decode step.  Expert generation is excluded."""
+    from moe_inputs import SHAPES
+
+    cores = len(os.sched_getaffinity(0))
+    v, dt, ne, blas = _time_oracle(shape, seed, n_tokens, cores)
+    res = {"value": v, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+           "sample": f"first {n_tokens} tokens of the {shape.name} batch (seed {seed}): route, permute, {ne} experts' "
+                     f"SwiGLU FFN and combine in float64 numpy, {cores} host threads (BLAS {blas}); {dt:.1f} s"}
+    single = {}
+    for name in ("tiny", "decode" if shape.wfmt == "bf16" else "decode_q3"):
+        s1 = SHAPES[name]
+        v1, dt1, ne1, _ = _time_oracle(s1, seed, s1.T, 1)
+        single[name] = {"value": v1, "unit": "tokens/s", "cores": 1, "seconds": dt1, "experts": ne1}
+    res["single_thread"] = single
+    return res
 
 
 def chunk_sweep(sizes, seed, thr):
@@ -214,7 +292,8 @@ def chunk_sweep(sizes, seed, thr):
         shape = LayerShape(f"chunk{T}", T, base.H, base.I, base.E, base.k, base.router, base.wfmt)
         run = Runner(shape, seed, dev_w, thr)
         steps = max(3, min(50, int(2e5 / T)))
-        ms, gu = run.measure(steps, 2)
+        st = run.measure(steps, 2)
+        ms, gu = st.mean, st.gate_up_mean
         roof = run.roofline(gu)
         line = {"mode": "chunk_sweep", "tokens": T, "ms_per_step": ms, "tokens_per_s": T / (ms * 1e-3),
                 "gate_up_ms": gu, "gate_up_roofline": roof, "steps": steps, "config": workload_desc(shape, thr)}
@@ -423,28 +502,39 @@ def main():
     dev_w = upload_weights(shape, args.seed)
     log(f"[bench] weights for {shape.name} generated and uploaded in {time.perf_counter() - t0:.1f} s")
 
+    flush = None if args.no_flush else torch.ones(FLUSH_BYTES // 8, dtype=torch.int64, device="cuda")
     run = Runner(shape, args.seed, dev_w, args.fat_threshold)
-    ms, gu_ms = run.measure(args.steps, args.warmup)
+    st = run.measure(args.steps, args.warmup, flush)
+    ms, gu_ms = st.mean, st.gate_up_mean
     roof = run.roofline(gu_ms)
-    log(f"[bench] {shape.name}: {ms:.3f} ms/step, gate/up {gu_ms:.3f} ms, "
+    log(f"[bench] {shape.name}: {ms:.3f} ms/step (median {st.stats()['median_ms']:.3f}, p10 "
+        f"{st.stats()['p10_ms']:.3f}, p90 {st.stats()['p90_ms']:.3f}), gate/up {gu_ms:.3f} ms, "
         f"{roof['achieved']:.1f} {roof['unit']} ({100 * roof['frac']:.1f}% of peak)")
     res = {
         "metric": METRIC, "value": shape.T / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": shape.wfmt, "data": "synthetic",
         "config": workload_desc(shape, args.fat_threshold), "roofline": roof,
+        "timing": {**st.stats(), "mall_flush_bytes": 0 if flush is None else FLUSH_BYTES,
+                   "method": "HIP events around each layer call on the library's stream; a 512 MiB scratch buffer "
+                             "is read between steps outside the events"},
     }
+    if shape.T <= 64:
+        res["layer_roofline"] = run.layer_hbm(ms)
     if not args.no_decode and not args.workload.startswith("decode"):
         # the 4-token decode step on the same weights (same format, same layer)
         dshape = SHAPES["decode" if shape.wfmt == "bf16" else "decode_q3"]
         drun = Runner(dshape, args.seed, dev_w, args.fat_threshold)
-        dms, dgu = drun.measure(args.decode_steps, 20)
+        dst = drun.measure(args.decode_steps, 20, flush)
+        dms, dgu = dst.mean, dst.gate_up_mean
         droof = drun.roofline(dgu)
-        log(f"[bench] decode: {dms * 1e3:.1f} us/step, gate/up {dgu * 1e3:.1f} us, "
-            f"{droof['achieved']:.1f} {droof['unit']} ({100 * droof['frac']:.1f}% of peak)")
+        dlayer = drun.layer_hbm(dms)
+        log(f"[bench] decode: {dms * 1e3:.1f} us/step (median {dst.stats()['median_ms'] * 1e3:.1f}), gate/up "
+            f"{dgu * 1e3:.1f} us, {droof['achieved']:.1f} {droof['unit']} ({100 * droof['frac']:.1f}% of peak); "
+            f"whole layer {dlayer['achieved']:.0f} GB/s ({100 * dlayer['frac']:.1f}%)")
         res["decode"] = {"value": dshape.T / (dms * 1e-3), "unit": "tokens/s", "ms_per_step": dms,
                          "steps": args.decode_steps, "config": workload_desc(dshape, args.fat_threshold),
-                         "roofline": droof}
+                         "roofline": droof, "layer_roofline": dlayer, "timing": dst.stats()}
     if not args.no_cpu_baseline:
         n = min(args.cpu_sample, shape.T)
         res["cpu_baseline"] = cpu_baseline(shape, args.seed, n)

@@ -56,3 +56,58 @@ def check_indices(got, ref):
     assert np.array_equal(got["sorted_pair"], ref["sorted_pair"]), "sorted_pair differs"
     assert np.array_equal(got["pair_to_sorted"], ref["pair_to_sorted"]), "pair_to_sorted differs"
     np.testing.assert_allclose(got["w"], ref["w"], rtol=0, atol=TOL_W)
+
+
+def oracle_rows(shape, seed, x_bits, sorted_pair, offsets, rows, chunk=16):
+    """Float64 oracle Y for the sorted rows ``rows`` only (dict row -> [H]).
+
+    The experts those rows belong to are generated a few at a time (never the
+    whole layer on the host) and each runs oracle.expert_ffn on just its
+    requested rows."""
+    from moe_inputs import for_each_expert
+    rows = np.unique(np.asarray(rows, dtype=np.int64))
+    owner = np.searchsorted(offsets, rows, side="right") - 1
+    x = oracle.bf16_to_f64(x_bits)
+    out = {}
+    experts = np.unique(owner).tolist()
+    for c0 in range(0, len(experts), chunk):
+        part = experts[c0:c0 + chunk]
+        raw = {}
+        for_each_expert(shape, seed, lambda e, a: raw.__setitem__(e, a), experts=part)
+        for e in part:
+            r = rows[owner == e]
+            tok = np.asarray(sorted_pair)[r] // shape.k
+            y = oracle.expert_ffn(x[tok], *oracle.expert_matrices(raw.pop(e)))
+            for i, row in enumerate(r.tolist()):
+                out[row] = y[i]
+    return out
+
+
+def oracle_out_tokens(yrows: dict, w, pair_to_sorted, k, tokens):
+    """oracle.combine for ``tokens`` on the compact rows of ``oracle_rows``."""
+    keys = sorted(yrows)
+    index = {r: i for i, r in enumerate(keys)}
+    Yc = np.stack([yrows[r] for r in keys])
+    p2s = np.full(len(pair_to_sorted), -1, dtype=np.int64)
+    for t in tokens:
+        for j in range(k):
+            p2s[t * k + j] = index[int(pair_to_sorted[t * k + j])]
+    return oracle.combine(Yc, np.asarray(w, dtype=np.float64), p2s, k, tokens=list(tokens))
+
+
+def tile_edge_rows(offsets, tile=32):
+    """First and last sorted row of every 32-row tile of every route list.
+    Every MFMA M-tile and every streaming tile is made of whole 32-row tiles,
+    so these rows touch each of them."""
+    rows = []
+    for e in range(len(offsets) - 1):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        for r0 in range(lo, hi, tile):
+            rows.append(r0)
+            rows.append(min(r0 + tile, hi) - 1)
+    return rows
+
+
+def parity_line(config, what, err, bar, n):
+    """One machine-readable parity record in the test log."""
+    say(f"PARITY {config} {what} err={err:.4e} bar={bar:.0e} n={n}")

@@ -124,3 +124,85 @@ def test_ffn_phases_repeat_on_one_plan(shape):
         torch.cuda.synchronize()
         assert torch.equal(b.y_sorted, refs[i]), f"repeat {rep} (input {i}): y differs"
         say(f"   repeat {rep} on input {i}: identical")
+
+
+# Several decode layers captured into one graph and replayed, every layer's
+# output checked against the float64 oracle on every replay (not only against
+# eager execution): the pages run decode as captured graphs and re-enabled
+# them only after a parity run over many decode steps showed no mismatch.
+MULTI_CASES = [
+    (LayerShape("dec_small", 4, 512, 256, 64, 8, "zipf", "bf16"), 3),
+    (LayerShape("dec_small_q3", 4, 512, 256, 64, 8, "zipf", "q3"), 3),
+    (LayerShape("dec_full_q3", 4, 4096, 2048, 384, 8, "zipf", "q3"), 3),
+    (LayerShape("dec_full_b1_q3", 1, 4096, 2048, 384, 8, "zipf", "q3"), 2),
+]
+
+
+@pytest.mark.gpu
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("shape,n_layers", MULTI_CASES, ids=[s.name for s, _ in MULTI_CASES])
+def test_multilayer_decode_graph_against_oracle(shape, n_layers):
+    import oracle
+    from moe_inputs import for_each_expert
+    from moe_inputs.device import upload_weights
+    from tests.gpu_util import TOL_BF16, TOL_Q3, oracle_out_tokens, oracle_rows, parity_line
+
+    bar = TOL_BF16 if shape.wfmt == "bf16" else TOL_Q3
+    say(f"[multilayer graph] {shape.name}: {n_layers} layers, T={shape.T} H={shape.H} I={shape.I} E={shape.E}")
+    layers, bufs, ins, refs = [], [], [], []
+    for li in range(n_layers):
+        wseed = 50 + li
+        layers.append(upload_weights(shape, wseed))
+        bufs.append(moe.MoELayerBuffers(shape.T, shape.E, shape.k, shape.H, shape.I, wfmt_id(shape)))
+        ins.append((torch.empty((shape.T, shape.E), dtype=torch.float32, device="cuda"),
+                    torch.empty((shape.T, shape.H), dtype=torch.int16, device="cuda")))
+        # two input sets per layer: the replays alternate between them
+        per = []
+        for iset in range(2):
+            lg, x = routing_inputs(shape, 1000 * iset + li)
+            ids, w = oracle.route_topk(lg, shape.k)
+            _, offsets, sp, p2s = oracle.permute(ids, shape.E)
+            yrows = oracle_rows(shape, wseed, x, sp, offsets, range(shape.T * shape.k))
+            out = oracle_out_tokens(yrows, w, p2s, shape.k, range(shape.T))
+            per.append((lg, x, ids, out))
+        refs.append(per)
+
+    def load(iset):
+        for li in range(n_layers):
+            lg, x = refs[li][iset][0], refs[li][iset][1]
+            ins[li][0].copy_(torch.from_numpy(lg))
+            ins[li][1].copy_(torch.from_numpy(x.view(np.int16)))
+
+    def step():
+        for li in range(n_layers):
+            bufs[li].forward(ins[li][0], ins[li][1], layers[li])
+
+    load(0)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    for rep in range(6):
+        iset = rep % 2
+        load(iset)
+        for b in bufs:
+            b.out.zero_()
+            b.topk_ids.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for li in range(n_layers):
+            _, _, ids, out_ref = refs[li][iset]
+            assert np.array_equal(bufs[li].topk_ids.cpu().numpy(), ids), f"replay {rep} layer {li}: ids"
+            err = oracle.rel_max_err(bufs[li].out.cpu().numpy(), out_ref)
+            if rep < 2:
+                parity_line(f"{shape.name}/graph/layer{li}/inputs{iset}", "out(all tokens)", err, bar, shape.T)
+            assert err <= bar, f"replay {rep} layer {li}: {err:.3e}"
+    say(f"   6 replays x {n_layers} layers match the oracle")
+    del graph

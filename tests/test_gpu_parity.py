@@ -91,13 +91,16 @@ def test_thin_tile_boundaries(wfmt):
     ref = oracle.moe_layer(logits, x, host_raw(W), k)
     assert np.array_equal(np.bincount(ref["ids"].ravel(), minlength=E), THIN_COUNTS)
     bufs = moe.MoELayerBuffers(T, E, k, shape.H, shape.I, wfmt_id(shape))
-    say(f"[thin edges] {wfmt} T={T} counts={THIN_COUNTS}")
-    got = run_layer(bufs, logits, x, to_dev_weights(W), fat_threshold=10**6)
-    check_indices(got, ref)
-    ey = oracle.rel_max_err(got["Y"], ref["Y"])
-    eo = oracle.rel_max_err(got["out"], ref["out"])
-    say(f"   Y err {ey:.3e}  out err {eo:.3e}")
-    assert ey <= tol(shape) and eo <= tol(shape)
+    # all lists streaming, then the 32-, 48- and 49-row lists as MFMA tiles
+    # next to the streaming 31-row one
+    for thr in (10**6, 32):
+        say(f"[thin edges] {wfmt} T={T} counts={THIN_COUNTS} fat_threshold={thr}")
+        got = run_layer(bufs, logits, x, to_dev_weights(W), fat_threshold=thr)
+        check_indices(got, ref)
+        ey = oracle.rel_max_err(got["Y"], ref["Y"])
+        eo = oracle.rel_max_err(got["out"], ref["out"])
+        say(f"   Y err {ey:.3e}  out err {eo:.3e}")
+        assert ey <= tol(shape) and eo <= tol(shape)
 
 
 def _tie_logits(T, E, seed):
