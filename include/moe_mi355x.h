@@ -30,7 +30,9 @@
  * Conventions shared by every entry point
  *   - Pointers are device pointers unless stated; the caller owns every
  *     buffer (inputs, outputs and the workspace).  The library allocates no
- *     device or host memory.
+ *     device or host memory; its one static array (the workspace of
+ *     moe_grouped_ffn_noalloc, MOE_NOALLOC_SCRATCH_BYTES per GPU) comes with
+ *     the code object.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     All work is enqueued on it; no call synchronises the host with the
  *     device, so every call may be captured into a HIP graph.
@@ -68,6 +70,10 @@ typedef int32_t moe_status;
 
 #define MOE_MAX_TOPK    32
 #define MOE_MAX_EXPERTS 1024
+
+/* Bytes of the per-GPU array that moe_grouped_ffn_noalloc uses as its
+ * workspace (64 MiB). */
+#define MOE_NOALLOC_SCRATCH_BYTES (64ull << 20)
 
 /* Human-readable name of a status code (static string, never NULL). */
 const char* moe_status_string(moe_status s);
@@ -237,6 +243,33 @@ moe_status moe_ffn_gate_up(const uint16_t* x, int wfmt, const void* w_gate, cons
 moe_status moe_ffn_down(int wfmt, const void* w_down, const uint16_t* s_down, int T, int E, int k, int H, int I,
                         int fat_threshold, uint16_t* y_sorted, void* workspace, size_t workspace_bytes,
                         void* stream);
+
+/*
+ * moe_grouped_ffn_noalloc -- moe_grouped_ffn without a caller workspace and
+ * without any allocation, for callers that cannot allocate: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ *
+ * Same arguments, kernels and results as moe_grouped_ffn (bit for bit), minus
+ * `workspace` / `workspace_bytes`: the batch lists and the activation a live
+ * in one array of MOE_NOALLOC_SCRATCH_BYTES per GPU inside the library (it
+ * stays allocated until the process ends).  The FFN part of the workspace,
+ * moe_workspace_size(T, E, k, H, I, wfmt) minus the permute part (ceil(T /
+ * 256) * E * 4 bytes, rounded up to 256), must fit in it, else
+ * MOE_ERR_WORKSPACE and nothing is enqueued: about T * k * I * 2 bytes plus a
+ * few KB of lists, so up to 2,048 tokens at k = 8, I = 2048 (the 3-bit format
+ * needs T * H * 2 + T * H / 32 bytes more).  Every call writes its lists
+ * before reading them, so nothing carries over between calls.
+ *
+ * Every call on one GPU shares that GPU's array: two calls that overlap on
+ * one GPU (on different streams, or from different threads without stream
+ * ordering) race and give undefined results.  Calls ordered on one stream are
+ * safe.
+ */
+moe_status moe_grouped_ffn_noalloc(const uint16_t* x, int wfmt, const void* w_gate, const void* w_up,
+                                   const void* w_down, const uint16_t* s_gate, const uint16_t* s_up,
+                                   const uint16_t* s_down, const int32_t* expert_offsets, const int32_t* sorted_pair,
+                                   int T, int E, int k, int H, int I, int fat_threshold, uint16_t* y_sorted,
+                                   void* stream);
 
 /*
  * moe_combine -- out[t, :] = sum_{j=0..k-1} topk_w[t, j] * y_sorted[pair_to_sorted[t*k+j], :]

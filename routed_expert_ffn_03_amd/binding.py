@@ -23,7 +23,9 @@ DEFAULT_FAT_THRESHOLD = 32
 
 EXPORTS = ("moe_status_string", "moe_version", "moe_workspace_size", "moe_route_topk", "moe_router_topk",
            "moe_permute", "moe_grouped_ffn", "moe_ffn_plan", "moe_ffn_gate_up", "moe_ffn_down",
-           "moe_combine")
+           "moe_combine", "moe_grouped_ffn_noalloc")
+
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 _lib = None
 
@@ -63,6 +65,9 @@ def lib() -> ctypes.CDLL:
         L.moe_ffn_gate_up.argtypes = [vp, i32, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, vp, sz, vp]
         L.moe_ffn_down.restype = i32
         L.moe_ffn_down.argtypes = [i32, vp, vp, i32, i32, i32, i32, i32, i32, vp, vp, sz, vp]
+        L.moe_grouped_ffn_noalloc.restype = i32
+        L.moe_grouped_ffn_noalloc.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp, vp, vp,
+                                              i32, i32, i32, i32, i32, i32, vp, vp]
         L.moe_combine.restype = i32
         L.moe_combine.argtypes = [vp, vp, vp, i32, i32, i32, vp, vp]
         _lib = L
@@ -164,6 +169,28 @@ def moe_grouped_ffn(x, w_gate, w_up, w_down, expert_offsets, sorted_pair, k, y_s
                                  _ptr(s_up), _ptr(s_down), _ptr(expert_offsets), _ptr(sorted_pair), T, E, k, H, I,
                                  fat_threshold, _ptr(y_sorted), _ptr(workspace), workspace.numel(),
                                  _stream(stream)), "moe_grouped_ffn")
+
+
+def moe_grouped_ffn_noalloc(x, w_gate, w_up, w_down, expert_offsets, sorted_pair, k, y_sorted, s_gate=None,
+                            s_up=None, s_down=None, fat_threshold=DEFAULT_FAT_THRESHOLD, wfmt=MOE_WFMT_BF16,
+                            stream=None):
+    """moe_grouped_ffn with the library's own per-GPU scratch array as its
+    workspace (no allocation; calls that overlap on one GPU race)."""
+    T, H = x.shape
+    E = expert_offsets.numel() - 1
+    I = w_gate.shape[1]
+    for t, n in ((x, "x"), (y_sorted, "y_sorted"), (w_gate, "w_gate"), (w_up, "w_up"), (w_down, "w_down"),
+                 (expert_offsets, "expert_offsets"), (sorted_pair, "sorted_pair")):
+        if not (t.is_cuda and t.is_contiguous()):
+            raise ValueError(f"{n}: expected a contiguous GPU tensor")
+    if x.element_size() != 2 or y_sorted.element_size() != 2:
+        raise ValueError("x and y_sorted must have 16-bit elements")
+    if tuple(y_sorted.shape) != (T * k, H):
+        raise ValueError(f"y_sorted: shape {tuple(y_sorted.shape)} != {(T * k, H)}")
+    _check(lib().moe_grouped_ffn_noalloc(_ptr(x), wfmt, _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(s_gate),
+                                         _ptr(s_up), _ptr(s_down), _ptr(expert_offsets), _ptr(sorted_pair), T, E,
+                                         k, H, I, fat_threshold, _ptr(y_sorted), _stream(stream)),
+           "moe_grouped_ffn_noalloc")
 
 
 def moe_ffn_plan(expert_offsets, T, k, H, I, workspace, fat_threshold=DEFAULT_FAT_THRESHOLD,

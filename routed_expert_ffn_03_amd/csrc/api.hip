@@ -6,7 +6,36 @@
 #include "../../include/moe_mi355x.h"
 #include "kernels.h"
 
+#include <mutex>
+
 namespace {
+
+// Workspace of moe_grouped_ffn_noalloc: one array per GPU, held by the code
+// object for the life of the process.  Host code never passes the array's
+// name to a kernel (on the host it is only a stand-in for the symbol): the
+// device address comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) unsigned char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64] = {};
+
+// The device address of `scratch` on the current device.
+hipError_t scratch_address(void** out) {
+    int dev = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess) return err;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (err != hipSuccess) return err;
+        if (!p) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
+}
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
@@ -164,6 +193,41 @@ moe_status moe_grouped_ffn(const uint16_t* x, int wfmt, const void* w_gate, cons
     if (st != MOE_OK) return st;
     return moe_ffn_down(wfmt, w_down, s_down, T, E, k, H, I, fat_threshold, y_sorted, workspace, workspace_bytes,
                         stream);
+}
+
+moe_status moe_grouped_ffn_noalloc(const uint16_t* x, int wfmt, const void* w_gate, const void* w_up,
+                                   const void* w_down, const uint16_t* s_gate, const uint16_t* s_up,
+                                   const uint16_t* s_down, const int32_t* expert_offsets, const int32_t* sorted_pair,
+                                   int T, int E, int k, int H, int I, int fat_threshold, uint16_t* y_sorted,
+                                   void* stream) {
+    if (!x || !w_gate || !w_up || !w_down || !expert_offsets || !sorted_pair || !y_sorted)
+        return MOE_ERR_INVALID_ARG;
+    if (fat_threshold < 1 || bad_tek(T, E, k) || H < 1 || I < 1) return MOE_ERR_INVALID_ARG;
+    if (wfmt != MOE_WFMT_BF16 && wfmt != MOE_WFMT_Q3G128) return MOE_ERR_UNSUPPORTED;
+    if (!scales_ok(wfmt, s_gate, s_up) || !scales_ok(wfmt, s_down, s_down)) return MOE_ERR_INVALID_ARG;
+    if (!ffn_shape_ok(T, k, H, I)) return MOE_ERR_UNSUPPORTED;
+    if (moe::ffn_ws_bytes(T, E, k, H, I, wfmt) > MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_WORKSPACE;
+    void* ws = nullptr;
+    hipError_t err = scratch_address(&ws);
+    if (err != hipSuccess) return MOE_ERR_HIP;
+    moe::FfnLaunch a{};
+    a.x = x;
+    a.wfmt = wfmt;
+    a.wg = w_gate; a.wu = w_up; a.wd = w_down;
+    a.sg = s_gate; a.su = s_up; a.sd = s_down;
+    a.offsets = expert_offsets;
+    a.sorted_pair = sorted_pair;
+    a.T = T; a.E = E; a.k = k; a.H = H; a.I = I;
+    a.fat_threshold = fat_threshold;
+    a.y = y_sorted;
+    a.ws = ws;
+    const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    // the plan rewrites the list header, totals and the tail counters of
+    // the shared array before the two phases read them
+    err = moe::launch_ffn_plan(a, s);
+    if (err == hipSuccess) err = moe::launch_ffn_phase(a, 1, s);
+    if (err == hipSuccess) err = moe::launch_ffn_phase(a, 2, s);
+    return hip_status(err);
 }
 
 moe_status moe_combine(const uint16_t* y_sorted, const float* topk_w, const int32_t* pair_to_sorted, int T, int k,

@@ -146,3 +146,28 @@ def test_combine_rejects(L):
     assert L.moe_combine(FAKE, FAKE, FAKE, 0, 2, 64, FAKE, None) == moe.MOE_ERR_INVALID_ARG
     assert L.moe_combine(FAKE, FAKE, FAKE, 4, 33, 64, FAKE, None) == moe.MOE_ERR_INVALID_ARG
     assert L.moe_combine(FAKE, FAKE, FAKE, 4, 2, 60, FAKE, None) == moe.MOE_ERR_UNSUPPORTED
+
+
+def test_noalloc_rejects(L):
+    F = FAKE
+    args = [F, 0, F, F, F, None, None, None, F, F, 64, 16, 2, 256, 128, 32, F, None]
+    for i in (0, 2, 3, 4, 8, 9, 16):
+        bad = list(args)
+        bad[i] = None
+        assert L.moe_grouped_ffn_noalloc(*bad) == moe.MOE_ERR_INVALID_ARG, i
+    bad = list(args)
+    bad[15] = 0                                     # fat_threshold
+    assert L.moe_grouped_ffn_noalloc(*bad) == moe.MOE_ERR_INVALID_ARG
+    bad = list(args)
+    bad[5] = F                                      # bf16 weights take no scales
+    assert L.moe_grouped_ffn_noalloc(*bad) == moe.MOE_ERR_INVALID_ARG
+    bad = list(args)
+    bad[1] = 1                                      # 3-bit without scales
+    assert L.moe_grouped_ffn_noalloc(*bad) == moe.MOE_ERR_INVALID_ARG
+    bad = list(args)
+    bad[13] = 200                                   # H not a multiple of 256
+    assert L.moe_grouped_ffn_noalloc(*bad) == moe.MOE_ERR_UNSUPPORTED
+    # beyond the 64 MiB array: 4096 x 8 pairs x 2048 x 2 bytes of activation
+    big = list(args)
+    big[10:15] = [4096, 384, 8, 4096, 2048]
+    assert L.moe_grouped_ffn_noalloc(*big) == moe.MOE_ERR_WORKSPACE
