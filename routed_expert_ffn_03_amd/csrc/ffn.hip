@@ -37,6 +37,7 @@
 // MFMA with W_down converted to fp16 when staged.  3-bit weights are decoded
 // to bf16 (phase 1) or fp16 (phase 2) as they are staged.
 #include "common.h"
+#include "ffn_shared.h"
 #include "kernels.h"
 #include "lds_dma.h"
 
@@ -45,54 +46,6 @@
 
 namespace moe {
 namespace {
-
-// One M-tile of an expert's route list: rows [row0, row0 + rows) of the
-// sorted pairs; `first` / `count` locate all M-tiles of the same expert.
-struct MTile {
-    int32_t e, row0, rows, first, count, pad[3];
-};
-
-struct FfnHeader {
-    int32_t n_fat, n_thin;
-    int32_t tail_next[2];         // fat items handed out past the static rounds, per phase
-    int32_t tail_done[2];         // blocks past their last item; the last one re-zeroes both counters
-    int32_t pad[58];
-};
-
-// The fat kernels walk their items in static rounds (block b: item b, b + G,
-// ...).  In the gate/up phase the last partial round and the three full
-// rounds before it are handed out instead one item at a time from a counter,
-// as blocks finish: item costs vary with the M-tile's row tiles, and the
-// static split alone leaves the busiest CU ~7% above the mean at the 16k chunk
-// (the dynamic tail gains 2% there; the shorter down kernel loses 1-2% with
-// it and stays static).
-constexpr int FAT_TAIL_ROUNDS = 3;
-
-constexpr int FAT_BM = 256;              // rows per fat M-tile
-constexpr int FAT_THREADS = 256;
-constexpr int THIN_BM = 32;
-constexpr int THIN_THREADS = 256;
-
-constexpr int Q3_WORDS = 13;
-
-struct FfnArgs {
-    const uint16_t* x;
-    const void* wg;
-    const void* wu;
-    const void* wd;
-    const uint16_t* sg;
-    const uint16_t* su;
-    const uint16_t* sd;
-    const int32_t* sorted_pair;
-    int T, k, H, I;
-    uint16_t* act;
-    uint16_t* y;
-    uint16_t* xq;                 // 3-bit thin path: x rows in pair-slot order per 128-group
-    uint32_t* xs;                 // ... and each (token, group) sum of x as a bf16 hi, lo pair
-    const FfnHeader* hdr;
-    const MTile* fat;
-    const MTile* thin;
-};
 
 // ------------------------------------------------------------ tile builder
 
@@ -140,38 +93,7 @@ __device__ __forceinline__ f32x16 mma(u32x4 a, u32x4 b, f32x16 c) {
     return PHASE == 1 ? mfma_bf16(a, b, c) : mfma_f16(a, b, c);
 }
 
-__device__ __forceinline__ int logical_block() {
-    const int G = gridDim.x, b = blockIdx.x;
-    return (G % 8 == 0) ? (b % 8) * (G / 8) + b / 8 : b;
-}
-
 // ------------------------------------------------------------ fat kernel
-
-// Fat work item -> (M-tile, N-tile).  The items of one expert (count M-tiles
-// x NT N-tiles) are contiguous: its M-tiles are split into ceil(count / 8)
-// blocks of near-equal size s (at most 8), and within a block the items run
-// N-tile by N-tile with the s M-tiles of each N-tile next to each other.  The
-// 32 consecutive items that the blocks of one XCD take at a time then cover s
-// activation tiles and about 32 / s weight tiles, each fetched once into that
-// XCD's L2 and shared.
-__device__ __forceinline__ void fat_item(const MTile* __restrict__ fat, int item, int NT, MTile& t, int& nt) {
-    const int q0 = item / NT;
-    const MTile t0 = fat[q0];
-    const int me = t0.count, local = item - t0.first * NT;
-    const int nblk = (me + 7) >> 3;
-    const int q = me / nblk, r = me - q * nblk;              // r blocks of q + 1 M-tiles, then blocks of q
-    const int big = (q + 1) * NT;
-    int s, m0, off;
-    if (local < r * big) {
-        const int b = local / big;
-        s = q + 1; m0 = b * s; off = local - b * big;
-    } else {
-        const int l2 = local - r * big, b = l2 / (q * NT);
-        s = q; m0 = r * (q + 1) + b * q; off = l2 - b * q * NT;
-    }
-    nt = off / s;
-    t = fat[t0.first + m0 + (off - nt * s)];
-}
 
 // Wait until at most N of this wave's LDS reads are outstanding; the operand
 // registers the wait is for are tied to it, so no use of them is scheduled
@@ -185,20 +107,6 @@ __device__ __forceinline__ void lds_wait_frag(u32x4 (&x)[8], u32x4 (&y)[2]) {
                  : "memory");
 }
 
-// Wait until at most `stages` stages of this wave's loads are outstanding
-// (loads complete in issue order, L load instructions per stage).
-template <int L>
-__device__ __forceinline__ void vm_wait_stages(int stages) {
-    switch (stages) {
-        case 0: vm_wait<0>(); break;
-        case 1: vm_wait<L>(); break;
-        case 2: vm_wait<2 * L>(); break;
-        case 3: vm_wait<3 * L>(); break;
-        case 4: vm_wait<4 * L>(); break;
-        default: vm_wait<5 * L>(); break;
-    }
-}
-
 // 3-bit field at bit OFF as one v_bfe_u32 (left to the compiler, a constant
 // offset becomes a shift, a mask and a byte conversion: one more instruction)
 template <int OFF>
@@ -207,10 +115,6 @@ __device__ __forceinline__ uint32_t field3(uint32_t bits) {
     asm("v_bfe_u32 %0, %1, %2, 3" : "=v"(r) : "v"(bits), "n"(OFF));
     return r;
 }
-
-constexpr int DMA_BK = 32;                                  // k per LDS stage
-constexpr uint32_t DMA_ROW = DMA_BK * 2;                    // bytes of one row per stage
-constexpr uint32_t DMA_OPER = FAT_BM * DMA_ROW;             // 16 KB: 256 rows of one operand
 
 // Ring stage layout of the fat kernel per weight format.  bf16: activations
 // and weight rows, 16 KB each, 64-byte rows.  3-bit: activations, the four
@@ -1159,7 +1063,6 @@ FfnLayout ffn_layout(int T, int E, int k, int H, int I, int wfmt) {
 
 struct DevInfo {
     int cus = 0;
-    int ring = 4;                               // LDS ring stages of the bf16 fat kernels (4 or 5)
     int q3ring = 5;                             // ... of the 3-bit fat kernels (5 or 6)
     int thin_blocks[2][2][2] = {};              // [wfmt][phase-1][chunk width 2 / 4]
 };
@@ -1184,24 +1087,18 @@ hipError_t dev_info(DevInfo& out) {
         int cus = 0;
         err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
         if (err != hipSuccess) return err;
-        // the fat kernels use up to 160 KB of dynamic LDS (above the default
-        // cap): a fifth 32 KB bf16 stage and a sixth 21 KB 3-bit stage where a
-        // block may hold that much
+        // the 3-bit fat kernels use up to 126 KB of dynamic LDS (above the
+        // default cap): a sixth 21 KB stage where a block may hold that much
         int lds_max = 0;
         err = hipDeviceGetAttribute(&lds_max, hipDeviceAttributeMaxSharedMemoryPerBlock, dev);
         if (err != hipSuccess) return err;
         const struct {
             const void* f;
             size_t bytes;
-        } fats[8] = {{(const void*)ffn_fat_kernel<1, 0, 4>, fat_lds_bytes<0, 4>()},
-                     {(const void*)ffn_fat_kernel<2, 0, 4>, fat_lds_bytes<0, 4>()},
-                     {(const void*)ffn_fat_kernel<1, 0, 5>, fat_lds_bytes<0, 5>()},
-                     {(const void*)ffn_fat_kernel<2, 0, 5>, fat_lds_bytes<0, 5>()},
-                     {(const void*)ffn_fat_kernel<1, 1, 5>, fat_lds_bytes<1, 5>()},
+        } fats[4] = {{(const void*)ffn_fat_kernel<1, 1, 5>, fat_lds_bytes<1, 5>()},
                      {(const void*)ffn_fat_kernel<2, 1, 5>, fat_lds_bytes<1, 5>()},
                      {(const void*)ffn_fat_kernel<1, 1, 6>, fat_lds_bytes<1, 6>()},
                      {(const void*)ffn_fat_kernel<2, 1, 6>, fat_lds_bytes<1, 6>()}};
-        d.ring = (size_t)lds_max >= fat_lds_bytes<0, 5>() ? 5 : 4;
         d.q3ring = (size_t)lds_max >= fat_lds_bytes<1, 6>() ? 6 : 5;
         for (const auto& f : fats) {
             if (f.bytes > (size_t)lds_max) continue;
@@ -1243,17 +1140,17 @@ FfnArgs make_args(const FfnLaunch& a) {
 // selects an expert at most once, so with T < fat_threshold (decode) there is
 // no fat work and that launch is skipped.
 template <int PHASE, int WFMT>
-void launch_phase_t(const FfnArgs& fa, const DevInfo& d, bool fat_possible, hipStream_t s) {
+hipError_t launch_phase_t(const FfnArgs& fa, const DevInfo& d, bool fat_possible, hipStream_t s) {
     if (fat_possible) {
         if constexpr (WFMT != 0) {
             if (d.q3ring == 6)
                 ffn_fat_kernel<PHASE, 1, 6><<<d.cus, FAT_THREADS, fat_lds_bytes<1, 6>(), s>>>(fa);
             else
                 ffn_fat_kernel<PHASE, 1, 5><<<d.cus, FAT_THREADS, fat_lds_bytes<1, 5>(), s>>>(fa);
-        } else if (d.ring == 5) {
-            ffn_fat_kernel<PHASE, 0, 5><<<d.cus, FAT_THREADS, fat_lds_bytes<0, 5>(), s>>>(fa);
         } else {
-            ffn_fat_kernel<PHASE, 0, 4><<<d.cus, FAT_THREADS, fat_lds_bytes<0, 4>(), s>>>(fa);
+            // bf16 weights: eight waves per CU, two per SIMD (fat8.hip)
+            const hipError_t err = launch_fat8_phase(fa, PHASE, d.cus, s);
+            if (err != hipSuccess) return err;
         }
     }
     if constexpr (WFMT != 0) {
@@ -1267,6 +1164,7 @@ void launch_phase_t(const FfnArgs& fa, const DevInfo& d, bool fat_possible, hipS
         else
             ffn_thin_kernel<PHASE, 2><<<d.cus * d.thin_blocks[0][PHASE - 1][0], THIN_THREADS, 0, s>>>(fa);
     }
+    return hipGetLastError();
 }
 
 }  // namespace
@@ -1289,14 +1187,8 @@ hipError_t launch_ffn_phase(const FfnLaunch& a, int phase, hipStream_t s) {
     if (err != hipSuccess) return err;
     const FfnArgs fa = make_args(a);
     const bool fat = a.T >= a.fat_threshold;
-    if (phase == 1) {
-        if (a.wfmt == 0) launch_phase_t<1, 0>(fa, d, fat, s);
-        else launch_phase_t<1, 1>(fa, d, fat, s);
-    } else {
-        if (a.wfmt == 0) launch_phase_t<2, 0>(fa, d, fat, s);
-        else launch_phase_t<2, 1>(fa, d, fat, s);
-    }
-    return hipGetLastError();
+    if (phase == 1) return a.wfmt == 0 ? launch_phase_t<1, 0>(fa, d, fat, s) : launch_phase_t<1, 1>(fa, d, fat, s);
+    return a.wfmt == 0 ? launch_phase_t<2, 0>(fa, d, fat, s) : launch_phase_t<2, 1>(fa, d, fat, s);
 }
 
 }  // namespace moe

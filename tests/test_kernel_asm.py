@@ -23,8 +23,8 @@ from tests.asm_check import kernel_bodies, stale_lds_uses
 from routed_expert_ffn_03_amd.build import BUILD, CSRC, HIPCC_FLAGS
 
 # sources compiled to assembly, and every file their hash covers
-UNITS = ["ffn.hip", "route.hip"]
-SOURCES = UNITS + ["common.h", "kernels.h", "lds_dma.h"]
+UNITS = ["ffn.hip", "fat8.hip", "route.hip"]
+SOURCES = UNITS + ["common.h", "kernels.h", "lds_dma.h", "ffn_shared.h"]
 
 
 def _hipcc():
@@ -101,6 +101,7 @@ def test_checker_accepts_clean_code():
 def test_no_lds_result_used_before_its_wait(ffn_asm):
     kernels = {k: v for k, v in kernel_bodies(ffn_asm).items() if "ffn_" in k or "router_" in k}
     assert any("ffn_fat_kernel" in k for k in kernels) and any("router_topk_kernel" in k for k in kernels)
+    assert any("ffn_fat8_kernel" in k for k in kernels)
     assert any("router_logits_split_kernel" in k for k in kernels)
     bad = {}
     for name, lines in kernels.items():
@@ -128,7 +129,8 @@ def _loops(lines):
 
 
 def test_fat_k_loops_do_not_spill(ffn_asm):
-    kernels = {k: v for k, v in kernel_bodies(ffn_asm).items() if "ffn_fat_kernel" in k}
+    kernels = {k: v for k, v in kernel_bodies(ffn_asm).items() if "ffn_fat_kernel" in k or "ffn_fat8_kernel" in k}
+    assert any("ffn_fat8_kernel" in k for k in kernels)
     checked = 0
     for name, lines in kernels.items():
         for lab, body in _loops(lines):
