@@ -2,7 +2,8 @@
 """Throughput of the routed-expert layer on one MI355X.
 
 One step = one full layer call (route -> permute -> plan -> gate/up -> down
--> combine) over one batch of synthetic inputs already resident in HBM.
+-> combine; the first three in one launch for decode-sized batches) over one
+batch of synthetic inputs already resident in HBM.
 The headline workload is the 16,384-token prefill chunk (bf16 experts,
 Zipf-skewed router); the 4-token decode step is measured in the same run on
 the same weights and reported under "decode" (with --workload prefill16k_q3:
@@ -146,9 +147,10 @@ class Runner:
 
     def step(self, ev=None):
         m, b, s, w = self.moe, self.b, self.shape, self.w
-        m.moe_route_topk(self.logits, s.k, b.topk_ids, b.topk_w, b.expert_counts)
-        m.moe_permute(b.topk_ids, s.E, b.expert_offsets, b.sorted_pair, b.pair_to_sorted, b.workspace)
-        m.moe_ffn_plan(b.expert_offsets, s.T, s.k, s.H, s.I, b.workspace, fat_threshold=self.thr, wfmt=self.wfmt)
+        # route + permute + plan (one launch for decode-sized batches)
+        m.moe_route_permute_plan(self.logits, s.k, s.H, s.I, b.topk_ids, b.topk_w, b.expert_counts,
+                                 b.expert_offsets, b.sorted_pair, b.pair_to_sorted, b.workspace,
+                                 fat_threshold=self.thr, wfmt=self.wfmt)
         if ev is not None:
             ev[0].record()
         m.moe_ffn_gate_up(self.x, w["gate"], w["up"], b.sorted_pair, s.E, s.k, b.workspace,
@@ -432,15 +434,19 @@ def router_bench(seed, steps):
             torch.cuda.synchronize()
             return a.elapsed_time(b) / n
 
+        ws = torch.empty(s.T * s.E * 4, dtype=torch.uint8, device="cuda")
         fused = timed(lambda: moe.moe_router_topk(dx, dw, s.k, ids, tw, cnt))
+        fused_ws = timed(lambda: moe.moe_router_topk(dx, dw, s.k, ids, tw, cnt, workspace=ws))
         with_logits = timed(lambda: moe.moe_router_topk(dx, dw, s.k, ids, tw, cnt, logits=lg))
         gate_only = timed(lambda: moe.moe_route_topk(lg, s.k, ids, tw, cnt))
         flops = 2.0 * s.T * s.E * s.H
         r = {"workload": name, "tokens": s.T, "experts": s.E, "hidden": s.H, "top_k": s.k,
-             "fused_ms": fused, "with_logits_ms": with_logits, "gate_on_given_logits_ms": gate_only,
+             "fused_ms": fused, "fused_with_workspace_ms": fused_ws, "with_logits_ms": with_logits,
+             "gate_on_given_logits_ms": gate_only,
              "fused_tflops": flops / (fused * 1e-3) / 1e12,
              "fused_mfma_frac": flops / (fused * 1e-3) / 1e12 / PEAK_MFMA_TFLOPS["bf16"]}
-        log(f"[router] {name}: fused {fused * 1e3:.1f} us ({r['fused_tflops']:.0f} TFLOP/s), with logits out "
+        log(f"[router] {name}: fused {fused * 1e3:.1f} us ({r['fused_tflops']:.0f} TFLOP/s), with a workspace "
+            f"{fused_ws * 1e3:.1f} us, with logits out "
             f"{with_logits * 1e3:.1f} us, gate alone on given logits {gate_only * 1e3:.1f} us")
         res.append(r)
     print(json.dumps({"mode": "router", "data": "synthetic", "results": res}), flush=True)

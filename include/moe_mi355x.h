@@ -121,11 +121,14 @@ moe_status moe_route_topk(const float* logits, int T, int E, int k,
  * on MFMA), then for every token exactly the selection, gate weights and
  * histogram of moe_route_topk applied to these fp32 logits.  The logits stay
  * on chip unless `logits` is non-NULL, in which case they are also written
- * there (fp32 [T, E], row-major).  With `logits` non-NULL and T <= 32 the
- * GEMM is spread over E / 32 blocks that write the logits, and the gate then
- * runs on them; every logit goes through the same MFMA accumulation chain as
- * on chip, so ids, weights and histogram are bit-identical to the call
- * without `logits`.  Reading of the pages (routing over the
+ * there (fp32 [T, E], row-major).  For T <= 32 with somewhere to put the
+ * logits -- `logits`, or else `workspace` -- the GEMM is spread over E / 32
+ * blocks that write them, and the gate then runs on them (at 4 tokens and
+ * 384 experts about 17 us instead of 77 us on the single block that keeps
+ * them on chip); every logit goes through the same MFMA accumulation chain
+ * as on chip, so ids, weights and histogram are bit-identical either way.
+ * `workspace` (device, may be NULL) is used only then; when non-NULL it
+ * must hold T * E * 4 bytes, else MOE_ERR_WORKSPACE.  Reading of the pages (routing over the
  * layer's routed experts: dsv41-flash-offload wiki, opening paragraph; the
  * router itself is not written there): a bias-free linear router over the
  * hidden state, the expert's rows stored [E, H] like the expert matrices.
@@ -141,7 +144,7 @@ moe_status moe_route_topk(const float* logits, int T, int E, int k,
  */
 moe_status moe_router_topk(const uint16_t* x, const uint16_t* w_router, int T, int E, int H, int k,
                            int32_t* topk_ids, float* topk_w, int32_t* expert_counts, float* logits,
-                           void* stream);
+                           void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * moe_permute -- per-expert route lists (a stable counting sort of the
@@ -222,6 +225,20 @@ moe_status moe_grouped_ffn(const uint16_t* x, int wfmt,
  */
 moe_status moe_ffn_plan(const int32_t* expert_offsets, int T, int E, int k, int H, int I, int wfmt,
                         int fat_threshold, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * moe_route_permute_plan -- moe_route_topk, moe_permute and moe_ffn_plan in
+ * one call, with the same arguments (H, I, wfmt and fat_threshold as for the
+ * plan) and the same results bit for bit.  For T <= 64 tokens (decode
+ * batches) the three run in a single launch on one block, with the route
+ * lists kept on chip between them; larger batches run the three entry points
+ * in order.  Follow it with moe_ffn_gate_up, moe_ffn_down and moe_combine.
+ * Errors: those of the three calls (NULL outputs, shapes, workspace size).
+ */
+moe_status moe_route_permute_plan(const float* logits, int T, int E, int k, int H, int I, int wfmt,
+                                  int fat_threshold, int32_t* topk_ids, float* topk_w, int32_t* expert_counts,
+                                  int32_t* expert_offsets, int32_t* sorted_pair, int32_t* pair_to_sorted,
+                                  void* workspace, size_t workspace_bytes, void* stream);
 
 /* moe_ffn_gate_up -- a = silu(x W_gate^T) * (x W_up^T) for every planned batch,
  * stored fp16 in the workspace (row i of a belongs to sorted row i).

@@ -23,7 +23,7 @@ DEFAULT_FAT_THRESHOLD = 32
 
 EXPORTS = ("moe_status_string", "moe_version", "moe_workspace_size", "moe_route_topk", "moe_router_topk",
            "moe_permute", "moe_grouped_ffn", "moe_ffn_plan", "moe_ffn_gate_up", "moe_ffn_down",
-           "moe_combine", "moe_grouped_ffn_noalloc")
+           "moe_combine", "moe_grouped_ffn_noalloc", "moe_route_permute_plan")
 
 NOALLOC_SCRATCH_BYTES = 64 << 20
 
@@ -53,7 +53,7 @@ def lib() -> ctypes.CDLL:
         L.moe_route_topk.restype = i32
         L.moe_route_topk.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp]
         L.moe_router_topk.restype = i32
-        L.moe_router_topk.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp]
+        L.moe_router_topk.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp, vp, vp, vp, sz, vp]
         L.moe_permute.restype = i32
         L.moe_permute.argtypes = [vp, i32, i32, i32, vp, vp, vp, vp, sz, vp]
         L.moe_grouped_ffn.restype = i32
@@ -68,6 +68,8 @@ def lib() -> ctypes.CDLL:
         L.moe_grouped_ffn_noalloc.restype = i32
         L.moe_grouped_ffn_noalloc.argtypes = [vp, i32, vp, vp, vp, vp, vp, vp, vp, vp,
                                               i32, i32, i32, i32, i32, i32, vp, vp]
+        L.moe_route_permute_plan.restype = i32
+        L.moe_route_permute_plan.argtypes = [vp, i32, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.moe_combine.restype = i32
         L.moe_combine.argtypes = [vp, vp, vp, i32, i32, i32, vp, vp]
         _lib = L
@@ -114,9 +116,10 @@ def moe_route_topk(logits, k, topk_ids, topk_w, expert_counts, stream=None):
                                 _stream(stream)), "moe_route_topk")
 
 
-def moe_router_topk(x, w_router, k, topk_ids, topk_w, expert_counts, logits=None, stream=None):
+def moe_router_topk(x, w_router, k, topk_ids, topk_w, expert_counts, logits=None, workspace=None, stream=None):
     """Router GEMM (x [T, H] bf16 bits . w_router [E, H] bf16 bits) fused with the top-k gate;
-    ``logits`` (fp32 [T, E]) is written only when given."""
+    ``logits`` (fp32 [T, E]) is written only when given; ``workspace`` (uint8, >= T * E * 4
+    bytes) lets a batch of at most 32 tokens spread the GEMM over E / 32 blocks without it."""
     T, H = x.shape
     E = w_router.shape[0]
     if x.dtype not in (torch.int16, torch.bfloat16) or w_router.dtype not in (torch.int16, torch.bfloat16):
@@ -131,8 +134,13 @@ def moe_router_topk(x, w_router, k, topk_ids, topk_w, expert_counts, logits=None
     _dev(expert_counts, torch.int32, "expert_counts")
     if logits is not None:
         _dev(logits, torch.float32, "logits")
+    ws_bytes = 0
+    if workspace is not None:
+        _dev(workspace, torch.uint8, "workspace")
+        ws_bytes = workspace.numel()
     _check(lib().moe_router_topk(_ptr(x), _ptr(w_router), T, E, H, k, _ptr(topk_ids), _ptr(topk_w),
-                                 _ptr(expert_counts), _ptr(logits), _stream(stream)), "moe_router_topk")
+                                 _ptr(expert_counts), _ptr(logits), _ptr(workspace), ws_bytes, _stream(stream)),
+           "moe_router_topk")
 
 
 def moe_permute(topk_ids, E, expert_offsets, sorted_pair, pair_to_sorted, workspace, stream=None):
@@ -169,6 +177,27 @@ def moe_grouped_ffn(x, w_gate, w_up, w_down, expert_offsets, sorted_pair, k, y_s
                                  _ptr(s_up), _ptr(s_down), _ptr(expert_offsets), _ptr(sorted_pair), T, E, k, H, I,
                                  fat_threshold, _ptr(y_sorted), _ptr(workspace), workspace.numel(),
                                  _stream(stream)), "moe_grouped_ffn")
+
+
+def moe_route_permute_plan(logits, k, H, I, topk_ids, topk_w, expert_counts, expert_offsets, sorted_pair,
+                           pair_to_sorted, workspace, fat_threshold=DEFAULT_FAT_THRESHOLD, wfmt=MOE_WFMT_BF16,
+                           stream=None):
+    """moe_route_topk + moe_permute + moe_ffn_plan (one launch for T <= 64)."""
+    _dev(logits, torch.float32, "logits")
+    T, E = logits.shape
+    for t, dt, n, shp in ((topk_ids, torch.int32, "topk_ids", (T, k)), (topk_w, torch.float32, "topk_w", (T, k)),
+                          (expert_counts, torch.int32, "expert_counts", (E,)),
+                          (expert_offsets, torch.int32, "expert_offsets", (E + 1,)),
+                          (sorted_pair, torch.int32, "sorted_pair", (T * k,)),
+                          (pair_to_sorted, torch.int32, "pair_to_sorted", (T * k,))):
+        _dev(t, dt, n)
+        if tuple(t.shape) != shp:
+            raise ValueError(f"{n}: shape {tuple(t.shape)} != {shp}")
+    _dev(workspace, torch.uint8, "workspace")
+    _check(lib().moe_route_permute_plan(_ptr(logits), T, E, k, H, I, wfmt, fat_threshold, _ptr(topk_ids),
+                                        _ptr(topk_w), _ptr(expert_counts), _ptr(expert_offsets), _ptr(sorted_pair),
+                                        _ptr(pair_to_sorted), _ptr(workspace), workspace.numel(), _stream(stream)),
+           "moe_route_permute_plan")
 
 
 def moe_grouped_ffn_noalloc(x, w_gate, w_up, w_down, expert_offsets, sorted_pair, k, y_sorted, s_gate=None,

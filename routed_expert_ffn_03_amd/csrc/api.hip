@@ -4,6 +4,7 @@
 // Failing loudly instead of falling back: "dsv41-flash-engram-disk-prestage",
 // section "The prestage, per decode step", point 4.
 #include "../../include/moe_mi355x.h"
+#include "ffn_shared.h"
 #include "kernels.h"
 
 #include <mutex>
@@ -89,11 +90,15 @@ moe_status moe_route_topk(const float* logits, int T, int E, int k, int32_t* top
 }
 
 moe_status moe_router_topk(const uint16_t* x, const uint16_t* w_router, int T, int E, int H, int k,
-                           int32_t* topk_ids, float* topk_w, int32_t* expert_counts, float* logits, void* stream) {
+                           int32_t* topk_ids, float* topk_w, int32_t* expert_counts, float* logits, void* workspace,
+                           size_t workspace_bytes, void* stream) {
     if (!x || !w_router || !topk_ids || !topk_w || !expert_counts) return MOE_ERR_INVALID_ARG;
     if (bad_tek(T, E, k) || H < 1) return MOE_ERR_INVALID_ARG;
     if (!moe::router_shape_ok(T, E, H)) return MOE_ERR_UNSUPPORTED;
+    // a workspace, when given, must hold the logits of the batch
+    if (workspace && workspace_bytes < (size_t)T * (size_t)E * sizeof(float)) return MOE_ERR_WORKSPACE;
     return hip_status(moe::launch_router_topk(x, w_router, T, E, H, k, topk_ids, topk_w, expert_counts, logits,
+                                              reinterpret_cast<float*>(workspace),
                                               reinterpret_cast<hipStream_t>(stream)));
 }
 
@@ -193,6 +198,32 @@ moe_status moe_grouped_ffn(const uint16_t* x, int wfmt, const void* w_gate, cons
     if (st != MOE_OK) return st;
     return moe_ffn_down(wfmt, w_down, s_down, T, E, k, H, I, fat_threshold, y_sorted, workspace, workspace_bytes,
                         stream);
+}
+
+moe_status moe_route_permute_plan(const float* logits, int T, int E, int k, int H, int I, int wfmt,
+                                  int fat_threshold, int32_t* topk_ids, float* topk_w, int32_t* expert_counts,
+                                  int32_t* expert_offsets, int32_t* sorted_pair, int32_t* pair_to_sorted,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+    if (!logits || !topk_ids || !topk_w || !expert_counts || !expert_offsets || !sorted_pair || !pair_to_sorted)
+        return MOE_ERR_INVALID_ARG;
+    if (fat_threshold < 1) return MOE_ERR_INVALID_ARG;
+    moe::FfnLaunch a;
+    moe_status st = ffn_prepare(a, wfmt, T, E, k, H, I, workspace, workspace_bytes);
+    if (st != MOE_OK) return st;
+    const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    if (T <= moe::FRONT_MAX_T) {
+        const moe::FfnPlanPtrs pp = moe::ffn_plan_ptrs(T, E, k, H, I, wfmt, a.ws);
+        return hip_status(moe::launch_route_permute_plan(logits, T, E, k, fat_threshold, topk_ids, topk_w,
+                                                         expert_counts, expert_offsets, sorted_pair, pair_to_sorted,
+                                                         pp, s));
+    }
+    st = moe_route_topk(logits, T, E, k, topk_ids, topk_w, expert_counts, stream);
+    if (st == MOE_OK)
+        st = moe_permute(topk_ids, T, E, k, expert_offsets, sorted_pair, pair_to_sorted, workspace, workspace_bytes,
+                         stream);
+    if (st == MOE_OK)
+        st = moe_ffn_plan(expert_offsets, T, E, k, H, I, wfmt, fat_threshold, workspace, workspace_bytes, stream);
+    return st;
 }
 
 moe_status moe_grouped_ffn_noalloc(const uint16_t* x, int wfmt, const void* w_gate, const void* w_up,

@@ -63,23 +63,7 @@ void build_tiles_kernel(const int32_t* __restrict__ offsets, int E, int thr, Ffn
     }
     const int fi = block_inclusive_scan(nf, scratch);
     const int ti = block_inclusive_scan(nt, scratch);
-    // the expert's 32-row tiles are spread evenly over its nf M-tiles, so the
-    // M-tiles of one expert cost the same and walk the weights in step
-    const int rt = (n + 31) >> 5;
-    for (int i = 0; i < nf; ++i) {
-        const int rt0 = i * (rt / nf) + min(i, rt % nf);
-        const int rti = rt / nf + (i < rt % nf ? 1 : 0);
-        MTile m = {};
-        m.e = e; m.row0 = r0 + 32 * rt0; m.rows = min(32 * rti, n - 32 * rt0);
-        m.first = fi - nf; m.count = nf;
-        fat[fi - nf + i] = m;
-    }
-    for (int i = 0; i < nt; ++i) {
-        MTile m = {};
-        m.e = e; m.row0 = r0 + i * THIN_BM; m.rows = min(THIN_BM, n - i * THIN_BM);
-        m.first = ti - nt; m.count = nt;
-        thin[ti - nt + i] = m;
-    }
+    write_expert_tiles(e, r0, n, nf, nt, fi - nf, ti - nt, fat, thin);
     if (e == (int)blockDim.x - 1) {
         hdr->n_fat = fi;
         hdr->n_thin = ti;
@@ -1170,6 +1154,13 @@ hipError_t launch_phase_t(const FfnArgs& fa, const DevInfo& d, bool fat_possible
 }  // namespace
 
 size_t ffn_ws_bytes(int T, int E, int k, int H, int I, int wfmt) { return ffn_layout(T, E, k, H, I, wfmt).total; }
+
+FfnPlanPtrs ffn_plan_ptrs(int T, int E, int k, int H, int I, int wfmt, void* ffn_ws) {
+    const FfnLayout L = ffn_layout(T, E, k, H, I, wfmt);
+    char* ws = reinterpret_cast<char*>(ffn_ws);
+    return {reinterpret_cast<FfnHeader*>(ws + L.hdr), reinterpret_cast<MTile*>(ws + L.fat),
+            reinterpret_cast<MTile*>(ws + L.thin)};
+}
 
 hipError_t launch_ffn_plan(const FfnLaunch& a, hipStream_t s) {
     const FfnLayout L = ffn_layout(a.T, a.E, a.k, a.H, a.I, a.wfmt);

@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "common.h"
 #include "lds_dma.h"
 
 namespace moe {
@@ -89,6 +90,30 @@ __device__ __forceinline__ void fat_item(const MTile* __restrict__ fat, int item
     t = fat[t0.first + m0 + (off - nt * s)];
 }
 
+// The M-tiles of expert e (route list rows [r0, r0 + n)): nf fat tiles from
+// index f0 of the fat list or nt thin (32-row) tiles from index t0 of the
+// thin list.  The expert's 32-row tiles are spread evenly over its nf
+// M-tiles, so the M-tiles of one expert cost the same and walk the weights in
+// step.
+__device__ __forceinline__ void write_expert_tiles(int e, int r0, int n, int nf, int nt, int f0, int t0,
+                                                   MTile* __restrict__ fat, MTile* __restrict__ thin) {
+    const int rt = (n + 31) >> 5;
+    for (int i = 0; i < nf; ++i) {
+        const int rt0 = i * (rt / nf) + min(i, rt % nf);
+        const int rti = rt / nf + (i < rt % nf ? 1 : 0);
+        MTile m = {};
+        m.e = e; m.row0 = r0 + 32 * rt0; m.rows = min(32 * rti, n - 32 * rt0);
+        m.first = f0; m.count = nf;
+        fat[f0 + i] = m;
+    }
+    for (int i = 0; i < nt; ++i) {
+        MTile m = {};
+        m.e = e; m.row0 = r0 + i * THIN_BM; m.rows = min(THIN_BM, n - i * THIN_BM);
+        m.first = t0; m.count = nt;
+        thin[t0 + i] = m;
+    }
+}
+
 // Wait until at most `stages` stages of this wave's loads are outstanding
 // (loads complete in issue order, L load instructions per stage).
 template <int L>
@@ -106,6 +131,20 @@ __device__ __forceinline__ void vm_wait_stages(int stages) {
 constexpr int DMA_BK = 32;                                  // k per LDS stage
 constexpr uint32_t DMA_ROW = DMA_BK * 2;                    // bytes of one row per stage
 constexpr uint32_t DMA_OPER = FAT_BM * DMA_ROW;             // 16 KB: 256 rows of one operand
+
+// Where the FFN part of a workspace keeps its header and tile lists.
+struct FfnPlanPtrs {
+    FfnHeader* hdr;
+    MTile* fat;
+    MTile* thin;
+};
+FfnPlanPtrs ffn_plan_ptrs(int T, int E, int k, int H, int I, int wfmt, void* ffn_ws);
+
+// Route + permute + plan in one block (front.hip), for 1 <= T <= FRONT_MAX_T.
+constexpr int FRONT_MAX_T = 64;
+hipError_t launch_route_permute_plan(const float* logits, int T, int E, int k, int fat_threshold, int32_t* topk_ids,
+                                     float* topk_w, int32_t* counts, int32_t* offsets, int32_t* sorted_pair,
+                                     int32_t* pair_to_sorted, const FfnPlanPtrs& pp, hipStream_t s);
 
 // The bf16 MFMA-tile kernels with two waves per SIMD (fat8.hip): the device's
 // LDS limit is raised for them on first use; `phase` 1 = gate/up, 2 = down.

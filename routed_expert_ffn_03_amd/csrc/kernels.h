@@ -15,7 +15,8 @@ hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* 
 
 bool router_shape_ok(int T, int E, int H);
 hipError_t launch_router_topk(const uint16_t* x, const uint16_t* w_router, int T, int E, int H, int k,
-                              int32_t* topk_ids, float* topk_w, int32_t* counts, float* logits, hipStream_t s);
+                              int32_t* topk_ids, float* topk_w, int32_t* counts, float* logits, float* scratch_logits,
+                              hipStream_t s);
 
 size_t permute_ws_bytes(int T, int E);
 hipError_t launch_permute(const int32_t* ids, int T, int E, int k, int32_t* offsets,

@@ -14,6 +14,7 @@
 #include "common.h"
 #include "kernels.h"
 #include "lds_dma.h"
+#include "route_keys.h"
 
 #include <mutex>
 
@@ -22,58 +23,6 @@ namespace {
 
 constexpr int ROUTE_THREADS = 256;
 constexpr int ROUTE_WAVES = ROUTE_THREADS / WAVE;
-
-__device__ __forceinline__ uint32_t ordered_bits(float v) {
-    if (v == 0.0f) v = 0.0f;                        // -0 -> +0
-    uint32_t u = __float_as_uint(v);
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-__device__ __forceinline__ float from_ordered(uint32_t o) {
-    return __uint_as_float((o & 0x80000000u) ? (o ^ 0x80000000u) : ~o);
-}
-
-// Wave-wide max of a 64-bit key without LDS round trips: four DPP steps give
-// every lane the max of its 16-lane row (lane ^ 1, lane ^ 2, the other quad
-// of its 8 by the half-row mirror, the other 8 by the row mirror), then the
-// row swaps of gfx950 combine rows 0/1 and 2/3, and the two halves.  Called
-// with every lane active.
-template <int CTRL>
-__device__ __forceinline__ uint64_t dpp_max_u64(uint64_t v) {
-    const uint32_t lo = __builtin_amdgcn_update_dpp(0u, (uint32_t)v, CTRL, 0xF, 0xF, false);
-    const uint32_t hi = __builtin_amdgcn_update_dpp(0u, (uint32_t)(v >> 32), CTRL, 0xF, 0xF, false);
-    const uint64_t o = ((uint64_t)hi << 32) | lo;
-    return o > v ? o : v;
-}
-
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-    v = dpp_max_u64<0xB1>(v);                         // quad_perm [1, 0, 3, 2]
-    v = dpp_max_u64<0x4E>(v);                         // quad_perm [2, 3, 0, 1]
-    v = dpp_max_u64<0x141>(v);                        // row_half_mirror
-    v = dpp_max_u64<0x140>(v);                        // row_mirror
-    {
-        // both operands the same register: one result holds rows (0, 0, 2, 2),
-        // the other rows (1, 1, 3, 3)
-        const auto lo = __builtin_amdgcn_permlane16_swap((uint32_t)v, (uint32_t)v, false, false);
-        const auto hi = __builtin_amdgcn_permlane16_swap((uint32_t)(v >> 32), (uint32_t)(v >> 32), false, false);
-        const uint64_t a = ((uint64_t)hi[0] << 32) | lo[0], b = ((uint64_t)hi[1] << 32) | lo[1];
-        v = a > b ? a : b;
-    }
-    {
-        // lower and upper 32 lanes
-        const auto lo = __builtin_amdgcn_permlane32_swap((uint32_t)v, (uint32_t)v, false, false);
-        const auto hi = __builtin_amdgcn_permlane32_swap((uint32_t)(v >> 32), (uint32_t)(v >> 32), false, false);
-        const uint64_t a = ((uint64_t)hi[0] << 32) | lo[0], b = ((uint64_t)hi[1] << 32) | lo[1];
-        v = a > b ? a : b;
-    }
-    return v;
-}
-
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-    return v;
-}
 
 // tokens_per_block tokens per block; waves take tokens round-robin.
 // direct_counts: the grid is one block covering all tokens, so the block
@@ -526,9 +475,12 @@ bool router_shape_ok(int T, int E, int H) {
 }
 
 hipError_t launch_router_topk(const uint16_t* x, const uint16_t* w_router, int T, int E, int H, int k,
-                              int32_t* topk_ids, float* topk_w, int32_t* counts, float* logits, hipStream_t s) {
-    // a few tokens with the logits wanted in memory: the GEMM over E / 32
-    // blocks, then the gate on the stored logits (the same logits and choice)
+                              int32_t* topk_ids, float* topk_w, int32_t* counts, float* logits, float* scratch_logits,
+                              hipStream_t s) {
+    // a few tokens with somewhere to put the logits (the caller's buffer, or
+    // else the caller's workspace): the GEMM over E / 32 blocks, then the
+    // gate on the stored logits (the same logits and choice as on chip)
+    if (!logits && T <= RS_TMAX) logits = scratch_logits;
     if (logits && T <= 16) return router_split_launch<16>(x, w_router, T, E, H, k, topk_ids, topk_w, counts, logits, s);
     if (logits && T <= RS_TMAX)
         return router_split_launch<32>(x, w_router, T, E, H, k, topk_ids, topk_w, counts, logits, s);

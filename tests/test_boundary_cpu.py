@@ -71,9 +71,9 @@ def test_route_rejects(L):
 
 
 def test_router_rejects(L):
-    ok = dict(x=FAKE, w=FAKE, T=64, E=384, H=4096, k=8, ids=FAKE, tw=FAKE, cnt=FAKE, lg=None)
+    ok = dict(x=FAKE, w=FAKE, T=64, E=384, H=4096, k=8, ids=FAKE, tw=FAKE, cnt=FAKE, lg=None, ws=None, wsb=0)
     call = lambda **kw: L.moe_router_topk(*[{**ok, **kw}[n] for n in ("x", "w", "T", "E", "H", "k", "ids", "tw",
-                                                                         "cnt", "lg")], None)
+                                                                         "cnt", "lg", "ws", "wsb")], None)
     for key in ("x", "w", "ids", "tw", "cnt"):
         assert call(**{key: None}) == moe.MOE_ERR_INVALID_ARG, key
     assert call(T=0) == moe.MOE_ERR_INVALID_ARG
@@ -84,6 +84,8 @@ def test_router_rejects(L):
         assert call(E=E, k=2) == moe.MOE_ERR_UNSUPPORTED, E
     assert call(H=4080) == moe.MOE_ERR_UNSUPPORTED                      # not a multiple of 32
     assert call(T=1 << 19, H=4096, k=1) == moe.MOE_ERR_UNSUPPORTED      # x = 4 GiB
+    # a workspace, when given, holds the batch's logits
+    assert call(T=4, ws=FAKE, wsb=4 * 384 * 4 - 1) == moe.MOE_ERR_WORKSPACE
 
 
 def test_permute_rejects(L):
@@ -171,3 +173,21 @@ def test_noalloc_rejects(L):
     big = list(args)
     big[10:15] = [4096, 384, 8, 4096, 2048]
     assert L.moe_grouped_ffn_noalloc(*big) == moe.MOE_ERR_WORKSPACE
+
+
+def test_route_permute_plan_rejects(L):
+    F = FAKE
+    args = [F, 4, 384, 8, 4096, 2048, 0, 32, F, F, F, F, F, F, F, 1 << 40, None]
+    for i in (0, 8, 9, 10, 11, 12, 13):
+        bad = list(args)
+        bad[i] = None
+        assert L.moe_route_permute_plan(*bad) == moe.MOE_ERR_INVALID_ARG, i
+    bad = list(args)
+    bad[7] = 0
+    assert L.moe_route_permute_plan(*bad) == moe.MOE_ERR_INVALID_ARG
+    bad = list(args)
+    bad[15] = 1024                                    # workspace too small
+    assert L.moe_route_permute_plan(*bad) == moe.MOE_ERR_WORKSPACE
+    bad = list(args)
+    bad[6] = 7                                        # unknown weight format
+    assert L.moe_route_permute_plan(*bad) == moe.MOE_ERR_UNSUPPORTED

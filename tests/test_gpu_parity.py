@@ -244,3 +244,50 @@ def test_layer_full_shape(name, n_sample):
     shape = SHAPES[name]
     say(f"[full layer] {name} T={shape.T} wfmt={shape.wfmt}")
     full_layer_case(shape, 0, n_sample)
+
+
+# moe_route_permute_plan against moe_route_topk + moe_permute + moe_ffn_plan
+# and the oracle: the single-block launch (T <= 64) and the sequence above it.
+FRONT_CASES = [(1, 384, 8, "bf16"), (4, 384, 8, "bf16"), (4, 384, 8, "q3"), (13, 16, 2, "bf16"),
+               (64, 384, 8, "bf16"), (65, 384, 8, "bf16"), (64, 1024, 32, "bf16"), (40, 100, 1, "bf16"),
+               (64, 40, 6, "q3")]
+
+
+@pytest.mark.parametrize("T,E,k,wfmt", FRONT_CASES, ids=[f"T{c[0]}_E{c[1]}_k{c[2]}_{c[3]}" for c in FRONT_CASES])
+def test_route_permute_plan(T, E, k, wfmt):
+    shape = LayerShape(f"front_{T}_{E}_{k}", T, 256, 128, E, k, "zipf", wfmt)
+    say(f"[front] T={T} E={E} k={k} {wfmt}")
+    logits, x = routing_inputs(shape, 4)
+    ids_ref, w_ref = oracle.route_topk(logits, k)
+    counts, offsets, sp, p2s = oracle.permute(ids_ref, E)
+    W = layer_weights(shape, 0)
+    dw = to_dev_weights(W)
+    dl = torch.from_numpy(logits).cuda()
+    dx = torch.from_numpy(x.view(np.int16)).cuda()
+    kw = dict(s_gate=dw.get("gate_scale"), s_up=dw.get("up_scale"), fat_threshold=8, wfmt=wfmt_id(shape))
+    outs = []
+    for fused in (False, True):
+        b = moe.MoELayerBuffers(T, E, k, shape.H, shape.I, wfmt_id(shape))
+        for t in (b.topk_ids, b.expert_counts, b.expert_offsets, b.sorted_pair, b.pair_to_sorted):
+            t.fill_(-7)
+        if fused:
+            moe.moe_route_permute_plan(dl, k, shape.H, shape.I, b.topk_ids, b.topk_w, b.expert_counts,
+                                       b.expert_offsets, b.sorted_pair, b.pair_to_sorted, b.workspace,
+                                       fat_threshold=8, wfmt=wfmt_id(shape))
+        else:
+            moe.moe_route_topk(dl, k, b.topk_ids, b.topk_w, b.expert_counts)
+            moe.moe_permute(b.topk_ids, E, b.expert_offsets, b.sorted_pair, b.pair_to_sorted, b.workspace)
+            moe.moe_ffn_plan(b.expert_offsets, T, k, shape.H, shape.I, b.workspace, fat_threshold=8,
+                             wfmt=wfmt_id(shape))
+        moe.moe_ffn_gate_up(dx, dw["gate"], dw["up"], b.sorted_pair, E, k, b.workspace, **kw)
+        moe.moe_ffn_down(dw["down"], T, E, k, shape.I, b.y_sorted, b.workspace, s_down=dw.get("down_scale"),
+                         fat_threshold=8, wfmt=wfmt_id(shape))
+        torch.cuda.synchronize()
+        got = {"ids": b.topk_ids.cpu().numpy(), "w": b.topk_w.cpu().numpy(), "counts": b.expert_counts.cpu().numpy(),
+               "offsets": b.expert_offsets.cpu().numpy(), "sorted_pair": b.sorted_pair.cpu().numpy(),
+               "pair_to_sorted": b.pair_to_sorted.cpu().numpy()}
+        check_indices(got, dict(ids=ids_ref, w=w_ref, counts=counts, offsets=offsets, sorted_pair=sp,
+                                pair_to_sorted=p2s))
+        outs.append((b.topk_w.clone(), b.y_sorted.clone()))
+    # same gate weights and the same FFN result (the plan is the same) bit for bit
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])

@@ -67,11 +67,17 @@ def test_router_topk(T, E, H, k):
     np.testing.assert_allclose(got_w, ref_w, rtol=0, atol=TOL_W)
     assert np.array_equal(got_c, oracle.expert_histogram(ref_ids, E))
 
-    # fused: no logits output, same choice
+    # fused: no logits output, same choice; then with only a workspace (at
+    # most 32 tokens: the split GEMM writes its logits there), same choice
     ids2, tw2, cnt2 = torch.empty_like(ids), torch.empty_like(tw), torch.empty_like(cnt)
     moe.moe_router_topk(dx, dw, k, ids2, tw2, cnt2)
     torch.cuda.synchronize()
     assert torch.equal(ids2, ids) and torch.equal(tw2, tw) and torch.equal(cnt2, cnt)
+    ws = torch.empty(T * E * 4, dtype=torch.uint8, device="cuda")
+    ids3, tw3, cnt3 = torch.empty_like(ids), torch.empty_like(tw), torch.full_like(cnt, 77)
+    moe.moe_router_topk(dx, dw, k, ids3, tw3, cnt3, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(ids3, ids) and torch.equal(tw3, tw) and torch.equal(cnt3, cnt)
 
     # validity against float64: a selected logit is not below an unselected one by more than the bounds
     sel = np.take_along_axis(ref_l, got_ids.astype(np.int64), axis=1)
