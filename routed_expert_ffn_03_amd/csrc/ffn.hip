@@ -589,42 +589,6 @@ void ffn_fat_kernel(FfnArgs a) {
     }
 }
 
-// ------------------------------------------------------------ 3-bit pair slots
-//
-// The gate/up thin path for tiles of at most 16 rows feeds the MFMA with the
-// 3-bit codes themselves: the bf16 number 128 + u (bits 0x4300 | u) is exact,
-// and two of them come out of one packed 16-bit shift and one and-or when the
-// pair is fields i and i + 5 of a word (bits 3i and 3i + 15).  Slot 2P and
-// 2P + 1 of a 128-group hold pair P: fields 10w + i and 10w + i + 5 for
-// P = 5w + i < 60, fields 120 + i and 125 + i for P = 60 + i < 63, and fields
-// 123, 124 for P = 63.  The activations are stored in the same slot order
-// (the MFMA sums over k in any order), and
-//   sum_k x_k (u_k - 4) = sum_k x_k (128 + u_k) - 132 sum_k x_k,
-// the last term through one more MFMA step against the group sum of x.
-__host__ __device__ constexpr int pair_field(int slot) {
-    const int P = slot >> 1, hi = slot & 1;
-    if (P == 63) return 123 + hi;
-    const int a = P < 60 ? 10 * (P / 5) + P % 5 : 120 + (P - 60);
-    return a + 5 * hi;
-}
-
-typedef __attribute__((ext_vector_type(2))) unsigned short u16x2;
-
-// bf16 pair (128 + u_a, 128 + u_b) of pair P from the group's 13 words;
-// `magic` holds 0x43004300 in a VGPR, so the mask and the or are one
-// v_and_or_b32 (a VOP3 instruction reads at most one SGPR or constant here)
-template <int P>
-__device__ __forceinline__ uint32_t magic_pair(const uint32_t (&w)[Q3_WORDS], uint32_t magic) {
-    if constexpr (P == 63) {
-        return ((w[12] >> 9) & 7u) | (((w[12] >> 12) & 7u) << 16) | magic;
-    } else {
-        constexpr int W = P < 60 ? P / 5 : 12, I = P < 60 ? P % 5 : P - 60;
-        const u16x2 v = __builtin_bit_cast(u16x2, w[W] << 1);
-        const u16x2 sh = {(unsigned short)(3 * I + 1), (unsigned short)(3 * I)};
-        return (__builtin_bit_cast(uint32_t, v >> sh) & 0x00070007u) | magic;
-    }
-}
-
 typedef __attribute__((ext_vector_type(4), aligned(4))) uint32_t u32x4a4;   // 4-byte aligned 16-byte load
 
 // For every token of a thin tile of at most 16 rows: its x row in pair-slot
@@ -642,33 +606,7 @@ void q3_xprep_kernel(FfnArgs a) {
         const MTile t = a.thin[mt];
         if (t.rows > 16 || m >= t.rows) continue;
         const size_t tok = (size_t)(a.sorted_pair[t.row0 + m] / a.k);
-        const u32x4* src = reinterpret_cast<const u32x4*>(a.x + tok * a.H + (size_t)G * 128);
-        u32x4* dst = reinterpret_cast<u32x4*>(a.xq + tok * a.H + (size_t)G * 128);
-        uint32_t v[64];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const u32x4 q = src[i];
-#pragma unroll
-            for (int j = 0; j < 4; ++j) v[4 * i + j] = q[j];
-        }
-        auto half = [&](int f) -> uint32_t { return (v[f >> 1] >> (16 * (f & 1))) & 0xFFFFu; };
-        double sum = 0.0;
-#pragma unroll
-        for (int f = 0; f < 128; ++f) sum += (double)__uint_as_float(half(f) << 16);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            u32x4 o;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int d = 4 * i + j;
-                o[j] = half(pair_field(2 * d)) | (half(pair_field(2 * d + 1)) << 16);
-            }
-            dst[i] = o;
-        }
-        const __bf16 hi = (__bf16)(float)sum;
-        const __bf16 lo = (__bf16)(float)(sum - (double)(float)hi);
-        a.xs[tok * NG + G] = (uint32_t)__builtin_bit_cast(uint16_t, hi) |
-                             ((uint32_t)__builtin_bit_cast(uint16_t, lo) << 16);
+        q3_prep_group(a.x + tok * a.H + (size_t)G * 128, a.xq + tok * a.H + (size_t)G * 128, a.xs + tok * NG + G);
     }
 }
 
@@ -1109,7 +1047,7 @@ FfnArgs make_args(const FfnLaunch& a) {
     fa.wg = a.wg; fa.wu = a.wu; fa.wd = a.wd;
     fa.sg = a.sg; fa.su = a.su; fa.sd = a.sd;
     fa.sorted_pair = a.sorted_pair;
-    fa.T = a.T; fa.k = a.k; fa.H = a.H; fa.I = a.I;
+    fa.T = a.T; fa.k = a.k; fa.H = a.H; fa.I = a.I; fa.E = a.E;
     fa.act = reinterpret_cast<uint16_t*>(ws + L.act);
     fa.xq = a.wfmt == 1 ? reinterpret_cast<uint16_t*>(ws + L.xq) : nullptr;
     fa.xs = a.wfmt == 1 ? reinterpret_cast<uint32_t*>(ws + L.xs) : nullptr;
@@ -1138,7 +1076,11 @@ hipError_t launch_phase_t(const FfnArgs& fa, const DevInfo& d, bool fat_possible
         }
     }
     if constexpr (WFMT != 0) {
-        if constexpr (PHASE == 1) q3_xprep_kernel<<<d.cus, 256, 0, s>>>(fa);
+        if constexpr (PHASE == 1) {
+            // decode batches: every tile thin and every token's x row in LDS (q3dec.hip)
+            if (q3dec_fits(fa.T, fa.E, fa.k, fa.H)) return launch_q3dec_gate_up(fa, d.cus, s);
+            q3_xprep_kernel<<<d.cus, 256, 0, s>>>(fa);
+        }
         ffn_thin_q3_kernel<PHASE><<<d.cus * d.thin_blocks[1][PHASE - 1][0], THIN_THREADS, 0, s>>>(fa);
     } else {
         // whole 128-byte lines per row when each wave's quarter of K is a multiple of 64

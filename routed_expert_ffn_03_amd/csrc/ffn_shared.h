@@ -48,7 +48,7 @@ struct FfnArgs {
     const uint16_t* su;
     const uint16_t* sd;
     const int32_t* sorted_pair;
-    int T, k, H, I;
+    int T, k, H, I, E;
     uint16_t* act;
     uint16_t* y;
     uint16_t* xq;                 // 3-bit thin path: x rows in pair-slot order per 128-group
@@ -132,6 +132,75 @@ constexpr int DMA_BK = 32;                                  // k per LDS stage
 constexpr uint32_t DMA_ROW = DMA_BK * 2;                    // bytes of one row per stage
 constexpr uint32_t DMA_OPER = FAT_BM * DMA_ROW;             // 16 KB: 256 rows of one operand
 
+// ------------------------------------------------------------ 3-bit pair slots
+//
+// The gate/up thin path for tiles of at most 16 rows feeds the MFMA with the
+// 3-bit codes themselves: the bf16 number 128 + u (bits 0x4300 | u) is exact,
+// and two of them come out of one packed 16-bit shift and one and-or when the
+// pair is fields i and i + 5 of a word (bits 3i and 3i + 15).  Slot 2P and
+// 2P + 1 of a 128-group hold pair P: fields 10w + i and 10w + i + 5 for
+// P = 5w + i < 60, fields 120 + i and 125 + i for P = 60 + i < 63, and fields
+// 123, 124 for P = 63.  The activations are stored in the same slot order
+// (the MFMA sums over k in any order), and
+//   sum_k x_k (u_k - 4) = sum_k x_k (128 + u_k) - 132 sum_k x_k,
+// the last term through one more MFMA step against the group sum of x.
+__host__ __device__ constexpr int pair_field(int slot) {
+    const int P = slot >> 1, hi = slot & 1;
+    if (P == 63) return 123 + hi;
+    const int a = P < 60 ? 10 * (P / 5) + P % 5 : 120 + (P - 60);
+    return a + 5 * hi;
+}
+
+typedef __attribute__((ext_vector_type(2))) unsigned short u16x2;
+
+// bf16 pair (128 + u_a, 128 + u_b) of pair P from the group's 13 words;
+// `magic` holds 0x43004300 in a VGPR, so the mask and the or are one
+// v_and_or_b32 (a VOP3 instruction reads at most one SGPR or constant here)
+template <int P>
+__device__ __forceinline__ uint32_t magic_pair(const uint32_t (&w)[Q3_WORDS], uint32_t magic) {
+    if constexpr (P == 63) {
+        return ((w[12] >> 9) & 7u) | (((w[12] >> 12) & 7u) << 16) | magic;
+    } else {
+        constexpr int W = P < 60 ? P / 5 : 12, I = P < 60 ? P % 5 : P - 60;
+        const u16x2 v = __builtin_bit_cast(u16x2, w[W] << 1);
+        const u16x2 sh = {(unsigned short)(3 * I + 1), (unsigned short)(3 * I)};
+        return (__builtin_bit_cast(uint32_t, v >> sh) & 0x00070007u) | magic;
+    }
+}
+
+
+// One 128-group of a token's x row in pair-slot order (dst) and the group's
+// sum of x, summed in fp64 and stored as a bf16 hi, lo pair (sum_dst).  src
+// and dst may be global or LDS; both 16-byte aligned.
+__device__ __forceinline__ void q3_prep_group(const uint16_t* src16, uint16_t* dst16, uint32_t* sum_dst) {
+    const u32x4* src = reinterpret_cast<const u32x4*>(src16);
+    u32x4* dst = reinterpret_cast<u32x4*>(dst16);
+    uint32_t v[64];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const u32x4 q = src[i];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[4 * i + j] = q[j];
+    }
+    auto half = [&](int f) -> uint32_t { return (v[f >> 1] >> (16 * (f & 1))) & 0xFFFFu; };
+    double sum = 0.0;
+#pragma unroll
+    for (int f = 0; f < 128; ++f) sum += (double)__uint_as_float(half(f) << 16);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        u32x4 o;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int d = 4 * i + j;
+            o[j] = half(pair_field(2 * d)) | (half(pair_field(2 * d + 1)) << 16);
+        }
+        dst[i] = o;
+    }
+    const __bf16 hi = (__bf16)(float)sum;
+    const __bf16 lo = (__bf16)(float)(sum - (double)(float)hi);
+    *sum_dst = (uint32_t)__builtin_bit_cast(uint16_t, hi) | ((uint32_t)__builtin_bit_cast(uint16_t, lo) << 16);
+}
+
 // Where the FFN part of a workspace keeps its header and tile lists.
 struct FfnPlanPtrs {
     FfnHeader* hdr;
@@ -139,6 +208,13 @@ struct FfnPlanPtrs {
     MTile* thin;
 };
 FfnPlanPtrs ffn_plan_ptrs(int T, int E, int k, int H, int I, int wfmt, void* ffn_ws);
+
+// The 3-bit gate/up streaming kernel for decode batches (q3dec.hip): every
+// tile thin, at most Q3DEC_MAX_T tokens whose x rows fit in LDS.  Returns
+// false (and launches nothing) for shapes it does not take.
+constexpr int Q3DEC_MAX_T = 14;
+bool q3dec_fits(int T, int E, int k, int H);
+hipError_t launch_q3dec_gate_up(const FfnArgs& fa, int cus, hipStream_t s);
 
 // Route + permute + plan in one block (front.hip), for 1 <= T <= FRONT_MAX_T.
 constexpr int FRONT_MAX_T = 64;

@@ -291,3 +291,15 @@ def test_route_permute_plan(T, E, k, wfmt):
         outs.append((b.topk_w.clone(), b.y_sorted.clone()))
     # same gate weights and the same FFN result (the plan is the same) bit for bit
     assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+
+
+# The 3-bit gate/up kernel for decode batches keeps every token's x row in
+# LDS (up to 14 tokens at hidden 4096); larger batches take the streaming
+# kernel.  Both sides of that limit, every output compared.
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("T", [1, 2, 7, 14, 15])
+def test_decode_q3_batch_sizes(T):
+    base = SHAPES["decode_q3"]
+    shape = LayerShape(f"decode_q3_T{T}", T, base.H, base.I, base.E, base.k, base.router, base.wfmt)
+    say(f"[full layer] {shape.name} T={T} wfmt=q3")
+    full_layer_case(shape, 0, T)
