@@ -11,31 +11,36 @@
 // expert is this library's reading; the pages do not give it.
 //
 // Schedule (all on the caller's stream, counts known only on the device):
-//   build_tiles   one block: per-expert row counts -> 128-row "fat" M-tiles for
-//                 experts with >= fat_threshold rows, 32-row "thin" M-tiles
-//                 for the rest; tile lists + totals into the workspace.
+//   build_tiles   one block: per-expert row counts -> "fat" M-tiles of up to
+//                 256 rows (equal multiples of 32) for experts with at least
+//                 fat_threshold rows, 32-row "thin" M-tiles for the rest; tile
+//                 lists + totals into the workspace (front.hip does the same
+//                 inside its single-block route + permute + plan launch).
 //   phase 1       gate/up: fat kernel, then thin kernel; SwiGLU fused in the
 //                 epilogue; the activation a is stored fp16 [P, I].
 //   phase 2       down: fat kernel, then thin kernel; y stored fp16 [P, H].
 //
-// Fat kernels (MFMA-bound at large M): persistent, one 256-thread block per
-// CU, 256-row M-tiles x 256 weight rows (phase 1: 128 gate rows + the
-// matching 128 up rows, so every wave applies SwiGLU to its own
-// accumulators), 4 waves of 128 x 128 (4 x 4 MFMA 32x32x16 tiles).  bf16
-// weights stream into LDS with direct-to-LDS buffer loads; 3-bit weights are
-// decoded on the way through registers.  Work items of one expert are walked
-// in super-tiles and 32 consecutive items run on one XCD, so tiles that share
-// activation rows or weights share that XCD's L2.
+// Fat kernels (MFMA-bound at large M): persistent, one block per CU, 256-row
+// M-tiles x 256 weight rows (phase 1: 128 gate rows + the matching 128 up
+// rows, so SwiGLU is applied to accumulators in registers), operands staged
+// in LDS by direct-to-LDS buffer loads.  bf16 weights: fat8.hip (eight waves,
+// two per SIMD taking turns between MFMA clusters and operand traffic).  3-bit
+// weights: ffn_fat_kernel below (four waves side by side, the 3-bit words
+// decoded into MFMA operands between the MFMAs).  Work items of one expert
+// are walked so that 32 consecutive items, which run on one XCD, share
+// activation and weight tiles in that XCD's L2.
 //
-// Thin kernel (HBM-bound): persistent, several blocks per CU, work item =
+// Thin kernels (HBM-bound): persistent, several blocks per CU, work item =
 // (32 weight rows, thin M-tile); the four waves split the reduction index and
 // stream weights straight from HBM into MFMA operands (no LDS staging: every
-// weight element is used once), 4 chunks in flight per lane, then reduce the
-// four partial tiles through LDS.  Phase 1 items carry 16 gate + 16 up rows.
+// weight element is used once), then reduce the four partial tiles through
+// LDS.  Phase 1 items carry 16 gate + 16 up rows.  3-bit gate/up for decode
+// batches (every tile thin, at most 14 tokens): q3dec.hip.
 //
 // Precision: fp32 accumulation; a in fp16; the down projection runs on fp16
 // MFMA with W_down converted to fp16 when staged.  3-bit weights are decoded
-// to bf16 (phase 1) or fp16 (phase 2) as they are staged.
+// to bf16 (phase 1) or fp16 (phase 2), or enter the MFMA as exact codes
+// (pair-slot path).
 #include "common.h"
 #include "ffn_shared.h"
 #include "kernels.h"
