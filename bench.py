@@ -12,7 +12,9 @@ its own pair of HIP events on the library's stream, and a 512 MiB scratch
 buffer is read between steps (outside the events) so that no step starts
 with the previous one's weights in the MALL; the line reports the
 mean (value, ms_per_step) and the median, p10 and p90.  The dominant
-kernel's time (the gate/up phase) is taken live the same way.
+kernel's time (the gate/up phase) is taken the same way in a second timed
+run of the same steps (an event between two kernels idles the GPU for a few
+microseconds, so it is kept out of the layer timing).
 
 Prints ONE JSON line.  Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -162,12 +164,16 @@ class Runner:
         m.moe_combine(b.y_sorted, b.topk_w, b.pair_to_sorted, b.out)
 
     def measure(self, steps, warmup, flush=None):
-        """Time `steps` layer calls, each between its own pair of HIP events on
-        the library's stream.  With `flush` (a 512 MiB device buffer) the buffer
-        is read in full before every step, outside the events, so no step finds
-        the previous one's weights in the 256 MB MALL or the L2s.  A read leaves
-        only clean lines behind (a write would leave dirty ones that the timed
-        step would then have to write back)."""
+        """Two timed runs of `steps` layer calls each.  Run 1: each call between
+        its own pair of HIP events on the library's stream (the layer time).
+        Run 2: events around the gate/up phase only (the dominant kernel's
+        time).  An event between two kernels leaves the GPU idle for several
+        microseconds, so the layer is not timed with the phase events inside
+        it.  With `flush` (a 512 MiB device buffer) the buffer is read in full
+        before every call, outside the events, so no call finds the previous
+        one's weights in the 256 MB MALL or the L2s; a read leaves only clean
+        lines behind (a write would leave dirty ones that the timed call would
+        then have to write back)."""
         torch = self.torch
         for _ in range(warmup):
             self.step()
@@ -180,10 +186,15 @@ class Runner:
             if flush is not None:
                 flush.sum()
             layer[i][0].record()
-            self.step(gu[i])
+            self.step()
             layer[i][1].record()
         torch.cuda.synchronize()
         t1 = time.perf_counter()
+        for i in range(steps):
+            if flush is not None:
+                flush.sum()
+            self.step(gu[i])
+        torch.cuda.synchronize()
         return StepTimes([a.elapsed_time(b) for a, b in layer], [a.elapsed_time(b) for a, b in gu],
                          (t1 - t0) * 1e3 / steps)
 
@@ -522,8 +533,9 @@ def main():
         "scaling": "weak", "vs_baseline": None, "dtype": shape.wfmt, "data": "synthetic",
         "config": workload_desc(shape, args.fat_threshold), "roofline": roof,
         "timing": {**st.stats(), "mall_flush_bytes": 0 if flush is None else FLUSH_BYTES,
-                   "method": "HIP events around each layer call on the library's stream; a 512 MiB scratch buffer "
-                             "is read between steps outside the events"},
+                   "method": "HIP events around each layer call on the library's stream (the gate/up phase timed "
+                             "in a second run of the same steps); a 512 MiB scratch buffer is read between "
+                             "steps outside the events"},
     }
     if shape.T <= 64:
         res["layer_roofline"] = run.layer_hbm(ms)

@@ -5,7 +5,7 @@
 // CPU-tier entry.  Reading: the combine is the gate-weighted sum.
 //
 // A gather-sum, not a scatter: every output element is owned by one thread
-// that adds its k terms in ascending j in fp32, so the result is bit-identical
+// that adds its k terms in ascending j in fp32 (one fma each), so the result is bit-identical
 // from run to run (no atomics).  Each thread moves 16-byte fp16 loads and
 // 32-byte fp32 stores; the per-token indices and weights are wave-uniform.
 #include "common.h"
@@ -16,6 +16,7 @@ namespace {
 
 constexpr int CB_THREADS = 128;
 constexpr int CB_COLS = CB_THREADS * 8;     // columns per block
+constexpr int CB_J = 8;                     // rows loaded ahead
 
 __global__ __launch_bounds__(CB_THREADS)
 void combine_kernel(const uint16_t* __restrict__ y, const float* __restrict__ w,
@@ -27,14 +28,28 @@ void combine_kernel(const uint16_t* __restrict__ y, const float* __restrict__ w,
     float acc[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
-    for (int j = 0; j < k; ++j) {
-        const size_t p = (size_t)t * k + j;
-        const float wj = w[p];
-        const size_t row = (size_t)p2s[p];
-        const f16x8 h = __builtin_bit_cast(f16x8, ldg16(y + row * H + col));
+    // CB_J rows at a time, all loaded before the first product so that their
+    // latencies overlap; then the rest one by one
+    const float* wt = w + (size_t)t * k;
+    const int32_t* pt = p2s + (size_t)t * k;
+    auto term = [&](float wj, u32x4 h) {
+        const f16x8 v = __builtin_bit_cast(f16x8, h);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] += wj * (float)h[i];
+        for (int i = 0; i < 8; ++i) acc[i] = fmaf(wj, (float)v[i], acc[i]);
+    };
+    int j0 = 0;
+    for (; j0 + CB_J <= k; j0 += CB_J) {
+        float wj[CB_J];
+        u32x4 h[CB_J];
+#pragma unroll
+        for (int jj = 0; jj < CB_J; ++jj) {
+            wj[jj] = wt[j0 + jj];
+            h[jj] = ldg16(y + (size_t)pt[j0 + jj] * H + col);
+        }
+#pragma unroll
+        for (int jj = 0; jj < CB_J; ++jj) term(wj[jj], h[jj]);
     }
+    for (; j0 < k; ++j0) term(wt[j0], ldg16(y + (size_t)pt[j0] * H + col));
     float* o = out + (size_t)t * H + col;
     u32x4 a, b;
 #pragma unroll

@@ -31,11 +31,14 @@
 // activation and weight tiles in that XCD's L2.
 //
 // Thin kernels (HBM-bound): persistent, several blocks per CU, work item =
-// (32 weight rows, thin M-tile); the four waves split the reduction index and
-// stream weights straight from HBM into MFMA operands (no LDS staging: every
-// weight element is used once), then reduce the four partial tiles through
-// LDS.  Phase 1 items carry 16 gate + 16 up rows.  3-bit gate/up for decode
-// batches (every tile thin, at most 14 tokens): q3dec.hip.
+// (32 weight rows, thin M-tile); the four waves split the reduction index,
+// stream the weights and reduce the four partial tiles through LDS.  Phase 1
+// items carry 16 gate + 16 up rows.  bf16 weights: stream.hip (whole-line
+// non-temporal loads through a per-wave LDS ring); the kernel below, which
+// loads the MFMA operand layout straight into registers, only where a wave's
+// quarter of K is not a multiple of 64.  3-bit: ffn_thin_q3_kernel below, and
+// q3dec.hip for the gate/up of decode batches (every tile thin, at most 14
+// tokens).
 //
 // Precision: fp32 accumulation; a in fp16; the down projection runs on fp16
 // MFMA with W_down converted to fp16 when staged.  3-bit weights are decoded
@@ -617,38 +620,10 @@ void q3_xprep_kernel(FfnArgs a) {
 
 // ------------------------------------------------------------ thin kernels
 
-// The four waves' partial 32 x 32 tiles of one thin item are summed through
-// LDS; wave 0 stores the result: phase 1 silu(gate) * up for the 16 gate
-// columns (the up partner sits 16 lanes over), phase 2 the 32 y columns.
-template <int PHASE>
-__device__ __forceinline__ void thin_reduce_store(const FfnArgs& a, const f32x16& acc, const MTile& t, int nt,
-                                                  float (&red)[4][16][64], int wave, int lane) {
-    const int m = lane & 31, g = lane >> 5;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) red[wave][r][lane] = acc[r];
-    __syncthreads();
-    if (wave == 0) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const float v = red[0][r][lane] + red[1][r][lane] + red[2][r][lane] + red[3][r][lane];
-            const int row = 8 * (r >> 2) + 4 * g + (r & 3);
-            if (PHASE == 1) {
-                const float u = __shfl(v, (lane + 16) & 63, 64);
-                if (m < 16 && row < t.rows)
-                    a.act[(size_t)(t.row0 + row) * a.I + nt * 16 + m] = f32_to_f16_bits(silu_mul(v, u));
-            } else {
-                if (row < t.rows) a.y[(size_t)(t.row0 + row) * a.H + nt * 32 + m] = f32_to_f16_bits(v);
-            }
-        }
-    }
-    __syncthreads();
-}
-
 // CW: 16-byte pieces per lane and row per chunk; lane half g covers 8*CW
-// consecutive k of a 16*CW-wide chunk, so with CW = 4 every row is read in
-// whole 128-byte lines.  D: chunks in the register ring (D - 1 in flight);
-// with CW = 4 one chunk ahead keeps the kernel at 3 waves per SIMD, which
-// streams faster at decode than two chunks ahead at 2 waves.
+// consecutive k of a 16*CW-wide chunk.  D: chunks in the register ring (D - 1
+// in flight).  Used with CW = 2 (any K that is a multiple of 128); K a
+// multiple of 256 goes to the streaming kernel of stream.hip instead.
 template <int PHASE, int CW>
 __global__ __launch_bounds__(THIN_THREADS)
 void ffn_thin_kernel(FfnArgs a) {
@@ -1033,9 +1008,9 @@ hipError_t dev_info(DevInfo& out) {
             if (err != hipSuccess) return err;
         }
         d.thin_blocks[0][0][0] = occupancy_of((const void*)ffn_thin_kernel<1, 2>);
-        d.thin_blocks[0][0][1] = occupancy_of((const void*)ffn_thin_kernel<1, 4>);
+        d.thin_blocks[0][0][1] = stream_occupancy(1);
         d.thin_blocks[0][1][0] = occupancy_of((const void*)ffn_thin_kernel<2, 2>);
-        d.thin_blocks[0][1][1] = occupancy_of((const void*)ffn_thin_kernel<2, 4>);
+        d.thin_blocks[0][1][1] = stream_occupancy(2);
         d.thin_blocks[1][0][0] = d.thin_blocks[1][0][1] = occupancy_of((const void*)ffn_thin_q3_kernel<1>);
         d.thin_blocks[1][1][0] = d.thin_blocks[1][1][1] = occupancy_of((const void*)ffn_thin_q3_kernel<2>);
         d.cus = cus;
@@ -1088,12 +1063,11 @@ hipError_t launch_phase_t(const FfnArgs& fa, const DevInfo& d, bool fat_possible
         }
         ffn_thin_q3_kernel<PHASE><<<d.cus * d.thin_blocks[1][PHASE - 1][0], THIN_THREADS, 0, s>>>(fa);
     } else {
-        // whole 128-byte lines per row when each wave's quarter of K is a multiple of 64
-        const int K = PHASE == 1 ? fa.H : fa.I;
-        if ((K / 4) % 64 == 0)
-            ffn_thin_kernel<PHASE, 4><<<d.cus * d.thin_blocks[0][PHASE - 1][1], THIN_THREADS, 0, s>>>(fa);
-        else
-            ffn_thin_kernel<PHASE, 2><<<d.cus * d.thin_blocks[0][PHASE - 1][0], THIN_THREADS, 0, s>>>(fa);
+        // weights through LDS in whole lines (stream.hip) when each wave's
+        // quarter of K is a multiple of 64; else straight into registers
+        if (stream_fits(PHASE, fa.T, fa.k, fa.H, fa.I))
+            return launch_stream_phase(fa, PHASE, d.cus * d.thin_blocks[0][PHASE - 1][1], s);
+        ffn_thin_kernel<PHASE, 2><<<d.cus * d.thin_blocks[0][PHASE - 1][0], THIN_THREADS, 0, s>>>(fa);
     }
     return hipGetLastError();
 }

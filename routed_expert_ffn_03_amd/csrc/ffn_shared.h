@@ -114,6 +114,39 @@ __device__ __forceinline__ void write_expert_tiles(int e, int r0, int n, int nf,
     }
 }
 
+// The four waves' partial 32 x 32 tiles of one thin item are summed through
+// LDS; wave 0 stores the result (the barriers wait for LDS traffic only,
+// so loads of later work issued before them stay in flight): phase 1 silu(gate) * up for the 16 gate
+// columns (the up partner sits 16 lanes over), phase 2 the 32 y columns.
+template <int PHASE>
+__device__ __forceinline__ void thin_reduce_store(const FfnArgs& a, const f32x16& acc, const MTile& t, int nt,
+                                                  float (&red)[4][16][64], int wave, int lane) {
+    const int m = lane & 31, g = lane >> 5;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) red[wave][r][lane] = acc[r];
+    lds_barrier();
+    if (wave == 0) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const float v = red[0][r][lane] + red[1][r][lane] + red[2][r][lane] + red[3][r][lane];
+            const int row = 8 * (r >> 2) + 4 * g + (r & 3);
+            if (PHASE == 1) {
+                const float u = __shfl(v, (lane + 16) & 63, 64);
+                if (m < 16 && row < t.rows)
+                    a.act[(size_t)(t.row0 + row) * a.I + nt * 16 + m] = f32_to_f16_bits(silu_mul(v, u));
+            } else {
+                if (row < t.rows) a.y[(size_t)(t.row0 + row) * a.H + nt * 32 + m] = f32_to_f16_bits(v);
+            }
+        }
+    }
+    lds_barrier();
+}
+
+// bf16 thin phases with the weights streamed through LDS (stream.hip)
+bool stream_fits(int phase, int T, int k, int H, int I);
+hipError_t launch_stream_phase(const FfnArgs& fa, int phase, int blocks, hipStream_t s);
+int stream_occupancy(int phase);
+
 // Wait until at most `stages` stages of this wave's loads are outstanding
 // (loads complete in issue order, L load instructions per stage).
 template <int L>

@@ -50,6 +50,12 @@ __device__ __forceinline__ uint32_t ds_read4(uint32_t addr) {
 __device__ __forceinline__ void lds_wait_all() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 __device__ __forceinline__ void tie_after_wait(u32x4& v) { asm volatile("" : "+v"(v)); }
+__device__ __forceinline__ void tie_after_wait(uint32_t& v) { asm volatile("" : "+v"(v)); }
+
+// Workgroup barrier for data exchanged through LDS only: waits for this
+// wave's LDS (and scalar) traffic, not for its vector memory loads, which
+// __syncthreads() would also drain when direct-to-LDS loads are in flight.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 template <int N>
 __device__ __forceinline__ void vm_wait() {

@@ -7,6 +7,9 @@ cross-compiles, nothing runs on a GPU).
    complete at once; a register copy placed before the wait would hold stale
    data and give wrong results only on some paths).
 2. The fat kernels' K-loops (the innermost loops) spill nothing to scratch.
+3. The streaming kernel's chunk loop never waits for all of its loads
+   (``s_waitcnt vmcnt(0)``): the next chunk's weights stay in flight while
+   the current one is multiplied, across items too.
 
 The checker itself is pinned on hand-written snippets with and without such
 a hazard.
@@ -23,7 +26,7 @@ from tests.asm_check import kernel_bodies, stale_lds_uses
 from routed_expert_ffn_03_amd.build import BUILD, CSRC, HIPCC_FLAGS
 
 # sources compiled to assembly, and every file their hash covers
-UNITS = ["ffn.hip", "fat8.hip", "route.hip"]
+UNITS = ["ffn.hip", "fat8.hip", "stream.hip", "route.hip"]
 SOURCES = UNITS + ["common.h", "kernels.h", "lds_dma.h", "ffn_shared.h"]
 
 
@@ -102,6 +105,7 @@ def test_no_lds_result_used_before_its_wait(ffn_asm):
     kernels = {k: v for k, v in kernel_bodies(ffn_asm).items() if "ffn_" in k or "router_" in k}
     assert any("ffn_fat_kernel" in k for k in kernels) and any("router_topk_kernel" in k for k in kernels)
     assert any("ffn_fat8_kernel" in k for k in kernels)
+    assert any("ffn_stream_kernel" in k for k in kernels)
     assert any("router_logits_split_kernel" in k for k in kernels)
     bad = {}
     for name, lines in kernels.items():
@@ -117,7 +121,9 @@ def _loops(lines):
     out = []
     for i, l in enumerate(lines):
         if "Inner Loop Header" in l and i > 0:
-            lab = lines[i - 1].split(":")[0].strip()
+            # the header label sits on the comment's line or on the one before
+            own = l.split(":")[0].strip()
+            lab = own if own.startswith(".LBB") else lines[i - 1].split(":")[0].strip()
             if not lab.startswith(".LBB"):
                 continue
             tag = "Header=" + lab[2:] + " "
@@ -140,3 +146,55 @@ def test_fat_k_loops_do_not_spill(ffn_asm):
             spills = [x.strip() for x in body if "scratch_" in x]
             assert not spills, (name, lab, spills[:3])
     assert checked > 0
+
+
+def _loop_blocks(lines):
+    """(label, lines) of every loop as the union of its basic blocks: the
+    header and every block tagged as inside it (the back edge may fall
+    through, so the loop need not end in a branch to its header)."""
+    starts = [i for i, x in enumerate(lines) if re.match(r"^(\.LBB\w+:|; %bb\.\d+:)", x.strip())]
+    blocks = [(i, (starts[n + 1] if n + 1 < len(starts) else len(lines))) for n, i in enumerate(starts)]
+    out = []
+    for i, _ in blocks:
+        if "Inner Loop Header" not in lines[i]:
+            continue
+        lab = lines[i].split(":")[0].strip()
+        tag = "Header=" + lab[2:] + " "
+        body = []
+        for b0, b1 in blocks:
+            if b0 == i or tag in lines[b0]:
+                body += lines[b0:b1]
+        out.append((lab, body))
+    return out
+
+
+def test_stream_loop_keeps_loads_in_flight(ffn_asm):
+    kernels = {k: v for k, v in kernel_bodies(ffn_asm).items() if "ffn_stream_kernel" in k}
+    assert len(kernels) == 2
+    for name, lines in kernels.items():
+        loops = [(lab, body) for lab, body in _loop_blocks(lines) if any("v_mfma" in x for x in body)]
+        assert len(loops) == 1, (name, [lab for lab, _ in loops])
+        body = loops[0][1]
+        assert sum(" lds" in x and "buffer_load_dwordx4" in x for x in body) >= 4
+        drains = [x.strip() for x in body if re.search(r"s_waitcnt\s+vmcnt\(0\)", x)]
+        assert not drains, (name, drains)
+        assert not [x for x in body if "scratch_" in x], name
+
+
+def test_loop_blocks_follow_fall_through_back_edges():
+    lines = """
+.LBB0_1:                                ;   in Loop: Header=BB0_2 Depth=1
+    s_mov_b32 s1, s2
+    s_waitcnt vmcnt(0)
+    s_cbranch_vccnz .LBB0_9
+.LBB0_2:                                ; =>This Inner Loop Header: Depth=1
+    buffer_load_dwordx4 v1, s[4:7], s8 offen nt lds
+    v_mfma_f32_32x32x16_bf16 a[0:15], v[0:3], v[4:7], a[0:15]
+    s_cbranch_scc1 .LBB0_1
+.LBB0_9:
+    s_endpgm
+""".split("\n")
+    loops = _loop_blocks(lines)
+    assert [lab for lab, _ in loops] == [".LBB0_2"]
+    body = loops[0][1]
+    assert any("vmcnt(0)" in x for x in body) and not any("s_endpgm" in x for x in body)
