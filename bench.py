@@ -34,13 +34,20 @@ METRIC = "MoE-layer tokens/s at 16k-token prefill and 4-token decode; % MFMA/HBM
 PEAK_MFMA_TFLOPS = {"bf16": 2500.0, "fp16": 2500.0}      # dense, MI355X published
 PEAK_HBM_GBS = 8000.0
 FLUSH_BYTES = 512 << 20                                   # > the 256 MB MALL
-FAT_GATE_UP_NAME = "ffn_fat_kernel<1, 0, 5>"
+# gate/up phase kernels (template argument: the phase)
+GATE_UP_KERNELS = {"bf16": ("ffn_fat8_kernel<1>", "ffn_stream_kernel<1>"),
+                   "q3": ("ffn_fat_kernel<1, 1, 6>", "ffn_thin_q3_kernel<1> or, at decode, ffn_q3_decode_kernel")}
+# the sources of the expert-FFN kernels; their hash keys the counter figures in profiles/hbm_traffic.md
+FFN_SOURCES = ("ffn.hip", "fat8.hip", "stream.hip", "q3dec.hip", "ffn_shared.h", "lds_dma.h", "common.h")
 
 
 def ffn_source_hash() -> str:
     import hashlib
-    src = os.path.join(ROOT, "routed_expert_ffn_03_amd", "csrc", "ffn.hip")
-    return hashlib.sha256(open(src, "rb").read()).hexdigest()[:12]
+    h = hashlib.sha256()
+    for name in FFN_SOURCES:
+        with open(os.path.join(ROOT, "routed_expert_ffn_03_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:12]
 
 
 def measured_traffic(workload: str):
@@ -223,11 +230,10 @@ class Runner:
             per = f"{per_expert} gate+up weight bytes per touched expert x {touched} experts"
         r["frac"] = r["achieved"] / r["peak"]
         r["traffic"] = measured_traffic(s.name)
-        r["traffic_source"] = ("rocprofv3 FETCH_SIZE + WRITE_SIZE of this kernel source, profiles/hbm_traffic.md"
-                               if r["traffic"] is not None else "not measured for this kernel source")
-        # fat kernel template arguments: <phase, weight format, LDS ring stages>
-        fat_name = FAT_GATE_UP_NAME if s.wfmt == "bf16" else "ffn_fat_kernel<1, 1, 6>"
-        thin_name = "ffn_thin_kernel<1, 4>" if s.wfmt == "bf16" else "ffn_thin_q3_kernel<1>"
+        r["traffic_source"] = ("rocprofv3 FETCH_SIZE + WRITE_SIZE of these kernel sources "
+                               f"(sha256[:12] {ffn_source_hash()}), profiles/hbm_traffic.md"
+                               if r["traffic"] is not None else "not measured for these kernel sources")
+        fat_name, thin_name = GATE_UP_KERNELS[s.wfmt]
         r["kernel"] = f"gate/up phase ({fat_name} + {thin_name})"
         r["kernel_ms"] = gate_up_ms
         r["algorithmic"] = per
