@@ -183,7 +183,9 @@ void router_topk_kernel(const uint16_t* __restrict__ x, const uint16_t* __restri
             case 2: vm_wait<2 * LW>(); break;
             default: vm_wait<3 * LW>(); break;
         }
-        __syncthreads();                                          // ... and every wave's
+        // (LDS-only barriers: __syncthreads() would also wait for the later
+        // stages' loads, draining the ring every stage)
+        lds_barrier();                                            // ... and every wave's
         const uint32_t st = sbase + slot * SB;
         u32x4 af[2][2], bf[2][CT];
 #pragma unroll
@@ -209,7 +211,7 @@ void router_topk_kernel(const uint16_t* __restrict__ x, const uint16_t* __restri
             for (int r = 0; r < 2; ++r)
 #pragma unroll
                 for (int c = 0; c < CT; ++c) acc[r][c] = mfma_bf16(af[s][r], bf[s][c], acc[r][c]);
-        __syncthreads();                                          // every wave is done with this slot
+        lds_barrier();                                            // every wave is done with this slot
         if (kt + RNS < KT) issue(kt + RNS, slot);
     }
 
@@ -354,7 +356,7 @@ void router_logits_split_kernel(const uint16_t* __restrict__ x, const uint16_t* 
             case 1: vm_wait<R::LPW>(); break;
             default: vm_wait<2 * R::LPW>(); break;
         }
-        __syncthreads();                                    // ... and every wave's
+        lds_barrier();                                      // ... and every wave's
         if (wave == 0) {
             const uint32_t st = lds_addr(smem) + slot * R::SLOT;
             const uint32_t wb = st + (uint32_t)n * RS_ROW, xb = st + (uint32_t)(32 + (n & (XR - 1))) * RS_ROW;
@@ -401,7 +403,7 @@ void router_logits_split_kernel(const uint16_t* __restrict__ x, const uint16_t* 
                 }
             }
         }
-        __syncthreads();                                    // slot free
+        lds_barrier();                                      // slot free
         if (b + R::NSL < NB) issue(b + R::NSL, slot);
         slot = slot + 1 == R::NSL ? 0 : slot + 1;
     }
