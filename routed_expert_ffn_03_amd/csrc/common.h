@@ -55,6 +55,12 @@ __device__ __forceinline__ u32x4 ldg16(const void* p) {
     return *reinterpret_cast<const u32x4*>(p);
 }
 
+// A 16-byte load with the non-temporal hint, for data read once in whole
+// lines (the wave's 64 lanes cover contiguous lines).
+__device__ __forceinline__ u32x4 ldg16_stream(const void* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
 __device__ __forceinline__ void stg16(void* p, u32x4 v) {
     *reinterpret_cast<u32x4*>(p) = v;
 }
