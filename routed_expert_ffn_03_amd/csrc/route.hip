@@ -116,18 +116,21 @@ void route_launch(const float* logits, int T, int E, int k, int32_t* topk_ids, f
 //
 // Tile: RB = 64 tokens x E experts; the four waves side by side, wave w owning
 // experts [w E/4, (w+1) E/4) as CT = E/128 column tiles of 32 against both
-// 32-token row tiles.  Operands stream through a ring of RNS stages of 32 k
-// (activation rows 64 x 64 B, router rows E x 64 B) filled by direct-to-LDS
-// loads, 64-byte LDS rows with the 16-byte chunk c of row r at c ^ ((r >> 2) & 3).
+// 32-token row tiles.  Operands stream through two LDS slots of 64 k each
+// (activation rows 64 x 128 B, then router rows E x 128 B): direct-to-LDS
+// loads of 8 rows x 128 B, whole lines (the per-CU load path moves about one
+// line per clock whether it is used in full or not, so 64-byte pieces of a
+// 32-k stage cost twice the time per byte); the 16-byte piece c of LDS row r
+// at position c ^ swz(r), swz(r) = (r & 7) ^ ((r >> 3) & 1).  The next slot
+// is in flight while the current one is multiplied.
 constexpr int RB = 64;                    // tokens per block
-constexpr int RNS = 4;                    // ring stages
 constexpr int R_THREADS = 256;
-constexpr uint32_t R_ROW = 64;            // bytes of one row per 32-k stage
+constexpr uint32_t R_ROW = 128;           // bytes of one row per 64-k slot
 
 __host__ __device__ constexpr uint32_t router_stage_bytes(int E) { return (uint32_t)(RB + E) * R_ROW; }
 __host__ __device__ constexpr uint32_t router_lds_bytes(int E) {
-    return router_stage_bytes(E) * RNS > (uint32_t)RB * (E + 8) * 4 ? router_stage_bytes(E) * RNS
-                                                                    : (uint32_t)RB * (E + 8) * 4;
+    return router_stage_bytes(E) * 2 > (uint32_t)RB * (E + 8) * 4 ? router_stage_bytes(E) * 2
+                                                                  : (uint32_t)RB * (E + 8) * 4;
 }
 
 template <int CT>
@@ -136,7 +139,8 @@ void router_topk_kernel(const uint16_t* __restrict__ x, const uint16_t* __restri
                         int32_t* __restrict__ topk_ids, float* __restrict__ topk_w, int32_t* __restrict__ counts,
                         float* __restrict__ logits_out) {
     constexpr int E = 128 * CT;
-    constexpr int LW = 1 + 2 * CT;                       // load instructions per wave per stage
+    constexpr int NO = (RB + E) / 8;                     // 8-row octets per slot
+    constexpr int LW = (NO + 3) / 4;                     // load instructions per wave per slot (at most)
     constexpr uint32_t SB = router_stage_bytes(E);
     constexpr int LD = E + 8;                            // staged logit row (floats): conflict-free stores
     extern __shared__ u32x4 smem[];
@@ -145,26 +149,33 @@ void router_topk_kernel(const uint16_t* __restrict__ x, const uint16_t* __restri
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int n = lane & 31, g = lane >> 5;
     const int t0 = blockIdx.x * RB;
-    const int KT = H / 32;
+    const int KD = (H + 63) / 64;                        // 64-k slots (the last one may hold 32 k)
     for (int e = tid; e < E; e += R_THREADS) hist[e] = 0;
 
     const __amdgpu_buffer_rsrc_t xsrc = make_rsrc(x, (uint32_t)((size_t)T * H * 2));
     const __amdgpu_buffer_rsrc_t wsrc = make_rsrc(wr, (uint32_t)((size_t)E * H * 2));
-    // load roles: instruction q of a wave fills 16 rows (4 lanes per 64-byte row),
-    // the chunk landing at position L % 4 being (L % 4) ^ ((row >> 2) & 3)
-    const uint32_t lch16 = (uint32_t)(((lane & 3) ^ ((lane >> 4) & 3)) * 16);
-    const int xr = min(t0 + 16 * wave + (lane >> 2), T - 1);          // rows past T repeat the last one
-    const uint32_t xoff = (uint32_t)xr * (uint32_t)H * 2u + lch16;
-    uint32_t woff[2 * CT];
+    // wave w moves octets w, w + 4, ...: octet o < 8 is activation rows 8 o ..
+    // (rows past T repeat the last one), the rest router rows 8 (o - 8) ..;
+    // lane L puts row 8 o + L / 8 of the slot at position L % 8, which holds
+    // piece (L % 8) ^ (L / 8) ^ (o & 1)
+    uint32_t loff[LW];
 #pragma unroll
-    for (int q = 0; q < 2 * CT; ++q) woff[q] = (uint32_t)(wave * (E / 4) + 16 * q + (lane >> 2)) * (uint32_t)H * 2u + lch16;
+    for (int j = 0; j < LW; ++j) {
+        const int o = wave + 4 * j;
+        const uint32_t pc = (uint32_t)(((lane & 7) ^ (lane >> 3) ^ (o & 1)) * 16);
+        const int r = 8 * o + (lane >> 3);
+        loff[j] = o < 8 ? (uint32_t)min(t0 + r, T - 1) * (uint32_t)H * 2u + pc
+                        : (uint32_t)(r - RB) * (uint32_t)H * 2u + pc;
+    }
     const uint32_t sbase = lds_addr(smem);
-
-    auto issue = [&](int kt, int slot) {
+    auto issue = [&](int d, int slot) {
         char* st = reinterpret_cast<char*>(smem) + slot * SB;
-        dma16(xsrc, st + wave * 1024, xoff, kt * R_ROW);
+        const uint32_t soff = (uint32_t)d * R_ROW;
 #pragma unroll
-        for (int q = 0; q < 2 * CT; ++q) dma16(wsrc, st + RB * R_ROW + (wave * 2 * CT + q) * 1024, woff[q], kt * R_ROW);
+        for (int j = 0; j < LW; ++j) {
+            const int o = wave + 4 * j;
+            if (o < NO) dma16(o < 8 ? xsrc : wsrc, st + o * 1024, loff[j], soff);
+        }
     };
 
     f32x16 acc[2][CT];
@@ -173,47 +184,44 @@ void router_topk_kernel(const uint16_t* __restrict__ x, const uint16_t* __restri
 #pragma unroll
         for (int c = 0; c < CT; ++c) acc[r][c] = f32x16{};
 
-    const int pro = min(RNS, KT);
-    for (int s = 0; s < pro; ++s) issue(s, s);
-    for (int kt = 0; kt < KT; ++kt) {
-        const int slot = kt % RNS;
-        switch (min(RNS - 1, KT - 1 - kt)) {                      // stage kt landed (this wave's part) ...
-            case 0: vm_wait<0>(); break;
-            case 1: vm_wait<LW>(); break;
-            case 2: vm_wait<2 * LW>(); break;
-            default: vm_wait<3 * LW>(); break;
-        }
-        // (LDS-only barriers: __syncthreads() would also wait for the later
-        // stages' loads, draining the ring every stage)
-        lds_barrier();                                            // ... and every wave's
+    // fragment reads: step s (16 k) of a slot, lane (n, g): piece 2 s + g of
+    // row n of its tile; every tile's rows are n modulo 16, so one swizzle
+    const int swn = (n & 7) ^ ((n >> 3) & 1);
+    uint32_t arow[2], brow[CT];
+#pragma unroll
+    for (int r = 0; r < 2; ++r) arow[r] = (uint32_t)(32 * r + n) * R_ROW;
+#pragma unroll
+    for (int c = 0; c < CT; ++c) brow[c] = (uint32_t)(RB + wave * (E / 4) + 32 * c + n) * R_ROW;
+
+    issue(0, 0);
+    for (int d = 0; d < KD; ++d) {
+        const int slot = d & 1;
+        vm_wait<0>();                                             // this wave's part of slot d landed ...
+        // (LDS-only barrier: __syncthreads() would also wait for the next
+        // slot's loads)
+        lds_barrier();                                            // ... every wave's, and slot d - 1 is free
+        if (d + 1 < KD) issue(d + 1, slot ^ 1);
         const uint32_t st = sbase + slot * SB;
-        u32x4 af[2][2], bf[2][CT];
+        const int steps = min(4, (H - 64 * d) / 16);
+        for (int s = 0; s < steps; ++s) {
+            const uint32_t pc = (uint32_t)(((2 * s + g) ^ swn) * 16);
+            u32x4 af[2], bf[CT];
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            const uint32_t ch = (uint32_t)(((2 * s + g) ^ ((n >> 2) & 3)) * 16);
-            af[s][0] = ds_read16<0>(st + (uint32_t)n * R_ROW + ch);
-            af[s][1] = ds_read16<32 * R_ROW>(st + (uint32_t)n * R_ROW + ch);
+            for (int r = 0; r < 2; ++r) af[r] = ds_read16<0>(st + arow[r] + pc);
 #pragma unroll
-            for (int c = 0; c < CT; ++c)
-                bf[s][c] = ds_read16<0>(st + RB * R_ROW + (uint32_t)(wave * (E / 4) + 32 * c + n) * R_ROW + ch);
-        }
-        lds_wait_all();
+            for (int c = 0; c < CT; ++c) bf[c] = ds_read16<0>(st + brow[c] + pc);
+            lds_wait_all();
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            tie_after_wait(af[s][0]);
-            tie_after_wait(af[s][1]);
+            for (int r = 0; r < 2; ++r) tie_after_wait(af[r]);
 #pragma unroll
-            for (int c = 0; c < CT; ++c) tie_after_wait(bf[s][c]);
-        }
-#pragma unroll
-        for (int s = 0; s < 2; ++s)
+            for (int c = 0; c < CT; ++c) tie_after_wait(bf[c]);
 #pragma unroll
             for (int r = 0; r < 2; ++r)
 #pragma unroll
-                for (int c = 0; c < CT; ++c) acc[r][c] = mfma_bf16(af[s][r], bf[s][c], acc[r][c]);
-        lds_barrier();                                            // every wave is done with this slot
-        if (kt + RNS < KT) issue(kt + RNS, slot);
+                for (int c = 0; c < CT; ++c) acc[r][c] = mfma_bf16(af[r], bf[c], acc[r][c]);
+        }
     }
+    lds_barrier();                                                // every wave done with the last slot
 
     // logits to LDS: lane holds expert column n of its tile, tokens 8 (i >> 2) + 4 g + (i & 3)
     float* lg = reinterpret_cast<float*>(smem);
@@ -234,42 +242,60 @@ void router_topk_kernel(const uint16_t* __restrict__ x, const uint16_t* __restri
                 make_float4(src[0], src[1], src[2], src[3]);
         }
     }
-    // top-k per token, one wave per token: the selection of route_topk_kernel
+    // top-k per token, one wave per token: the selection of route_topk_kernel,
+    // two tokens at a time (r and r + 4) so that the two chains of k
+    // dependent wave reductions interleave (one wave per SIMD here: nothing
+    // else hides their latency)
     constexpr int NV = E / 64;
-    for (int r = wave; r < rows; r += R_THREADS / 64) {
-        const float* row = lg + r * LD;
-        uint64_t key[NV];
+    constexpr int TS = R_THREADS / 64;
+    for (int r = wave; r < rows; r += 2 * TS) {
+        const bool two = r + TS < rows;
+        const int rr[2] = {r, two ? r + TS : r};
+        uint64_t key[2][NV];
 #pragma unroll
-        for (int i = 0; i < NV; ++i) {
-            const int e = lane + 64 * i;
-            key[i] = ((uint64_t)ordered_bits(row[e]) << 32) | (uint32_t)(~e);
-        }
-        int my_e = 0;
-        float my_v = 0.0f;
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+            for (int i = 0; i < NV; ++i) {
+                const int e = lane + 64 * i;
+                key[q][i] = ((uint64_t)ordered_bits(lg[rr[q] * LD + e]) << 32) | (uint32_t)(~e);
+            }
+        int my_e[2] = {0, 0};
+        float my_v[2] = {0.0f, 0.0f};
         for (int j = 0; j < k; ++j) {
-            uint64_t m = 0;
+            uint64_t m[2];
 #pragma unroll
-            for (int i = 0; i < NV; ++i) m = key[i] > m ? key[i] : m;
-            m = wave_max_u64(m);
-            const int win = (int)(~(uint32_t)m);
-            if ((win & 63) == lane) {
+            for (int q = 0; q < 2; ++q) {
+                m[q] = 0;
 #pragma unroll
-                for (int i = 0; i < NV; ++i)
-                    if (i == (win >> 6)) key[i] = 0;
+                for (int i = 0; i < NV; ++i) m[q] = key[q][i] > m[q] ? key[q][i] : m[q];
             }
-            if (lane == j) {
-                my_e = win;
-                my_v = from_ordered((uint32_t)(m >> 32));
+            m[0] = wave_max_u64(m[0]);
+            m[1] = wave_max_u64(m[1]);
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const int win = (int)(~(uint32_t)m[q]);
+                if ((win & 63) == lane) {
+#pragma unroll
+                    for (int i = 0; i < NV; ++i)
+                        if (i == (win >> 6)) key[q][i] = 0;
+                }
+                if (lane == j) {
+                    my_e[q] = win;
+                    my_v[q] = from_ordered((uint32_t)(m[q] >> 32));
+                }
             }
         }
-        const float v0 = __shfl(my_v, 0, 64);
-        const float z = lane < k ? expf(my_v - v0) : 0.0f;
-        const float sum = wave_sum(z);
-        if (lane < k) {
-            const size_t t = (size_t)(t0 + r);
-            topk_ids[t * k + lane] = my_e;
-            topk_w[t * k + lane] = z / sum;
-            atomicAdd(&hist[my_e], 1);
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const float v0 = __shfl(my_v[q], 0, 64);
+            const float z = lane < k ? expf(my_v[q] - v0) : 0.0f;
+            const float sum = wave_sum(z);
+            if (lane < k && (q == 0 || two)) {
+                const size_t t = (size_t)(t0 + rr[q]);
+                topk_ids[t * k + lane] = my_e[q];
+                topk_w[t * k + lane] = z / sum;
+                atomicAdd(&hist[my_e[q]], 1);
+            }
         }
     }
     __syncthreads();
