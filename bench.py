@@ -86,6 +86,9 @@ def parse():
     p.add_argument("--no-flush", action="store_true",
                    help="do not read the 512 MiB scratch buffer between timed steps")
     p.add_argument("--seed", type=int, default=0)
+    p.add_argument("--layout", choices=("pairs", "plain"), default="pairs",
+                   help="storage of bf16 expert weights: the row-pair layout (MOE_WFMT_BF16_PAIRS, packed once "
+                        "after upload, outside any timed region) or plain row-major (MOE_WFMT_BF16)")
     p.add_argument("--fat-threshold", type=int, default=32)
     p.add_argument("--copy-calibration", action="store_true",
                    help="only run a plain 1 GiB device copy (HBM counter calibration)")
@@ -102,14 +105,35 @@ def parse():
     return p.parse_args()
 
 
-def workload_desc(shape, thr):
+def workload_desc(shape, thr, pairs=False):
     router = "Zipf(s=1.1) bias, beta=0.4" if shape.router == "zipf" else "N(0,1), no skew"
+    layout = ("row pairs interleaved every 32 k (MOE_WFMT_BF16_PAIRS)" if pairs else "plain row-major") \
+        if shape.wfmt == "bf16" else "3-bit groups of 128 (MOE_WFMT_Q3G128)"
     return {
         "workload": f"{shape.name}: routed-expert layer, {shape.T} tokens, hidden {shape.H}, "
                     f"expert inter {shape.I}, {shape.E} experts, top-{shape.k}, {shape.wfmt} experts",
         "tokens": shape.T, "hidden": shape.H, "inter": shape.I, "experts": shape.E, "top_k": shape.k,
-        "router": router, "expert_weights": shape.wfmt, "fat_threshold": thr,
+        "router": router, "expert_weights": shape.wfmt, "weight_layout": layout, "fat_threshold": thr,
     }
+
+
+def pack_pairs(dev_w):
+    """bf16 expert weights -> the row-pair layout (moe_pack_bf16_pairs), one
+    matrix family at a time, the plain copy freed as soon as it is packed."""
+    import torch
+
+    import routed_expert_ffn_03_amd as moe
+    t0 = time.perf_counter()
+    for name in list(dev_w):
+        src = dev_w[name]
+        dst = torch.empty_like(src)
+        moe.moe_pack_bf16_pairs(src, dst)
+        torch.cuda.synchronize()
+        dev_w[name] = dst
+        del src
+    torch.cuda.empty_cache()
+    log(f"[bench] bf16 weights packed into the row-pair layout in {time.perf_counter() - t0:.2f} s")
+    return dev_w
 
 
 class StepTimes:
@@ -140,7 +164,7 @@ class StepTimes:
 class Runner:
     """Buffers of one workload and a step that times the gate/up phase with events."""
 
-    def __init__(self, shape, seed, dev_w, thr):
+    def __init__(self, shape, seed, dev_w, thr, pairs=False):
         import numpy as np
         import torch
 
@@ -151,7 +175,9 @@ class Runner:
         self.logits_np, self.x_np = routing_inputs(shape, seed)
         self.logits = torch.from_numpy(self.logits_np).cuda()
         self.x = torch.from_numpy(self.x_np.view(np.int16)).cuda()
-        self.wfmt = 0 if shape.wfmt == "bf16" else 1
+        self.pairs = pairs and shape.wfmt == "bf16"
+        self.wfmt = moe.MOE_WFMT_Q3G128 if shape.wfmt != "bf16" else (
+            moe.MOE_WFMT_BF16_PAIRS if self.pairs else moe.MOE_WFMT_BF16)
         self.b = moe.MoELayerBuffers(shape.T, shape.E, shape.k, shape.H, shape.I, self.wfmt)
 
     def step(self, ev=None):
@@ -297,7 +323,7 @@ def cpu_baseline(shape, seed, n_tokens):
     return res
 
 
-def chunk_sweep(sizes, seed, thr):
+def chunk_sweep(sizes, seed, thr, pairs):
     """The bf16 layer (Zipf router) at several chunk sizes: where the step turns
     from weight streaming (HBM) to MFMA bound.  One JSON line per size."""
     import torch
@@ -307,15 +333,18 @@ def chunk_sweep(sizes, seed, thr):
 
     base = SHAPES["prefill16k"]
     dev_w = upload_weights(base, seed)
+    if pairs:
+        dev_w = pack_pairs(dev_w)
     for T in sizes:
         shape = LayerShape(f"chunk{T}", T, base.H, base.I, base.E, base.k, base.router, base.wfmt)
-        run = Runner(shape, seed, dev_w, thr)
+        run = Runner(shape, seed, dev_w, thr, pairs)
         steps = max(3, min(50, int(2e5 / T)))
         st = run.measure(steps, 2)
         ms, gu = st.mean, st.gate_up_mean
         roof = run.roofline(gu)
         line = {"mode": "chunk_sweep", "tokens": T, "ms_per_step": ms, "tokens_per_s": T / (ms * 1e-3),
-                "gate_up_ms": gu, "gate_up_roofline": roof, "steps": steps, "config": workload_desc(shape, thr)}
+                "gate_up_ms": gu, "gate_up_roofline": roof, "steps": steps,
+                "config": workload_desc(shape, thr, pairs)}
         log(f"[sweep] T={T}: {ms:.3f} ms/step, {T / ms * 1e3:.0f} tok/s, gate/up {gu:.3f} ms "
             f"({roof['bound']}, {100 * roof['frac']:.1f}% of peak)")
         print(json.dumps(line), flush=True)
@@ -503,7 +532,7 @@ def main():
         return
     if args.sweep:
         moe_lib_check()
-        chunk_sweep([int(v) for v in args.sweep.split(",")], args.seed, args.fat_threshold)
+        chunk_sweep([int(v) for v in args.sweep.split(",")], args.seed, args.fat_threshold, args.layout == "pairs")
         return
     if args.router:
         moe_lib_check()
@@ -524,9 +553,12 @@ def main():
     t0 = time.perf_counter()
     dev_w = upload_weights(shape, args.seed)
     log(f"[bench] weights for {shape.name} generated and uploaded in {time.perf_counter() - t0:.1f} s")
+    pairs = shape.wfmt == "bf16" and args.layout == "pairs"
+    if pairs:
+        dev_w = pack_pairs(dev_w)
 
     flush = None if args.no_flush else torch.ones(FLUSH_BYTES // 8, dtype=torch.int64, device="cuda")
-    run = Runner(shape, args.seed, dev_w, args.fat_threshold)
+    run = Runner(shape, args.seed, dev_w, args.fat_threshold, pairs)
     st = run.measure(args.steps, args.warmup, flush)
     ms, gu_ms = st.mean, st.gate_up_mean
     roof = run.roofline(gu_ms)
@@ -537,7 +569,7 @@ def main():
         "metric": METRIC, "value": shape.T / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": shape.wfmt, "data": "synthetic",
-        "config": workload_desc(shape, args.fat_threshold), "roofline": roof,
+        "config": workload_desc(shape, args.fat_threshold, pairs), "roofline": roof,
         "timing": {**st.stats(), "mall_flush_bytes": 0 if flush is None else FLUSH_BYTES,
                    "method": "HIP events around each layer call on the library's stream (the gate/up phase timed "
                              "in a second run of the same steps); a 512 MiB scratch buffer is read between "
@@ -548,7 +580,7 @@ def main():
     if not args.no_decode and not args.workload.startswith("decode"):
         # the 4-token decode step on the same weights (same format, same layer)
         dshape = SHAPES["decode" if shape.wfmt == "bf16" else "decode_q3"]
-        drun = Runner(dshape, args.seed, dev_w, args.fat_threshold)
+        drun = Runner(dshape, args.seed, dev_w, args.fat_threshold, pairs)
         dst = drun.measure(args.decode_steps, 20, flush)
         dms, dgu = dst.mean, dst.gate_up_mean
         droof = drun.roofline(dgu)
@@ -557,7 +589,7 @@ def main():
             f"{dgu * 1e3:.1f} us, {droof['achieved']:.1f} {droof['unit']} ({100 * droof['frac']:.1f}% of peak); "
             f"whole layer {dlayer['achieved']:.0f} GB/s ({100 * dlayer['frac']:.1f}%)")
         res["decode"] = {"value": dshape.T / (dms * 1e-3), "unit": "tokens/s", "ms_per_step": dms,
-                         "steps": args.decode_steps, "config": workload_desc(dshape, args.fat_threshold),
+                         "steps": args.decode_steps, "config": workload_desc(dshape, args.fat_threshold, pairs),
                          "roofline": droof, "layer_roofline": dlayer, "timing": dst.stats()}
     if not args.no_cpu_baseline:
         n = min(args.cpu_sample, shape.T)

@@ -67,6 +67,7 @@ typedef int32_t moe_status;
 /* Expert weight storage formats accepted by moe_grouped_ffn. */
 #define MOE_WFMT_BF16   0   /* bf16 matrices [E, out, in]                       */
 #define MOE_WFMT_Q3G128 1   /* 3-bit codes, groups of 128 along `in`, fp16 scale */
+#define MOE_WFMT_BF16_PAIRS 2 /* bf16 matrices in the row-pair layout (moe_pack_bf16_pairs) */
 
 #define MOE_MAX_TOPK    32
 #define MOE_MAX_EXPERTS 1024
@@ -178,11 +179,14 @@ moe_status moe_permute(const int32_t* topk_ids, int T, int E, int k,
  * expert; matrices stored [out, in] with the reduction index contiguous.
  *
  * x          bf16 [T, H]
- * w_gate     MOE_WFMT_BF16: bf16 [E, I, H];   MOE_WFMT_Q3G128: uint32 [E, I, H/128, 13]
+ * w_gate     MOE_WFMT_BF16: bf16 [E, I, H];   MOE_WFMT_Q3G128: uint32 [E, I, H/128, 13];
+ *            MOE_WFMT_BF16_PAIRS: the bf16 [E, I, H] values in the row-pair
+ *            layout that moe_pack_bf16_pairs writes (same size)
  * w_up       same as w_gate
- * w_down     MOE_WFMT_BF16: bf16 [E, H, I];   MOE_WFMT_Q3G128: uint32 [E, H, I/128, 13]
+ * w_down     MOE_WFMT_BF16: bf16 [E, H, I];   MOE_WFMT_Q3G128: uint32 [E, H, I/128, 13];
+ *            MOE_WFMT_BF16_PAIRS: [E, H, I] in the row-pair layout
  * s_gate, s_up, s_down   fp16 scales [E, I, H/128] / [E, H, I/128] for
- *            MOE_WFMT_Q3G128 (must be NULL for MOE_WFMT_BF16).  3-bit group
+ *            MOE_WFMT_Q3G128 (must be NULL for the bf16 formats).  3-bit group
  *            layout: 13 words per 128 weights; field j of a word at bits
  *            [3j, 3j+3), 10 fields in words 0..11, 8 in word 12; weight =
  *            scale * (field - 4).
@@ -200,7 +204,8 @@ moe_status moe_permute(const int32_t* topk_ids, int T, int E, int k,
  * Shapes: H % 256 == 0 and I % 128 == 0, and each of x (T*H*2 bytes), the
  * activation a (T*k*I*2 bytes) and one expert's bf16 matrix (I*H*2 bytes)
  * below 4 GiB (the kernels address them with 32-bit buffer offsets), else
- * MOE_ERR_UNSUPPORTED.
+ * MOE_ERR_UNSUPPORTED.  MOE_WFMT_BF16_PAIRS also needs I % 256 == 0 and
+ * T*k < 2^30.  The two bf16 formats give the same results bit for bit.
  * Workspace: >= moe_workspace_size(T, E, k, H, I, wfmt) bytes.
  */
 moe_status moe_grouped_ffn(const uint16_t* x, int wfmt,
@@ -287,6 +292,25 @@ moe_status moe_grouped_ffn_noalloc(const uint16_t* x, int wfmt, const void* w_ga
                                    const uint16_t* s_down, const int32_t* expert_offsets, const int32_t* sorted_pair,
                                    int T, int E, int k, int H, int I, int fat_threshold, uint16_t* y_sorted,
                                    void* stream);
+
+/*
+ * moe_pack_bf16_pairs -- copy bf16 matrices into the row-pair layout of
+ * MOE_WFMT_BF16_PAIRS (a storage layout of the same values; the pages fix
+ * none for the bf16 experts).
+ *
+ * src   bf16 [mats, rows, cols], plain row-major (e.g. W_gate with mats = E,
+ *       rows = I, cols = H; W_down with rows = H, cols = I).
+ * dst   bf16, same size: element (r, c) of matrix m at
+ *       m*rows*cols + ((r/2)*(cols/32) + c/32)*64 + (r%2)*32 + c%32,
+ *       i.e. rows 2p and 2p+1 alternate every 32 columns, so that 32 columns
+ *       of a row pair fill one 128-byte line.
+ * rows even and >= 2, cols a multiple of 32, both pointers 16-byte aligned,
+ * the two buffers not overlapping (no in-place packing), else
+ * MOE_ERR_INVALID_ARG.  One launch on `stream`; done once when weights are
+ * loaded, not per layer call.
+ */
+moe_status moe_pack_bf16_pairs(const uint16_t* src, uint16_t* dst, int64_t mats, int rows, int cols,
+                               void* stream);
 
 /*
  * moe_combine -- out[t, :] = sum_{j=0..k-1} topk_w[t, j] * y_sorted[pair_to_sorted[t*k+j], :]

@@ -12,8 +12,8 @@
 """
 from .binding import (  # noqa: F401
     MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP,
-    MOE_WFMT_BF16, MOE_WFMT_Q3G128, DEFAULT_FAT_THRESHOLD, EXPORTS, MoEError, lib,
+    MOE_WFMT_BF16, MOE_WFMT_Q3G128, MOE_WFMT_BF16_PAIRS, DEFAULT_FAT_THRESHOLD, EXPORTS, MoEError, lib,
     moe_workspace_size, moe_route_topk, moe_router_topk, moe_permute, moe_grouped_ffn, moe_ffn_plan, moe_ffn_gate_up,
-    moe_ffn_down, moe_combine, moe_grouped_ffn_noalloc, moe_route_permute_plan,
+    moe_ffn_down, moe_combine, moe_grouped_ffn_noalloc, moe_route_permute_plan, moe_pack_bf16_pairs,
 )
 from .layer import MoELayerBuffers  # noqa: F401

@@ -18,12 +18,13 @@ MOE_ERR_WORKSPACE = 3
 MOE_ERR_HIP = 4
 MOE_WFMT_BF16 = 0
 MOE_WFMT_Q3G128 = 1
+MOE_WFMT_BF16_PAIRS = 2
 
 DEFAULT_FAT_THRESHOLD = 32
 
 EXPORTS = ("moe_status_string", "moe_version", "moe_workspace_size", "moe_route_topk", "moe_router_topk",
            "moe_permute", "moe_grouped_ffn", "moe_ffn_plan", "moe_ffn_gate_up", "moe_ffn_down",
-           "moe_combine", "moe_grouped_ffn_noalloc", "moe_route_permute_plan")
+           "moe_combine", "moe_grouped_ffn_noalloc", "moe_route_permute_plan", "moe_pack_bf16_pairs")
 
 NOALLOC_SCRATCH_BYTES = 64 << 20
 
@@ -72,6 +73,8 @@ def lib() -> ctypes.CDLL:
         L.moe_route_permute_plan.argtypes = [vp, i32, i32, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.moe_combine.restype = i32
         L.moe_combine.argtypes = [vp, vp, vp, i32, i32, i32, vp, vp]
+        L.moe_pack_bf16_pairs.restype = i32
+        L.moe_pack_bf16_pairs.argtypes = [vp, vp, ctypes.c_int64, i32, i32, vp]
         _lib = L
     return _lib
 
@@ -257,3 +260,17 @@ def moe_combine(y_sorted, topk_w, pair_to_sorted, out, stream=None):
         raise ValueError("y_sorted: expected a contiguous 16-bit GPU tensor")
     _check(lib().moe_combine(_ptr(y_sorted), _ptr(topk_w), _ptr(pair_to_sorted), T, k, H, _ptr(out),
                              _stream(stream)), "moe_combine")
+
+
+def moe_pack_bf16_pairs(src, dst, stream=None):
+    """Copy bf16 matrices ``src`` [..., rows, cols] into ``dst`` (same shape) in the row-pair layout
+    that ``MOE_WFMT_BF16_PAIRS`` reads: rows 2p and 2p+1 alternate every 32 columns."""
+    for t, name in ((src, "src"), (dst, "dst")):
+        if not (isinstance(t, torch.Tensor) and t.is_cuda and t.is_contiguous() and t.element_size() == 2):
+            raise ValueError(f"{name}: expected a contiguous 16-bit GPU tensor")
+    if src.dim() < 2 or tuple(src.shape) != tuple(dst.shape):
+        raise ValueError(f"src {tuple(src.shape)} and dst {tuple(dst.shape)}: same shape [..., rows, cols] expected")
+    rows, cols = int(src.shape[-2]), int(src.shape[-1])
+    mats = src.numel() // (rows * cols) if rows * cols else 0
+    _check(lib().moe_pack_bf16_pairs(_ptr(src), _ptr(dst), mats, rows, cols, _stream(stream)),
+           "moe_pack_bf16_pairs")

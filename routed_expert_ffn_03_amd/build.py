@@ -16,7 +16,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmoe_mi355x.so")
-SOURCES = ["api.hip", "route.hip", "permute.hip", "ffn.hip", "fat8.hip", "stream.hip", "front.hip", "q3dec.hip", "combine.hip"]
+SOURCES = ["api.hip", "route.hip", "permute.hip", "ffn.hip", "fat8.hip", "stream.hip", "front.hip", "q3dec.hip", "combine.hip", "pack.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

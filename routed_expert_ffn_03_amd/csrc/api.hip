@@ -58,6 +58,24 @@ bool ffn_shape_ok(int T, int k, int H, int I) {
 
 moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
+bool wfmt_known(int wfmt) {
+    return wfmt == MOE_WFMT_BF16 || wfmt == MOE_WFMT_Q3G128 || wfmt == MOE_WFMT_BF16_PAIRS;
+}
+
+// Shape rules of a format beyond ffn_shape_ok: the row-pair layout is read
+// by the MFMA-tile and the whole-line streaming kernels only, and the latter
+// needs each wave's quarter of the reduction index (H / 4 and I / 4) to be a
+// multiple of 64.
+bool wfmt_shape_ok(int wfmt, int T, int k, int H, int I) {
+    if (wfmt != MOE_WFMT_BF16_PAIRS) return true;
+    return moe::stream_fits(1, T, k, H, I) && moe::stream_fits(2, T, k, H, I);
+}
+
+// Scales come with the 3-bit format and only with it.
+bool scales_ok(int wfmt, const void* a, const void* b) {
+    return wfmt == MOE_WFMT_Q3G128 ? (a && b) : (!a && !b);
+}
+
 }  // namespace
 
 extern "C" {
@@ -77,7 +95,7 @@ const char* moe_version(void) { return "0.1.0"; }
 
 size_t moe_workspace_size(int T, int E, int k, int H, int I, int wfmt) {
     if (bad_tek(T, E, k) || !ffn_shape_ok(T, k, H, I)) return 0;
-    if (wfmt != MOE_WFMT_BF16 && wfmt != MOE_WFMT_Q3G128) return 0;
+    if (!wfmt_known(wfmt) || !wfmt_shape_ok(wfmt, T, k, H, I)) return 0;
     return align256(moe::permute_ws_bytes(T, E)) + moe::ffn_ws_bytes(T, E, k, H, I, wfmt);
 }
 
@@ -117,8 +135,8 @@ moe_status moe_permute(const int32_t* topk_ids, int T, int E, int k, int32_t* ex
 static moe_status ffn_prepare(moe::FfnLaunch& a, int wfmt, int T, int E, int k, int H, int I,
                               void* workspace, size_t workspace_bytes) {
     if (bad_tek(T, E, k) || H < 1 || I < 1) return MOE_ERR_INVALID_ARG;
-    if (wfmt != MOE_WFMT_BF16 && wfmt != MOE_WFMT_Q3G128) return MOE_ERR_UNSUPPORTED;
-    if (!ffn_shape_ok(T, k, H, I)) return MOE_ERR_UNSUPPORTED;
+    if (!wfmt_known(wfmt)) return MOE_ERR_UNSUPPORTED;
+    if (!ffn_shape_ok(T, k, H, I) || !wfmt_shape_ok(wfmt, T, k, H, I)) return MOE_ERR_UNSUPPORTED;
     const size_t need = moe_workspace_size(T, E, k, H, I, wfmt);
     if (!workspace || workspace_bytes < need) return MOE_ERR_WORKSPACE;
     a = moe::FfnLaunch{};
@@ -126,10 +144,6 @@ static moe_status ffn_prepare(moe::FfnLaunch& a, int wfmt, int T, int E, int k, 
     a.T = T; a.E = E; a.k = k; a.H = H; a.I = I;
     a.ws = reinterpret_cast<char*>(workspace) + align256(moe::permute_ws_bytes(T, E));
     return MOE_OK;
-}
-
-static bool scales_ok(int wfmt, const void* a, const void* b) {
-    return wfmt == MOE_WFMT_BF16 ? (!a && !b) : (a && b);
 }
 
 moe_status moe_ffn_plan(const int32_t* expert_offsets, int T, int E, int k, int H, int I, int wfmt,
@@ -148,7 +162,7 @@ moe_status moe_ffn_gate_up(const uint16_t* x, int wfmt, const void* w_gate, cons
                            int T, int E, int k, int H, int I, int fat_threshold, void* workspace,
                            size_t workspace_bytes, void* stream) {
     if (!x || !w_gate || !w_up || !sorted_pair || fat_threshold < 1) return MOE_ERR_INVALID_ARG;
-    if ((wfmt == MOE_WFMT_BF16 || wfmt == MOE_WFMT_Q3G128) && !scales_ok(wfmt, s_gate, s_up))
+    if (wfmt_known(wfmt) && !scales_ok(wfmt, s_gate, s_up))
         return MOE_ERR_INVALID_ARG;
     moe::FfnLaunch a;
     moe_status st = ffn_prepare(a, wfmt, T, E, k, H, I, workspace, workspace_bytes);
@@ -165,7 +179,7 @@ moe_status moe_ffn_down(int wfmt, const void* w_down, const uint16_t* s_down, in
                         int fat_threshold, uint16_t* y_sorted, void* workspace, size_t workspace_bytes,
                         void* stream) {
     if (!w_down || !y_sorted || fat_threshold < 1) return MOE_ERR_INVALID_ARG;
-    if ((wfmt == MOE_WFMT_BF16 || wfmt == MOE_WFMT_Q3G128) && !scales_ok(wfmt, s_down, s_down))
+    if (wfmt_known(wfmt) && !scales_ok(wfmt, s_down, s_down))
         return MOE_ERR_INVALID_ARG;
     moe::FfnLaunch a;
     moe_status st = ffn_prepare(a, wfmt, T, E, k, H, I, workspace, workspace_bytes);
@@ -185,7 +199,7 @@ moe_status moe_grouped_ffn(const uint16_t* x, int wfmt, const void* w_gate, cons
     if (!x || !w_gate || !w_up || !w_down || !expert_offsets || !sorted_pair || !y_sorted)
         return MOE_ERR_INVALID_ARG;
     if (fat_threshold < 1) return MOE_ERR_INVALID_ARG;
-    if (wfmt == MOE_WFMT_BF16 || wfmt == MOE_WFMT_Q3G128) {
+    if (wfmt_known(wfmt)) {
         if (!scales_ok(wfmt, s_gate, s_up) || !scales_ok(wfmt, s_down, s_down)) return MOE_ERR_INVALID_ARG;
     }
     moe::FfnLaunch a;
@@ -234,9 +248,9 @@ moe_status moe_grouped_ffn_noalloc(const uint16_t* x, int wfmt, const void* w_ga
     if (!x || !w_gate || !w_up || !w_down || !expert_offsets || !sorted_pair || !y_sorted)
         return MOE_ERR_INVALID_ARG;
     if (fat_threshold < 1 || bad_tek(T, E, k) || H < 1 || I < 1) return MOE_ERR_INVALID_ARG;
-    if (wfmt != MOE_WFMT_BF16 && wfmt != MOE_WFMT_Q3G128) return MOE_ERR_UNSUPPORTED;
+    if (!wfmt_known(wfmt)) return MOE_ERR_UNSUPPORTED;
     if (!scales_ok(wfmt, s_gate, s_up) || !scales_ok(wfmt, s_down, s_down)) return MOE_ERR_INVALID_ARG;
-    if (!ffn_shape_ok(T, k, H, I)) return MOE_ERR_UNSUPPORTED;
+    if (!ffn_shape_ok(T, k, H, I) || !wfmt_shape_ok(wfmt, T, k, H, I)) return MOE_ERR_UNSUPPORTED;
     if (moe::ffn_ws_bytes(T, E, k, H, I, wfmt) > MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_WORKSPACE;
     void* ws = nullptr;
     hipError_t err = scratch_address(&ws);
@@ -259,6 +273,19 @@ moe_status moe_grouped_ffn_noalloc(const uint16_t* x, int wfmt, const void* w_ga
     if (err == hipSuccess) err = moe::launch_ffn_phase(a, 1, s);
     if (err == hipSuccess) err = moe::launch_ffn_phase(a, 2, s);
     return hip_status(err);
+}
+
+moe_status moe_pack_bf16_pairs(const uint16_t* src, uint16_t* dst, int64_t mats, int rows, int cols,
+                               void* stream) {
+    if (!src || !dst || mats < 1 || rows < 2 || rows % 2 != 0 || cols < 32 || cols % 32 != 0)
+        return MOE_ERR_INVALID_ARG;
+    if (((uintptr_t)src | (uintptr_t)dst) & 15) return MOE_ERR_INVALID_ARG;
+    const unsigned long long per = (unsigned long long)rows * (unsigned long long)cols * 2ull;
+    if ((unsigned long long)mats > (1ull << 62) / per) return MOE_ERR_INVALID_ARG;
+    const uintptr_t bytes = (uintptr_t)((unsigned long long)mats * per);
+    const uintptr_t s0 = (uintptr_t)src, d0 = (uintptr_t)dst;
+    if (s0 < d0 + bytes && d0 < s0 + bytes) return MOE_ERR_INVALID_ARG;     // overlapping buffers
+    return hip_status(moe::launch_pack_pairs(src, dst, mats, rows, cols, reinterpret_cast<hipStream_t>(stream)));
 }
 
 moe_status moe_combine(const uint16_t* y_sorted, const float* topk_w, const int32_t* pair_to_sorted, int T, int k,

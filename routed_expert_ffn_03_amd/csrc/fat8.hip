@@ -24,6 +24,12 @@
 // count), so the two groups share the MFMA work of any M-tile to within one
 // row tile.
 //
+// Weight rows in the row-pair layout (weight format 2: rows 2p and 2p + 1
+// alternate every 32 k) make each weight load instruction cover 8 whole
+// 128-byte lines instead of 16 half lines; the per-CU load path moves about
+// one line per clock either way, so the weight loads cost half as much of it.
+// The LDS layout and everything after the loads are the same for both.
+//
 // Per round kt (one 32-k stage):
 //   half A: group 0 computes stage kt; group 1 reads its fragments of stage
 //           kt and issues its loads of stage kt + 4; barrier.
@@ -77,6 +83,9 @@ void ffn_fat8_kernel(FfnArgs a) {
         ? make_rsrc(a.x, (uint32_t)((size_t)a.T * a.H * 2))
         : make_rsrc(a.act, (uint32_t)((size_t)a.T * a.k * a.I * 2));
     const size_t wbytes = (size_t)a.I * a.H * 2;
+    // weight bytes between consecutive stages of one row: 64, or 128 in the
+    // row-pair layout (rows 2p and 2p + 1 alternate every 32 k)
+    const uint32_t wstage = a.pairs ? 2 * DMA_ROW : DMA_ROW;
     // 16 rows x 64 B per load instruction, 4 lanes per row; the chunk landing
     // at position L % 4 of row r is (L % 4) ^ ((r >> 2) & 3)
     const uint32_t lch16 = (uint32_t)(((lane & 3) ^ ((lane >> 4) & 3)) * 16);
@@ -126,7 +135,8 @@ void ffn_fat8_kernel(FfnArgs a) {
             aoff[j] = src * (uint32_t)K * 2u + lch16;
             const int b = 32 * wave + 16 * j + (lane >> 2);
             const uint32_t wrow = PHASE == 1 ? (uint32_t)(nt * 128 + (b & 127)) : (uint32_t)(nt * 256 + b);
-            boff[j] = wrow * (uint32_t)K * 2u + lch16;
+            boff[j] = a.pairs ? (wrow & ~1u) * (uint32_t)K * 2u + (wrow & 1u) * DMA_ROW + lch16
+                              : wrow * (uint32_t)K * 2u + lch16;
         }
 
         auto kloop = [&](auto rt_c) {
@@ -143,7 +153,7 @@ void ffn_fat8_kernel(FfnArgs a) {
 #pragma unroll
                 for (int j = 0; j < 2; ++j)
                     __builtin_amdgcn_raw_ptr_buffer_load_lds(wsrc, (lds_ptr_t)(st + DMA_OPER + (2 * wave + j) * 1024),
-                                                             16, boff[j], kt * DMA_ROW, 0, 0);
+                                                             16, boff[j], kt * wstage, 0, 0);
             };
             auto run = [&](auto rg_c, auto g0_c) {
                 constexpr int RG = decltype(rg_c)::value;            // row tiles of this wave

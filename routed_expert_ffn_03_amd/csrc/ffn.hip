@@ -1028,6 +1028,7 @@ FfnArgs make_args(const FfnLaunch& a) {
     fa.sg = a.sg; fa.su = a.su; fa.sd = a.sd;
     fa.sorted_pair = a.sorted_pair;
     fa.T = a.T; fa.k = a.k; fa.H = a.H; fa.I = a.I; fa.E = a.E;
+    fa.pairs = a.wfmt == 2;
     fa.act = reinterpret_cast<uint16_t*>(ws + L.act);
     fa.xq = a.wfmt == 1 ? reinterpret_cast<uint16_t*>(ws + L.xq) : nullptr;
     fa.xs = a.wfmt == 1 ? reinterpret_cast<uint32_t*>(ws + L.xs) : nullptr;
@@ -1067,6 +1068,7 @@ hipError_t launch_phase_t(const FfnArgs& fa, const DevInfo& d, bool fat_possible
         // quarter of K is a multiple of 64; else straight into registers
         if (stream_fits(PHASE, fa.T, fa.k, fa.H, fa.I))
             return launch_stream_phase(fa, PHASE, d.cus * d.thin_blocks[0][PHASE - 1][1], s);
+        if (fa.pairs) return hipErrorInvalidValue;           // the row-pair layout is read by the streaming kernel only
         ffn_thin_kernel<PHASE, 2><<<d.cus * d.thin_blocks[0][PHASE - 1][0], THIN_THREADS, 0, s>>>(fa);
     }
     return hipGetLastError();
@@ -1099,8 +1101,9 @@ hipError_t launch_ffn_phase(const FfnLaunch& a, int phase, hipStream_t s) {
     if (err != hipSuccess) return err;
     const FfnArgs fa = make_args(a);
     const bool fat = a.T >= a.fat_threshold;
-    if (phase == 1) return a.wfmt == 0 ? launch_phase_t<1, 0>(fa, d, fat, s) : launch_phase_t<1, 1>(fa, d, fat, s);
-    return a.wfmt == 0 ? launch_phase_t<2, 0>(fa, d, fat, s) : launch_phase_t<2, 1>(fa, d, fat, s);
+    // formats 0 and 2 (bf16, plain or row-pair layout) share the kernels
+    if (phase == 1) return a.wfmt != 1 ? launch_phase_t<1, 0>(fa, d, fat, s) : launch_phase_t<1, 1>(fa, d, fat, s);
+    return a.wfmt != 1 ? launch_phase_t<2, 0>(fa, d, fat, s) : launch_phase_t<2, 1>(fa, d, fat, s);
 }
 
 }  // namespace moe

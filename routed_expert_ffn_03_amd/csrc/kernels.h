@@ -25,7 +25,7 @@ hipError_t launch_permute(const int32_t* ids, int T, int E, int k, int32_t* offs
 
 struct FfnLaunch {
     const uint16_t* x;
-    int wfmt;                       // 0 = bf16, 1 = 3-bit groups of 128
+    int wfmt;                       // 0 = bf16, 1 = 3-bit groups of 128, 2 = bf16 in the row-pair layout
     const void* wg;
     const void* wu;
     const void* wd;
@@ -42,6 +42,9 @@ struct FfnLaunch {
 size_t ffn_ws_bytes(int T, int E, int k, int H, int I, int wfmt);
 hipError_t launch_ffn_plan(const FfnLaunch& a, hipStream_t s);
 hipError_t launch_ffn_phase(const FfnLaunch& a, int phase, hipStream_t s);   // 1 = gate/up, 2 = down
+
+// bf16 matrices [mats, rows, cols] -> the row-pair layout (pack.hip)
+hipError_t launch_pack_pairs(const uint16_t* src, uint16_t* dst, int64_t mats, int rows, int cols, hipStream_t s);
 
 hipError_t launch_combine(const uint16_t* y, const float* w, const int32_t* p2s, int T, int k, int H,
                           float* out, hipStream_t s);

@@ -74,12 +74,24 @@ void ffn_stream_kernel(FfnArgs a) {
     const int nch = Kw / ST_K;
     const uint32_t rowb = (uint32_t)K * 2u;
     const uint32_t kslice = (uint32_t)(wave * Kw) * 2u;
+    const bool pairs = a.pairs != 0;                       // row-pair layout (weight format 2)
+    // bytes from a row's (pair's) start to this wave's slice, and per chunk
+    const uint32_t kofs = pairs ? 2 * kslice : kslice;
+    const uint32_t chofs = pairs ? 2 * (ST_K * 2) : ST_K * 2;
     const size_t mbytes = (size_t)N * K * 2;
 
     // load instruction i moves rows 8 i .. 8 i + 7 of the chunk; lane L puts
-    // row 8 i + L / 8, position L % 8, which holds piece (L % 8) ^ swz(row)
+    // row 8 i + L / 8, position L % 8, which holds piece (L % 8) ^ swz(row).
+    // Piece P of a row's 64-k chunk lies at 16 P bytes from the chunk's start
+    // in the plain layout; in the row-pair layout (rows 2p and 2p + 1
+    // alternate every 32 k, 64 B each) the pair's chunk is 256 contiguous
+    // bytes and the piece lies at 128 (P / 4) + 64 (row & 1) + 16 (P % 4).
     const int lr = lane >> 3;
-    const uint32_t pofs[2] = {(uint32_t)(((lane & 7) ^ lr) * 16), (uint32_t)(((lane & 7) ^ lr ^ 1) * 16)};
+    auto piece_off = [&](int P) -> uint32_t {
+        return pairs ? (uint32_t)((P >> 2) * 128 + (lr & 1) * 64 + (P & 3) * 16) : (uint32_t)(P * 16);
+    };
+    const uint32_t pofs[2] = {piece_off((lane & 7) ^ lr), piece_off((lane & 7) ^ lr ^ 1)};
+    const int lrow = pairs ? (lr & ~1) : lr;               // the row (pair) whose start the lane adds
     uint32_t vconst[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -134,9 +146,9 @@ void ffn_stream_kernel(FfnArgs a) {
             make_rsrc(reinterpret_cast<const char*>(PHASE == 1 ? a.wg : a.wd) + eoff, (uint32_t)mbytes);
         const __amdgpu_buffer_rsrc_t w1 =
             PHASE == 1 ? make_rsrc(reinterpret_cast<const char*>(a.wu) + eoff, (uint32_t)mbytes) : w0;
-        const uint32_t vrow = (uint32_t)((PHASE == 1 ? 16 : 32) * q.nt + lr) * rowb;
+        const uint32_t vrow = (uint32_t)((PHASE == 1 ? 16 : 32) * q.nt + lrow) * rowb;
         char* st = ring + (wave * ST_SLOTS + sl) * ST_CHUNK;
-        const uint32_t soff = kslice + (uint32_t)ch * (ST_K * 2);
+        const uint32_t soff = kofs + (uint32_t)ch * chofs;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(i < 2 ? w0 : w1, (lds_ptr_t)(st + i * 1024), 16,

@@ -52,6 +52,10 @@ def test_workspace_size(L):
     # 3-bit: plus the reordered thin activation rows and their 128-group sums
     assert L.moe_workspace_size(16384, 384, 8, 4096, 2048, 1) == ws + r256(16384 * 4096 * 2) + r256(16384 * 32 * 4)
     assert L.moe_workspace_size(4, 384, 8, 4096, 2048, 0) > 0
+    # the row-pair bf16 layout: the same workspace, but I a multiple of 256
+    assert L.moe_workspace_size(16384, 384, 8, 4096, 2048, 2) == ws
+    assert L.moe_workspace_size(64, 16, 2, 256, 384, 0) > 0
+    assert L.moe_workspace_size(64, 16, 2, 256, 384, 2) == 0
     for bad in [(0, 384, 8, 4096, 2048, 0), (4, 2000, 8, 4096, 2048, 0), (4, 384, 0, 4096, 2048, 0),
                 (4, 384, 33, 4096, 2048, 0), (4, 4, 5, 4096, 2048, 0), (4, 384, 8, 4000, 2048, 0),
                 (4, 384, 8, 4096, 2000, 0), (4, 384, 8, 4096, 2048, 5), (1 << 28, 384, 8, 4096, 2048, 0),
@@ -110,7 +114,9 @@ def test_grouped_ffn_rejects(L):
     assert _ffn(L, thr=0) == moe.MOE_ERR_INVALID_ARG
     assert _ffn(L, sg=FAKE) == moe.MOE_ERR_INVALID_ARG                 # bf16 takes no scales
     assert _ffn(L, wfmt=1) == moe.MOE_ERR_INVALID_ARG                  # 3-bit needs scales
-    assert _ffn(L, wfmt=2) == moe.MOE_ERR_UNSUPPORTED
+    assert _ffn(L, wfmt=2) == moe.MOE_ERR_UNSUPPORTED                  # row pairs: I % 256 != 0
+    assert _ffn(L, wfmt=2, I=256, sg=FAKE) == moe.MOE_ERR_INVALID_ARG  # bf16 pairs take no scales
+    assert _ffn(L, wfmt=3) == moe.MOE_ERR_UNSUPPORTED
     assert _ffn(L, H=384) == moe.MOE_ERR_UNSUPPORTED
     assert _ffn(L, I=192) == moe.MOE_ERR_UNSUPPORTED
     # 32-bit buffer offsets: x, the activation and one expert matrix stay below 4 GiB
@@ -169,6 +175,9 @@ def test_noalloc_rejects(L):
     bad = list(args)
     bad[13] = 200                                   # H not a multiple of 256
     assert L.moe_grouped_ffn_noalloc(*bad) == moe.MOE_ERR_UNSUPPORTED
+    bad = list(args)
+    bad[1] = 2                                      # row pairs need I % 256 == 0
+    assert L.moe_grouped_ffn_noalloc(*bad) == moe.MOE_ERR_UNSUPPORTED
     # beyond the 64 MiB array: 4096 x 8 pairs x 2048 x 2 bytes of activation
     big = list(args)
     big[10:15] = [4096, 384, 8, 4096, 2048]
@@ -191,3 +200,18 @@ def test_route_permute_plan_rejects(L):
     bad = list(args)
     bad[6] = 7                                        # unknown weight format
     assert L.moe_route_permute_plan(*bad) == moe.MOE_ERR_UNSUPPORTED
+
+
+def test_pack_rejects(L):
+    i64 = ctypes.c_int64
+    call = lambda src, dst, mats, rows, cols: L.moe_pack_bf16_pairs(src, dst, i64(mats), rows, cols, None)
+    D = FAKE + (1 << 30)                               # a destination far from FAKE
+    assert call(None, D, 1, 2, 32) == moe.MOE_ERR_INVALID_ARG
+    assert call(FAKE, None, 1, 2, 32) == moe.MOE_ERR_INVALID_ARG
+    for mats, rows, cols in [(0, 2, 32), (1, 0, 32), (1, 3, 32), (1, 2, 16), (1, 2, 48), (-1, 2, 32),
+                             (1 << 60, 2048, 4096)]:
+        assert call(FAKE, D, mats, rows, cols) == moe.MOE_ERR_INVALID_ARG, (mats, rows, cols)
+    assert call(FAKE + 8, D, 1, 2, 32) == moe.MOE_ERR_INVALID_ARG     # not 16-byte aligned
+    assert call(FAKE, D + 2, 1, 2, 32) == moe.MOE_ERR_INVALID_ARG
+    assert call(FAKE, FAKE, 1, 2, 32) == moe.MOE_ERR_INVALID_ARG       # in place
+    assert call(FAKE, FAKE + 64, 1, 2, 32) == moe.MOE_ERR_INVALID_ARG  # overlapping (128 bytes each)
