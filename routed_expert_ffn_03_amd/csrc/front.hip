@@ -45,31 +45,17 @@ void route_permute_plan_kernel(const float* __restrict__ logits, int T, int E, i
     // 1. gate: one wave per token, the keys and k rounds of moe_route_topk
     for (int t = wave; t < T; t += FRONT_WAVES) {
         const float* row = logits + (size_t)t * E;
-        uint64_t key[NV];
+        uint32_t ord[1][NV];
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
             const int e = lane + WAVE * i;
-            key[i] = 0;
-            if (e < E) key[i] = ((uint64_t)ordered_bits(row[e]) << 32) | (uint32_t)(~e);
+            ord[0][i] = e < E ? ordered_bits(row[e]) : 0u;
         }
-        int my_e = 0;
-        float my_v = 0.0f;
-        for (int j = 0; j < k; ++j) {
-            uint64_t m = 0;
-#pragma unroll
-            for (int i = 0; i < NV; ++i) m = key[i] > m ? key[i] : m;
-            m = wave_max_u64(m);
-            const int win = (int)(~(uint32_t)m);
-            if ((win & 63) == lane) {
-#pragma unroll
-                for (int i = 0; i < NV; ++i)
-                    if (i == (win >> 6)) key[i] = 0;
-            }
-            if (lane == j) {
-                my_e = win;
-                my_v = from_ordered((uint32_t)(m >> 32));
-            }
-        }
+        int me[1] = {0};
+        float mv[1] = {0.0f};
+        wave_topk<NV, 1>(ord, k, lane, me, mv);
+        const int my_e = me[0];
+        const float my_v = mv[0];
         const float v0 = __shfl(my_v, 0, 64);
         const float z = lane < k ? expf(my_v - v0) : 0.0f;
         const float s = wave_sum(z);

@@ -41,38 +41,22 @@ void route_topk_kernel(const float* __restrict__ logits, int T, int E, int k, in
     const int t1 = min(T, t0 + tokens_per_block);
     for (int t = t0 + wave; t < t1; t += ROUTE_WAVES) {
         const float* row = logits + (size_t)t * E;
-        uint64_t key[NV];
+        uint32_t ord[1][NV];
 #pragma unroll
         for (int i = 0; i < NV; ++i) {
             const int e = lane + WAVE * i;
-            key[i] = 0;
-            if (e < E) key[i] = ((uint64_t)ordered_bits(row[e]) << 32) | (uint32_t)(~e);
+            ord[0][i] = e < E ? ordered_bits(row[e]) : 0u;
         }
-        int my_e = 0;
-        float my_v = 0.0f;
-        for (int j = 0; j < k; ++j) {
-            uint64_t m = 0;
-#pragma unroll
-            for (int i = 0; i < NV; ++i) m = key[i] > m ? key[i] : m;
-            m = wave_max_u64(m);
-            const int win = (int)(~(uint32_t)m);
-            if ((win & 63) == lane) {
-#pragma unroll
-                for (int i = 0; i < NV; ++i)
-                    if (i == (win >> 6)) key[i] = 0;
-            }
-            if (lane == j) {
-                my_e = win;
-                my_v = from_ordered((uint32_t)(m >> 32));
-            }
-        }
-        const float v0 = __shfl(my_v, 0, 64);
-        const float z = lane < k ? expf(my_v - v0) : 0.0f;
+        int my_e[1] = {0};
+        float my_v[1] = {0.0f};
+        wave_topk<NV, 1>(ord, k, lane, my_e, my_v);
+        const float v0 = __shfl(my_v[0], 0, 64);
+        const float z = lane < k ? expf(my_v[0] - v0) : 0.0f;
         const float s = wave_sum(z);
         if (lane < k) {
-            topk_ids[(size_t)t * k + lane] = my_e;
+            topk_ids[(size_t)t * k + lane] = my_e[0];
             topk_w[(size_t)t * k + lane] = z / s;
-            atomicAdd(&hist[my_e], 1);
+            atomicAdd(&hist[my_e[0]], 1);
         }
     }
     __syncthreads();
@@ -202,24 +186,46 @@ void router_topk_kernel(const uint16_t* __restrict__ x, const uint16_t* __restri
         lds_barrier();                                            // ... every wave's, and slot d - 1 is free
         if (d + 1 < KD) issue(d + 1, slot ^ 1);
         const uint32_t st = sbase + slot * SB;
-        const int steps = min(4, (H - 64 * d) / 16);
-        for (int s = 0; s < steps; ++s) {
-            const uint32_t pc = (uint32_t)(((2 * s + g) ^ swn) * 16);
-            u32x4 af[2], bf[CT];
+        // 4 steps of 16 k, or 2 in a last slot of 32 k (H % 64 == 32): its
+        // steps 2 and 3 read whatever the slot holds and multiply zeros
+        // instead
+        const bool full = H - 64 * d >= 64;
+        // fragments of step s into buffer s & 1; the reads of step s + 1 go
+        // out after the wait for step s and before its MFMAs, so their LDS
+        // latency passes under the MFMAs (one wave per SIMD: nothing else
+        // would hide it).  Every read is waited for on every path.
+        u32x4 af[2][2], bf[2][CT];
+        auto rd = [&](auto s_c) {
+            constexpr int S = decltype(s_c)::value, B = S & 1;
+            const uint32_t pc = (uint32_t)(((2 * S + g) ^ swn) * 16);
 #pragma unroll
-            for (int r = 0; r < 2; ++r) af[r] = ds_read16<0>(st + arow[r] + pc);
+            for (int r = 0; r < 2; ++r) af[B][r] = ds_read16<0>(st + arow[r] + pc);
 #pragma unroll
-            for (int c = 0; c < CT; ++c) bf[c] = ds_read16<0>(st + brow[c] + pc);
+            for (int c = 0; c < CT; ++c) bf[B][c] = ds_read16<0>(st + brow[c] + pc);
+        };
+        rd(std::integral_constant<int, 0>{});
+        static_for<4>([&](auto s_c) {
+            constexpr int S = decltype(s_c)::value, B = S & 1;
             lds_wait_all();
 #pragma unroll
-            for (int r = 0; r < 2; ++r) tie_after_wait(af[r]);
+            for (int r = 0; r < 2; ++r) tie_after_wait(af[B][r]);
 #pragma unroll
-            for (int c = 0; c < CT; ++c) tie_after_wait(bf[c]);
+            for (int c = 0; c < CT; ++c) tie_after_wait(bf[B][c]);
+            if constexpr (S >= 2) {
+                if (!full) {                                      // (zeros on both sides: no 0 x NaN)
+#pragma unroll
+                    for (int r = 0; r < 2; ++r) af[B][r] = u32x4{0, 0, 0, 0};
+#pragma unroll
+                    for (int c = 0; c < CT; ++c) bf[B][c] = u32x4{0, 0, 0, 0};
+                }
+            }
+            if constexpr (S + 1 < 4) rd(std::integral_constant<int, S + 1>{});
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int r = 0; r < 2; ++r)
 #pragma unroll
-                for (int c = 0; c < CT; ++c) acc[r][c] = mfma_bf16(af[r], bf[c], acc[r][c]);
-        }
+                for (int c = 0; c < CT; ++c) acc[r][c] = mfma_bf16(af[B][r], bf[B][c], acc[r][c]);
+        });
     }
     lds_barrier();                                                // every wave done with the last slot
 
@@ -243,54 +249,36 @@ void router_topk_kernel(const uint16_t* __restrict__ x, const uint16_t* __restri
         }
     }
     // top-k per token, one wave per token: the selection of route_topk_kernel,
-    // two tokens at a time (r and r + 4) so that the two chains of k
-    // dependent wave reductions interleave (one wave per SIMD here: nothing
-    // else hides their latency)
+    // four tokens at a time (r, r + 4, r + 8, r + 12) so that their chains of
+    // k dependent wave reductions interleave (one wave per SIMD here: nothing
+    // else hides their latency); a slot past the block's rows repeats the
+    // last row and stores nothing
     constexpr int NV = E / 64;
     constexpr int TS = R_THREADS / 64;
-    for (int r = wave; r < rows; r += 2 * TS) {
-        const bool two = r + TS < rows;
-        const int rr[2] = {r, two ? r + TS : r};
-        uint64_t key[2][NV];
+    constexpr int RQ = 4;
+    for (int r = wave; r < rows; r += RQ * TS) {
+        int rr[RQ];
 #pragma unroll
-        for (int q = 0; q < 2; ++q)
+        for (int q = 0; q < RQ; ++q) rr[q] = min(r + q * TS, rows - 1);
+        uint32_t ord[RQ][NV];
 #pragma unroll
-            for (int i = 0; i < NV; ++i) {
-                const int e = lane + 64 * i;
-                key[q][i] = ((uint64_t)ordered_bits(lg[rr[q] * LD + e]) << 32) | (uint32_t)(~e);
-            }
-        int my_e[2] = {0, 0};
-        float my_v[2] = {0.0f, 0.0f};
-        for (int j = 0; j < k; ++j) {
-            uint64_t m[2];
+        for (int q = 0; q < RQ; ++q)
 #pragma unroll
-            for (int q = 0; q < 2; ++q) {
-                m[q] = 0;
+            for (int i = 0; i < NV; ++i) ord[q][i] = ordered_bits(lg[rr[q] * LD + lane + 64 * i]);
+        int my_e[RQ];
+        float my_v[RQ];
 #pragma unroll
-                for (int i = 0; i < NV; ++i) m[q] = key[q][i] > m[q] ? key[q][i] : m[q];
-            }
-            m[0] = wave_max_u64(m[0]);
-            m[1] = wave_max_u64(m[1]);
-#pragma unroll
-            for (int q = 0; q < 2; ++q) {
-                const int win = (int)(~(uint32_t)m[q]);
-                if ((win & 63) == lane) {
-#pragma unroll
-                    for (int i = 0; i < NV; ++i)
-                        if (i == (win >> 6)) key[q][i] = 0;
-                }
-                if (lane == j) {
-                    my_e[q] = win;
-                    my_v[q] = from_ordered((uint32_t)(m[q] >> 32));
-                }
-            }
+        for (int q = 0; q < RQ; ++q) {
+            my_e[q] = 0;
+            my_v[q] = 0.0f;
         }
+        wave_topk<NV, RQ>(ord, k, lane, my_e, my_v);
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
+        for (int q = 0; q < RQ; ++q) {
             const float v0 = __shfl(my_v[q], 0, 64);
             const float z = lane < k ? expf(my_v[q] - v0) : 0.0f;
             const float sum = wave_sum(z);
-            if (lane < k && (q == 0 || two)) {
+            if (lane < k && r + q * TS < rows) {
                 const size_t t = (size_t)(t0 + rr[q]);
                 topk_ids[t * k + lane] = my_e[q];
                 topk_w[t * k + lane] = z / sum;

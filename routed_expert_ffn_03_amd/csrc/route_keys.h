@@ -1,9 +1,8 @@
-// Top-k selection keys shared by the router kernels (internal header).
+// Top-k selection shared by the router kernels (internal header).
 //
-// A logit and its expert index packed into one 64-bit key,
-//   key = (order-preserving bits of the logit) << 32 | ~expert,
-// so that one unsigned max over a wave yields the largest logit and, among
-// equal logits, the lowest expert index (-0 and +0 compare equal).
+// A logit becomes its order-preserving 32-bit pattern (-0 and +0 equal), so
+// that an unsigned max picks the largest logit; among equal logits the
+// lowest expert index is taken.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -21,40 +20,63 @@ __device__ __forceinline__ float from_ordered(uint32_t o) {
     return __uint_as_float((o & 0x80000000u) ? (o ^ 0x80000000u) : ~o);
 }
 
-// Wave-wide max of a 64-bit key without LDS round trips: four DPP steps give
-// every lane the max of its 16-lane row (lane ^ 1, lane ^ 2, the other quad
-// of its 8 by the half-row mirror, the other 8 by the row mirror), then the
-// row swaps of gfx950 combine rows 0/1 and 2/3, and the two halves.  Called
+// Wave-wide max of a 32-bit value, the same in every lane (a scalar): four
+// DPP max steps leave every lane of a 16-lane row with the row's max, then
+// the four rows' maxima are read out and combined on the scalar unit.  Called
 // with every lane active.
-template <int CTRL>
-__device__ __forceinline__ uint64_t dpp_max_u64(uint64_t v) {
-    const uint32_t lo = __builtin_amdgcn_update_dpp(0u, (uint32_t)v, CTRL, 0xF, 0xF, false);
-    const uint32_t hi = __builtin_amdgcn_update_dpp(0u, (uint32_t)(v >> 32), CTRL, 0xF, 0xF, false);
-    const uint64_t o = ((uint64_t)hi << 32) | lo;
-    return o > v ? o : v;
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));   // quad_perm [1, 0, 3, 2]
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));   // quad_perm [2, 3, 0, 1]
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));  // row_half_mirror
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));  // row_mirror
+    const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
+    const uint32_t b = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+    const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)v, 32);
+    const uint32_t d = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+    return max(max(a, b), max(c, d));
 }
 
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-    v = dpp_max_u64<0xB1>(v);                         // quad_perm [1, 0, 3, 2]
-    v = dpp_max_u64<0x4E>(v);                         // quad_perm [2, 3, 0, 1]
-    v = dpp_max_u64<0x141>(v);                        // row_half_mirror
-    v = dpp_max_u64<0x140>(v);                        // row_mirror
-    {
-        // both operands the same register: one result holds rows (0, 0, 2, 2),
-        // the other rows (1, 1, 3, 3)
-        const auto lo = __builtin_amdgcn_permlane16_swap((uint32_t)v, (uint32_t)v, false, false);
-        const auto hi = __builtin_amdgcn_permlane16_swap((uint32_t)(v >> 32), (uint32_t)(v >> 32), false, false);
-        const uint64_t a = ((uint64_t)hi[0] << 32) | lo[0], b = ((uint64_t)hi[1] << 32) | lo[1];
-        v = a > b ? a : b;
+// Top-k of Q tokens' logits held by one wave, the tokens' rounds interleaved:
+// ord[q][i] = ordered_bits of the logit of expert lane + 64 i of token q (0
+// for padding and for entries already taken).  Round j takes, per token, the
+// largest ord and among equal ones the lowest expert index -- the same order
+// as one unsigned max over the 64-bit keys (ord << 32 | ~expert): M = wave
+// max of ord; the winner is the smallest i whose ballot of (ord == M) is not
+// empty, and the lowest lane in that ballot.  Lane j keeps round j's expert
+// and logit.  Called with every lane active; logits must not be NaN.
+template <int NV, int Q>
+__device__ __forceinline__ void wave_topk(uint32_t (&ord)[Q][NV], int k, int lane, int (&my_e)[Q], float (&my_v)[Q]) {
+    for (int j = 0; j < k; ++j) {
+        uint32_t M[Q];
+#pragma unroll
+        for (int q = 0; q < Q; ++q) {
+            uint32_t m = ord[q][0];
+#pragma unroll
+            for (int i = 1; i < NV; ++i) m = max(m, ord[q][i]);
+            M[q] = wave_max_u32(m);
+        }
+#pragma unroll
+        for (int q = 0; q < Q; ++q) {
+            int wi = 0;
+            uint64_t b = 0;
+#pragma unroll
+            for (int i = NV - 1; i >= 0; --i) {                  // the smallest i with a match wins
+                const uint64_t bi = __builtin_amdgcn_ballot_w64(ord[q][i] == M[q]);
+                if (bi) {
+                    wi = i;
+                    b = bi;
+                }
+            }
+            const int wl = (int)__builtin_ctzll(b);
+#pragma unroll
+            for (int i = 0; i < NV; ++i)
+                if (i == wi && lane == wl) ord[q][i] = 0;
+            if (lane == j) {
+                my_e[q] = wl + 64 * wi;
+                my_v[q] = from_ordered(M[q]);
+            }
+        }
     }
-    {
-        // lower and upper 32 lanes
-        const auto lo = __builtin_amdgcn_permlane32_swap((uint32_t)v, (uint32_t)v, false, false);
-        const auto hi = __builtin_amdgcn_permlane32_swap((uint32_t)(v >> 32), (uint32_t)(v >> 32), false, false);
-        const uint64_t a = ((uint64_t)hi[0] << 32) | lo[0], b = ((uint64_t)hi[1] << 32) | lo[1];
-        v = a > b ? a : b;
-    }
-    return v;
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
