@@ -107,7 +107,8 @@ def parse():
 
 def workload_desc(shape, thr, pairs=False):
     router = "Zipf(s=1.1) bias, beta=0.4" if shape.router == "zipf" else "N(0,1), no skew"
-    layout = ("row pairs interleaved every 32 k (MOE_WFMT_BF16_PAIRS)" if pairs else "plain row-major") \
+    layout = ("row pairs interleaved every 32 k, W_down stored fp16 (MOE_WFMT_BF16_PAIRS)" if pairs
+              else "plain row-major") \
         if shape.wfmt == "bf16" else "3-bit groups of 128 (MOE_WFMT_Q3G128)"
     return {
         "workload": f"{shape.name}: routed-expert layer, {shape.T} tokens, hidden {shape.H}, "
@@ -118,8 +119,9 @@ def workload_desc(shape, thr, pairs=False):
 
 
 def pack_pairs(dev_w):
-    """bf16 expert weights -> the row-pair layout (moe_pack_bf16_pairs), one
-    matrix family at a time, the plain copy freed as soon as it is packed."""
+    """bf16 expert weights -> the row-pair layout (moe_pack_bf16_pairs; W_down
+    converted to fp16), one matrix family at a time, the plain copy freed as
+    soon as it is packed."""
     import torch
 
     import routed_expert_ffn_03_amd as moe
@@ -127,7 +129,7 @@ def pack_pairs(dev_w):
     for name in list(dev_w):
         src = dev_w[name]
         dst = torch.empty_like(src)
-        moe.moe_pack_bf16_pairs(src, dst)
+        moe.moe_pack_bf16_pairs(src, dst, to_fp16=(name == "down"))
         torch.cuda.synchronize()
         dev_w[name] = dst
         del src

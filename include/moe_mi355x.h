@@ -67,7 +67,7 @@ typedef int32_t moe_status;
 /* Expert weight storage formats accepted by moe_grouped_ffn. */
 #define MOE_WFMT_BF16   0   /* bf16 matrices [E, out, in]                       */
 #define MOE_WFMT_Q3G128 1   /* 3-bit codes, groups of 128 along `in`, fp16 scale */
-#define MOE_WFMT_BF16_PAIRS 2 /* bf16 matrices in the row-pair layout (moe_pack_bf16_pairs) */
+#define MOE_WFMT_BF16_PAIRS 2 /* row-pair layout (moe_pack_bf16_pairs): gate/up bf16, down fp16 */
 
 #define MOE_MAX_TOPK    32
 #define MOE_MAX_EXPERTS 1024
@@ -181,10 +181,12 @@ moe_status moe_permute(const int32_t* topk_ids, int T, int E, int k,
  * x          bf16 [T, H]
  * w_gate     MOE_WFMT_BF16: bf16 [E, I, H];   MOE_WFMT_Q3G128: uint32 [E, I, H/128, 13];
  *            MOE_WFMT_BF16_PAIRS: the bf16 [E, I, H] values in the row-pair
- *            layout that moe_pack_bf16_pairs writes (same size)
+ *            layout (moe_pack_bf16_pairs with to_fp16 = 0; same size)
  * w_up       same as w_gate
  * w_down     MOE_WFMT_BF16: bf16 [E, H, I];   MOE_WFMT_Q3G128: uint32 [E, H, I/128, 13];
- *            MOE_WFMT_BF16_PAIRS: [E, H, I] in the row-pair layout
+ *            MOE_WFMT_BF16_PAIRS: the bf16 [E, H, I] values converted to fp16
+ *            as the down projection converts them (below), in the row-pair
+ *            layout (moe_pack_bf16_pairs with to_fp16 = 1)
  * s_gate, s_up, s_down   fp16 scales [E, I, H/128] / [E, H, I/128] for
  *            MOE_WFMT_Q3G128 (must be NULL for the bf16 formats).  3-bit group
  *            layout: 13 words per 128 weights; field j of a word at bits
@@ -296,7 +298,7 @@ moe_status moe_grouped_ffn_noalloc(const uint16_t* x, int wfmt, const void* w_ga
 /*
  * moe_pack_bf16_pairs -- copy bf16 matrices into the row-pair layout of
  * MOE_WFMT_BF16_PAIRS (a storage layout of the same values; the pages fix
- * none for the bf16 experts).
+ * none for the bf16 experts), optionally converted to fp16.
  *
  * src   bf16 [mats, rows, cols], plain row-major (e.g. W_gate with mats = E,
  *       rows = I, cols = H; W_down with rows = H, cols = I).
@@ -304,12 +306,17 @@ moe_status moe_grouped_ffn_noalloc(const uint16_t* x, int wfmt, const void* w_ga
  *       m*rows*cols + ((r/2)*(cols/32) + c/32)*64 + (r%2)*32 + c%32,
  *       i.e. rows 2p and 2p+1 alternate every 32 columns, so that 32 columns
  *       of a row pair fill one 128-byte line.
+ * to_fp16  0: dst holds the bf16 values.  1: each value converted to fp16
+ *       toward zero (exact for |w| in [2^-14, 65504], smaller magnitudes
+ *       truncated, larger ones saturated) -- bit for bit what the down
+ *       projection of MOE_WFMT_BF16 computes from bf16 W_down; use it for
+ *       w_down of MOE_WFMT_BF16_PAIRS and 0 for w_gate and w_up.
  * rows even and >= 2, cols a multiple of 32, both pointers 16-byte aligned,
- * the two buffers not overlapping (no in-place packing), else
- * MOE_ERR_INVALID_ARG.  One launch on `stream`; done once when weights are
- * loaded, not per layer call.
+ * the two buffers not overlapping (no in-place packing), to_fp16 0 or 1,
+ * else MOE_ERR_INVALID_ARG.  One launch on `stream`; done once when weights
+ * are loaded, not per layer call.
  */
-moe_status moe_pack_bf16_pairs(const uint16_t* src, uint16_t* dst, int64_t mats, int rows, int cols,
+moe_status moe_pack_bf16_pairs(const uint16_t* src, uint16_t* dst, int64_t mats, int rows, int cols, int to_fp16,
                                void* stream);
 
 /*

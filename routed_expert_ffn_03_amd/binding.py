@@ -74,7 +74,7 @@ def lib() -> ctypes.CDLL:
         L.moe_combine.restype = i32
         L.moe_combine.argtypes = [vp, vp, vp, i32, i32, i32, vp, vp]
         L.moe_pack_bf16_pairs.restype = i32
-        L.moe_pack_bf16_pairs.argtypes = [vp, vp, ctypes.c_int64, i32, i32, vp]
+        L.moe_pack_bf16_pairs.argtypes = [vp, vp, ctypes.c_int64, i32, i32, i32, vp]
         _lib = L
     return _lib
 
@@ -262,9 +262,10 @@ def moe_combine(y_sorted, topk_w, pair_to_sorted, out, stream=None):
                              _stream(stream)), "moe_combine")
 
 
-def moe_pack_bf16_pairs(src, dst, stream=None):
+def moe_pack_bf16_pairs(src, dst, to_fp16=False, stream=None):
     """Copy bf16 matrices ``src`` [..., rows, cols] into ``dst`` (same shape) in the row-pair layout
-    that ``MOE_WFMT_BF16_PAIRS`` reads: rows 2p and 2p+1 alternate every 32 columns."""
+    that ``MOE_WFMT_BF16_PAIRS`` reads: rows 2p and 2p+1 alternate every 32 columns; with
+    ``to_fp16`` the values are converted to fp16 toward zero (that format's W_down)."""
     for t, name in ((src, "src"), (dst, "dst")):
         if not (isinstance(t, torch.Tensor) and t.is_cuda and t.is_contiguous() and t.element_size() == 2):
             raise ValueError(f"{name}: expected a contiguous 16-bit GPU tensor")
@@ -272,5 +273,5 @@ def moe_pack_bf16_pairs(src, dst, stream=None):
         raise ValueError(f"src {tuple(src.shape)} and dst {tuple(dst.shape)}: same shape [..., rows, cols] expected")
     rows, cols = int(src.shape[-2]), int(src.shape[-1])
     mats = src.numel() // (rows * cols) if rows * cols else 0
-    _check(lib().moe_pack_bf16_pairs(_ptr(src), _ptr(dst), mats, rows, cols, _stream(stream)),
+    _check(lib().moe_pack_bf16_pairs(_ptr(src), _ptr(dst), mats, rows, cols, int(bool(to_fp16)), _stream(stream)),
            "moe_pack_bf16_pairs")

@@ -275,17 +275,18 @@ moe_status moe_grouped_ffn_noalloc(const uint16_t* x, int wfmt, const void* w_ga
     return hip_status(err);
 }
 
-moe_status moe_pack_bf16_pairs(const uint16_t* src, uint16_t* dst, int64_t mats, int rows, int cols,
+moe_status moe_pack_bf16_pairs(const uint16_t* src, uint16_t* dst, int64_t mats, int rows, int cols, int to_fp16,
                                void* stream) {
     if (!src || !dst || mats < 1 || rows < 2 || rows % 2 != 0 || cols < 32 || cols % 32 != 0)
         return MOE_ERR_INVALID_ARG;
+    if (to_fp16 != 0 && to_fp16 != 1) return MOE_ERR_INVALID_ARG;
     if (((uintptr_t)src | (uintptr_t)dst) & 15) return MOE_ERR_INVALID_ARG;
     const unsigned long long per = (unsigned long long)rows * (unsigned long long)cols * 2ull;
     if ((unsigned long long)mats > (1ull << 62) / per) return MOE_ERR_INVALID_ARG;
     const uintptr_t bytes = (uintptr_t)((unsigned long long)mats * per);
     const uintptr_t s0 = (uintptr_t)src, d0 = (uintptr_t)dst;
     if (s0 < d0 + bytes && d0 < s0 + bytes) return MOE_ERR_INVALID_ARG;     // overlapping buffers
-    return hip_status(moe::launch_pack_pairs(src, dst, mats, rows, cols, reinterpret_cast<hipStream_t>(stream)));
+    return hip_status(moe::launch_pack_pairs(src, dst, mats, rows, cols, to_fp16, reinterpret_cast<hipStream_t>(stream)));
 }
 
 moe_status moe_combine(const uint16_t* y_sorted, const float* topk_w, const int32_t* pair_to_sorted, int T, int k,

@@ -6,7 +6,7 @@
 // entry: batches sharing one read of the expert's weights), each M-tile
 // multiplied with 256 weight rows at a time (phase 1: 128 gate rows and the
 // matching 128 up rows, SwiGLU applied in registers; phase 2: 256 rows of
-// W_down, converted bf16 -> fp16 for the fp16 products), operands staged
+// W_down, converted bf16 -> fp16 for the fp16 products unless stored fp16), operands staged
 // through an LDS ring of five 32-k stages by direct-to-LDS buffer loads.
 //
 // Eight waves per block, one block per CU, so two waves share each SIMD's
@@ -28,7 +28,10 @@
 // alternate every 32 k) make each weight load instruction cover 8 whole
 // 128-byte lines instead of 16 half lines; the per-CU load path moves about
 // one line per clock either way, so the weight loads cost half as much of it.
-// The LDS layout and everything after the loads are the same for both.
+// The LDS layout and everything after the loads are the same for both.  That
+// format also stores W_down already converted to fp16 (the same conversion
+// as below, done once when the weights are packed), which takes the 16
+// conversions per stage off the waves that feed the other group's MFMAs.
 //
 // Per round kt (one 32-k stage):
 //   half A: group 0 computes stage kt; group 1 reads its fragments of stage
@@ -190,8 +193,10 @@ void ffn_fat8_kernel(FfnArgs a) {
                             tie_after_wait(fb[S][0]);
                             tie_after_wait(fb[S][1]);
                             if constexpr (PHASE == 2) {
-                                fb[S][0] = bf16x8_to_f16x8(fb[S][0]);
-                                fb[S][1] = bf16x8_to_f16x8(fb[S][1]);
+                                if (!a.pairs) {                  // (weight format 2 stores W_down as fp16)
+                                    fb[S][0] = bf16x8_to_f16x8(fb[S][0]);
+                                    fb[S][1] = bf16x8_to_f16x8(fb[S][1]);
+                                }
                             }
                         });
                     }

@@ -49,7 +49,7 @@ struct FfnArgs {
     const uint16_t* sd;
     const int32_t* sorted_pair;
     int T, k, H, I, E;
-    int pairs;                    // bf16 matrices in the row-pair layout (weight format 2)
+    int pairs;                    // weight format 2: row-pair layout, gate/up bf16, W_down fp16
     uint16_t* act;
     uint16_t* y;
     uint16_t* xq;                 // 3-bit thin path: x rows in pair-slot order per 128-group

@@ -44,7 +44,8 @@ hipError_t launch_ffn_plan(const FfnLaunch& a, hipStream_t s);
 hipError_t launch_ffn_phase(const FfnLaunch& a, int phase, hipStream_t s);   // 1 = gate/up, 2 = down
 
 // bf16 matrices [mats, rows, cols] -> the row-pair layout (pack.hip)
-hipError_t launch_pack_pairs(const uint16_t* src, uint16_t* dst, int64_t mats, int rows, int cols, hipStream_t s);
+hipError_t launch_pack_pairs(const uint16_t* src, uint16_t* dst, int64_t mats, int rows, int cols, int to_fp16,
+                             hipStream_t s);
 
 hipError_t launch_combine(const uint16_t* y, const float* w, const int32_t* p2s, int T, int k, int H,
                           float* out, hipStream_t s);

@@ -41,9 +41,11 @@ constexpr int ST_K = 64;                             // k per chunk: one line of
 constexpr uint32_t ST_CHUNK = 32 * ST_K * 2;         // 4 KB: the item's 32 weight rows
 constexpr int ST_SLOTS = 2;
 
+// phase 2: b already holds fp16 weights (converted after the LDS read, or
+// stored fp16 by weight format 2)
 template <int PHASE>
 __device__ __forceinline__ f32x16 st_mma(u32x4 a, u32x4 b, f32x16 c) {
-    return PHASE == 1 ? mfma_bf16(a, b, c) : mfma_f16(a, bf16x8_to_f16x8(b), c);
+    return PHASE == 1 ? mfma_bf16(a, b, c) : mfma_f16(a, b, c);
 }
 
 // One work item (wave-uniform: scalar registers).
@@ -204,6 +206,12 @@ void ffn_stream_kernel(FfnArgs a) {
         lds_wait_all();
 #pragma unroll
         for (int s = 0; s < 4; ++s) tie_after_wait(b[s]);
+        if constexpr (PHASE == 2) {
+            if (!pairs) {                                  // W_down bf16 -> fp16 (format 2 stores fp16)
+#pragma unroll
+                for (int s = 0; s < 4; ++s) b[s] = bf16x8_to_f16x8(b[s]);
+            }
+        }
 #pragma unroll
         for (int s = 0; s < 4; ++s) acc = st_mma<PHASE>(ra[s], b[s], acc);
         sl ^= 1;

@@ -204,7 +204,7 @@ def test_route_permute_plan_rejects(L):
 
 def test_pack_rejects(L):
     i64 = ctypes.c_int64
-    call = lambda src, dst, mats, rows, cols: L.moe_pack_bf16_pairs(src, dst, i64(mats), rows, cols, None)
+    call = lambda src, dst, mats, rows, cols, f16=0: L.moe_pack_bf16_pairs(src, dst, i64(mats), rows, cols, f16, None)
     D = FAKE + (1 << 30)                               # a destination far from FAKE
     assert call(None, D, 1, 2, 32) == moe.MOE_ERR_INVALID_ARG
     assert call(FAKE, None, 1, 2, 32) == moe.MOE_ERR_INVALID_ARG
@@ -215,3 +215,4 @@ def test_pack_rejects(L):
     assert call(FAKE, D + 2, 1, 2, 32) == moe.MOE_ERR_INVALID_ARG
     assert call(FAKE, FAKE, 1, 2, 32) == moe.MOE_ERR_INVALID_ARG       # in place
     assert call(FAKE, FAKE + 64, 1, 2, 32) == moe.MOE_ERR_INVALID_ARG  # overlapping (128 bytes each)
+    assert call(FAKE, D, 1, 2, 32, 2) == moe.MOE_ERR_INVALID_ARG       # to_fp16 is 0 or 1

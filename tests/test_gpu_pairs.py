@@ -1,12 +1,15 @@
-"""The bf16 row-pair weight layout (MOE_WFMT_BF16_PAIRS) on the GPU.
+"""The row-pair weight format (MOE_WFMT_BF16_PAIRS) on the GPU.
 
-``moe_pack_bf16_pairs`` is a pure permutation of 16-bit values: it is
-checked bit for bit against the layout written out with numpy reshapes.  The
-layer with packed weights does the same arithmetic in the same order as with
-plain bf16 weights (only the addresses its loads read from differ), so every
-output must equal the plain layer's bit for bit; the small layers are also
-compared with the float64 oracle at the bf16 bar (max|err| / rms(ref) <=
-1e-2).
+``moe_pack_bf16_pairs`` is a permutation of 16-bit values, optionally with a
+bf16 -> fp16 conversion toward zero: it is checked bit for bit against the
+layout written out with numpy reshapes and the conversion written out with
+numpy's float16 (a round-to-nearest step taken back toward zero where it went
+away).  The layer with packed weights (W_down converted to fp16, as the
+format stores it) does the same arithmetic in the same order as with plain
+bf16 weights -- the plain path converts W_down with the same instruction
+after loading it -- so every output must equal the plain layer's bit for bit;
+the small layers are also compared with the float64 oracle at the bf16 bar
+(max|err| / rms(ref) <= 1e-2).
 """
 import numpy as np
 import pytest
@@ -35,11 +38,22 @@ def pairs_layout(a: np.ndarray) -> np.ndarray:
     return a.reshape(m, r // 2, 2, c // 32, 32).transpose(0, 1, 3, 2, 4).reshape(-1)
 
 
+def bf16_to_f16_toward_zero(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns -> fp16 bit patterns, rounded toward zero (finite fp16
+    results saturate at 65504; infinities and zeros keep their sign)."""
+    f = (bits.astype(np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    with np.errstate(over="ignore"):
+        h = f.astype(np.float16)
+    away = np.abs(h.astype(np.float64)) > np.abs(f)
+    h = np.where(away, np.nextafter(h, np.float16(0)), h)
+    return h.astype(np.float16).view(np.uint16)
+
+
 def packed(w: dict) -> dict:
     out = {}
     for n, t in w.items():
         d = torch.empty_like(t)
-        moe.moe_pack_bf16_pairs(t, d)
+        moe.moe_pack_bf16_pairs(t, d, to_fp16=(n == "down"))
         out[n] = d
     torch.cuda.synchronize()
     return out
@@ -55,6 +69,24 @@ def test_pack_matches_layout(shape):
     torch.cuda.synchronize()
     assert np.array_equal(dst.cpu().numpy().reshape(-1), pairs_layout(a))
     assert np.array_equal(src.cpu().numpy(), a)                      # the source is left as it was
+
+
+def test_pack_to_fp16():
+    """Finite bf16 values over fp16's whole range and beyond: normal, subnormal
+    and underflowing magnitudes, values past 65504, signed zeros, infinities."""
+    rng = np.random.default_rng(11)
+    mag = np.exp2(rng.uniform(-30.0, 20.0, size=(3, 64, 256)))
+    v = (mag * rng.choice([-1.0, 1.0], size=mag.shape)).astype(np.float32)
+    v.reshape(-1)[:6] = [0.0, -0.0, np.inf, -np.inf, 65504.0, 65520.0]
+    bits = (v.view(np.uint32) >> 16).astype(np.uint16)             # bf16 by truncation
+    src = torch.from_numpy(bits.view(np.int16)).cuda()
+    dst = torch.empty_like(src)
+    moe.moe_pack_bf16_pairs(src, dst, to_fp16=True)
+    torch.cuda.synchronize()
+    want = pairs_layout(bf16_to_f16_toward_zero(bits).view(np.int16))
+    got = dst.cpu().numpy().reshape(-1)
+    bad = np.flatnonzero(got != want)
+    assert bad.size == 0, f"{bad.size} values differ, e.g. index {bad[:4]}: got {got[bad[:4]]} want {want[bad[:4]]}"
 
 
 SMALL = [
