@@ -238,8 +238,9 @@ moe_status moe_ffn_plan(const int32_t* expert_offsets, int T, int E, int k, int 
  * one call, with the same arguments (H, I, wfmt and fat_threshold as for the
  * plan) and the same results bit for bit.  For T <= 64 tokens (decode
  * batches) the three run in a single launch on one block, with the route
- * lists kept on chip between them; larger batches run the three entry points
- * in order.  Follow it with moe_ffn_gate_up, moe_ffn_down and moe_combine.
+ * lists kept on chip between them; larger batches run the gate, the permute
+ * and the plan in order, the plan writing expert_counts from the route lists.
+ * Follow it with moe_ffn_gate_up, moe_ffn_down and moe_combine.
  * Errors: those of the three calls (NULL outputs, shapes, workspace size).
  */
 moe_status moe_route_permute_plan(const float* logits, int T, int E, int k, int H, int I, int wfmt,

@@ -231,13 +231,17 @@ moe_status moe_route_permute_plan(const float* logits, int T, int E, int k, int 
                                                          expert_counts, expert_offsets, sorted_pair, pair_to_sorted,
                                                          pp, s));
     }
-    st = moe_route_topk(logits, T, E, k, topk_ids, topk_w, expert_counts, stream);
-    if (st == MOE_OK)
-        st = moe_permute(topk_ids, T, E, k, expert_offsets, sorted_pair, pair_to_sorted, workspace, workspace_bytes,
-                         stream);
-    if (st == MOE_OK)
-        st = moe_ffn_plan(expert_offsets, T, E, k, H, I, wfmt, fat_threshold, workspace, workspace_bytes, stream);
-    return st;
+    // larger batches: the gate (ids and weights only), the permute, then the
+    // plan, which also writes the histogram from the route lists (the gate's
+    // own histogram would merge ~T/16 block histograms by global atomics)
+    if (moe::launch_route_topk(logits, T, E, k, topk_ids, topk_w, nullptr, s) != hipSuccess) return MOE_ERR_HIP;
+    st = moe_permute(topk_ids, T, E, k, expert_offsets, sorted_pair, pair_to_sorted, workspace, workspace_bytes,
+                     stream);
+    if (st != MOE_OK) return st;
+    a.offsets = expert_offsets;
+    a.fat_threshold = fat_threshold;
+    a.counts = expert_counts;
+    return hip_status(moe::launch_ffn_plan(a, s));
 }
 
 moe_status moe_grouped_ffn_noalloc(const uint16_t* x, int wfmt, const void* w_gate, const void* w_up,

@@ -59,13 +59,14 @@ namespace {
 
 __global__ __launch_bounds__(1024)
 void build_tiles_kernel(const int32_t* __restrict__ offsets, int E, int thr, FfnHeader* __restrict__ hdr,
-                        MTile* __restrict__ fat, MTile* __restrict__ thin) {
+                        MTile* __restrict__ fat, MTile* __restrict__ thin, int32_t* __restrict__ counts) {
     __shared__ int scratch[16];
     const int e = threadIdx.x;
     int n = 0, nf = 0, nt = 0, r0 = 0;
     if (e < E) {
         r0 = offsets[e];
         n = offsets[e + 1] - r0;
+        if (counts) counts[e] = n;                       // the load histogram, when asked for
         if (n >= thr) nf = (n + FAT_BM - 1) / FAT_BM;
         else nt = (n + THIN_BM - 1) / THIN_BM;
     }
@@ -1091,7 +1092,7 @@ hipError_t launch_ffn_plan(const FfnLaunch& a, hipStream_t s) {
     build_tiles_kernel<<<1, 1024, 0, s>>>(a.offsets, a.E, a.fat_threshold,
                                           reinterpret_cast<FfnHeader*>(ws + L.hdr),
                                           reinterpret_cast<MTile*>(ws + L.fat),
-                                          reinterpret_cast<MTile*>(ws + L.thin));
+                                          reinterpret_cast<MTile*>(ws + L.thin), a.counts);
     return hipGetLastError();
 }
 

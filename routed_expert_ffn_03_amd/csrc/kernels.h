@@ -10,6 +10,7 @@ namespace moe {
 constexpr int MAX_EXPERTS = 1024;
 constexpr int MAX_TOPK = 32;
 
+// counts == nullptr (only for T > 64): ids and weights only, no histogram
 hipError_t launch_route_topk(const float* logits, int T, int E, int k, int32_t* topk_ids,
                              float* topk_w, int32_t* counts, hipStream_t s);
 
@@ -37,6 +38,7 @@ struct FfnLaunch {
     int T, E, k, H, I, fat_threshold;
     uint16_t* y;
     void* ws;                       // FFN part of the workspace
+    int32_t* counts;                // plan only: per-expert row counts written too (nullable)
 };
 
 size_t ffn_ws_bytes(int T, int E, int k, int H, int I, int wfmt);

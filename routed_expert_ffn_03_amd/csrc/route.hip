@@ -25,12 +25,14 @@ constexpr int ROUTE_THREADS = 256;
 constexpr int ROUTE_WAVES = ROUTE_THREADS / WAVE;
 
 // tokens_per_block tokens per block; waves take tokens round-robin.
-// direct_counts: the grid is one block covering all tokens, so the block
-// histogram is the answer (no zeroing pass, no atomics).
+// hist_mode 0: the block histograms merge into counts with integer atomics;
+// 1: the grid is one block covering all tokens, so the block histogram is the
+// answer (no zeroing pass, no atomics); 2: no histogram (a later step derives
+// the counts from the route lists).
 template <int NV>                                   // keys per lane (>= E / 64)
 __global__ __launch_bounds__(ROUTE_THREADS)
 void route_topk_kernel(const float* __restrict__ logits, int T, int E, int k, int tokens_per_block,
-                       int direct_counts, int32_t* __restrict__ topk_ids, float* __restrict__ topk_w,
+                       int hist_mode, int32_t* __restrict__ topk_ids, float* __restrict__ topk_w,
                        int32_t* __restrict__ counts) {
     __shared__ int hist[MAX_EXPERTS];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -56,12 +58,13 @@ void route_topk_kernel(const float* __restrict__ logits, int T, int E, int k, in
         if (lane < k) {
             topk_ids[(size_t)t * k + lane] = my_e[0];
             topk_w[(size_t)t * k + lane] = z / s;
-            atomicAdd(&hist[my_e[0]], 1);
+            if (hist_mode != 2) atomicAdd(&hist[my_e[0]], 1);
         }
     }
+    if (hist_mode == 2) return;
     __syncthreads();
     for (int e = threadIdx.x; e < E; e += ROUTE_THREADS) {
-        if (direct_counts) counts[e] = hist[e];
+        if (hist_mode == 1) counts[e] = hist[e];
         else if (hist[e]) atomicAdd(&counts[e], hist[e]);
     }
 }
@@ -81,13 +84,17 @@ void route_launch(const float* logits, int T, int E, int k, int32_t* topk_ids, f
     // deterministic).
     const int single_max = 64;
     if (T <= single_max) {
-        route_topk_kernel<NV><<<1, ROUTE_THREADS, 0, s>>>(logits, T, E, k, T, 1, topk_ids, topk_w, counts);
+        route_topk_kernel<NV><<<1, ROUTE_THREADS, 0, s>>>(logits, T, E, k, T, counts ? 1 : 2, topk_ids, topk_w,
+                                                         counts);
         return;
     }
+    // (counts == nullptr: no histogram; the global atomics of ~1k blocks on E
+    // bins are a third of this launch at 16k tokens)
     const int tpb = 16;
-    zero_i32_kernel<<<(E + 255) / 256, 256, 0, s>>>(counts, E);
+    if (counts) zero_i32_kernel<<<(E + 255) / 256, 256, 0, s>>>(counts, E);
     const int blocks = (T + tpb - 1) / tpb;
-    route_topk_kernel<NV><<<blocks, ROUTE_THREADS, 0, s>>>(logits, T, E, k, tpb, 0, topk_ids, topk_w, counts);
+    route_topk_kernel<NV><<<blocks, ROUTE_THREADS, 0, s>>>(logits, T, E, k, tpb, counts ? 0 : 2, topk_ids, topk_w,
+                                                          counts);
 }
 
 // ------------------------------------------------------------ fused router
