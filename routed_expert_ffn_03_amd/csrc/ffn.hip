@@ -49,6 +49,7 @@
 #include "kernels.h"
 #include "lds_dma.h"
 
+#include <algorithm>
 #include <mutex>
 #include <type_traits>
 
@@ -832,10 +833,18 @@ __device__ __forceinline__ void thin_q3_pairs(const FfnArgs& a, const MTile& t, 
 // arithmetic.  Each lane loads its group's 13 words with three 16-byte loads
 // and one 4-byte load (52-byte groups are 4-byte aligned; a buffer load needs
 // no more), instead of re-reading words per 8 fields.
-template <int PHASE>
+//
+// XR > 0 (the down phase of a decode batch, every tile at most XR rows): a
+// block takes a contiguous run of items in tile-major order and keeps the
+// activation rows of its current tile in LDS (XR rows, then a row of zeros
+// that lanes without a row read), so the activation operand of each MFMA
+// step is one LDS read instead of a global load per lane.
+template <int PHASE, int XR>
 __global__ __launch_bounds__(THIN_THREADS)
 void ffn_thin_q3_kernel(FfnArgs a) {
+    static_assert(XR == 0 || PHASE == 2, "activation rows in LDS: down phase only");
     __shared__ float red[4][16][64];
+    extern __shared__ u32x4 xst[];                   // XR > 0: [XR + 1][K / 8] activation chunks
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform (SGPR)
     const int m = lane & 31, g = lane >> 5;
@@ -857,9 +866,28 @@ void ffn_thin_q3_kernel(FfnArgs a) {
     const __amdgpu_buffer_rsrc_t xqsrc = make_rsrc(a.xq, PHASE == 1 ? (uint32_t)((size_t)a.T * a.H * 2) : 0u);
     const __amdgpu_buffer_rsrc_t xssrc = make_rsrc(a.xs, PHASE == 1 ? (uint32_t)((size_t)a.T * NG * 4) : 0u);
 
-    for (int item = blockIdx.x; item < n_items; item += gridDim.x) {
-        const int nt = item / n_mt, mt = item % n_mt;
+    const int chunk = XR > 0 ? (n_items + (int)gridDim.x - 1) / (int)gridDim.x : 1;
+    const int i_first = XR > 0 ? (int)blockIdx.x * chunk : (int)blockIdx.x;
+    const int i_end = XR > 0 ? min(n_items, i_first + chunk) : n_items;
+    const int i_step = XR > 0 ? 1 : (int)gridDim.x;
+    int staged = -1;                                 // XR > 0: the tile whose rows are in LDS
+    for (int item = i_first; item < i_end; item += i_step) {
+        const int nt = XR > 0 ? item % NT : item / n_mt;
+        const int mt = XR > 0 ? item / NT : item % n_mt;
         const MTile t = a.thin[mt];
+        if constexpr (XR > 0) {
+            if (mt != staged) {
+                __syncthreads();                     // every wave done with the previous rows
+                const int cpr = K / 8;               // 16-byte chunks per row
+                for (int i = threadIdx.x; i < (XR + 1) * cpr; i += THIN_THREADS) {
+                    const int r = i / cpr;
+                    xst[i] = r < t.rows ? ldg16(a.act + (size_t)(t.row0 + r) * K + 8 * (i - r * cpr))
+                                        : u32x4{0, 0, 0, 0};
+                }
+                __syncthreads();
+                staged = mt;
+            }
+        }
         if constexpr (PHASE == 1) {
             if (t.rows <= 16) {
                 thin_q3_pairs(a, t, nt, xqsrc, xssrc, red, wave, lane);
@@ -912,9 +940,13 @@ void ffn_thin_q3_kernel(FfnArgs a) {
             const float sc = valid ? (float)__builtin_bit_cast(_Float16, cur.s) : 0.0f;
             const float m4 = -4.0f * sc;
             const uint32_t ao = (has_row && valid) ? aoff + (uint32_t)G * 256u : NOWHERE;
+            // XR > 0: chunk 16 G + J of this lane's row in LDS (the zero row XR without one)
+            const u32x4* xrow = xst + (size_t)((has_row && valid) ? m : XR) * (K / 8) + (valid ? 16 * G : 0);
             static_for<16>([&](auto j_c) {
                 constexpr int J = decltype(j_c)::value;
-                const u32x4 av = __builtin_amdgcn_raw_buffer_load_b128(asrc, ao, 16 * J, 0);
+                u32x4 av;
+                if constexpr (XR > 0) av = xrow[J];
+                else av = __builtin_amdgcn_raw_buffer_load_b128(asrc, ao, 16 * J, 0);
                 u32x4 bv;
                 static_for<4>([&](auto q_c) {
                     constexpr int Q = decltype(q_c)::value;
@@ -964,9 +996,14 @@ FfnLayout ffn_layout(int T, int E, int k, int H, int I, int wfmt) {
     return L;
 }
 
+// dynamic LDS cap of the 3-bit down kernels with activation rows in LDS
+// (the kernel's own 16 KB partial-tile buffer comes on top)
+constexpr size_t Q3X_LDS_MAX = 140 * 1024;
+
 struct DevInfo {
     int cus = 0;
     int q3ring = 5;                             // ... of the 3-bit fat kernels (5 or 6)
+    bool q3x_ok = false;                        // the LDS cap above could be set
     int thin_blocks[2][2][2] = {};              // [wfmt][phase-1][chunk width 2 / 4]
 };
 
@@ -1012,8 +1049,17 @@ hipError_t dev_info(DevInfo& out) {
         d.thin_blocks[0][0][1] = stream_occupancy(1);
         d.thin_blocks[0][1][0] = occupancy_of((const void*)ffn_thin_kernel<2, 2>);
         d.thin_blocks[0][1][1] = stream_occupancy(2);
-        d.thin_blocks[1][0][0] = d.thin_blocks[1][0][1] = occupancy_of((const void*)ffn_thin_q3_kernel<1>);
-        d.thin_blocks[1][1][0] = d.thin_blocks[1][1][1] = occupancy_of((const void*)ffn_thin_q3_kernel<2>);
+        d.thin_blocks[1][0][0] = d.thin_blocks[1][0][1] = occupancy_of((const void*)ffn_thin_q3_kernel<1, 0>);
+        d.thin_blocks[1][1][0] = d.thin_blocks[1][1][1] = occupancy_of((const void*)ffn_thin_q3_kernel<2, 0>);
+        // the down kernels with activation rows in LDS take up to 139 KB of it
+        const void* staged[3] = {(const void*)ffn_thin_q3_kernel<2, 4>, (const void*)ffn_thin_q3_kernel<2, 8>,
+                                 (const void*)ffn_thin_q3_kernel<2, 16>};
+        for (const void* f : staged) {
+            if ((size_t)lds_max < Q3X_LDS_MAX) break;
+            err = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)Q3X_LDS_MAX);
+            if (err != hipSuccess) return err;
+        }
+        d.q3x_ok = (size_t)lds_max >= Q3X_LDS_MAX;
         d.cus = cus;
     }
     out = d;
@@ -1063,7 +1109,22 @@ hipError_t launch_phase_t(const FfnArgs& fa, const DevInfo& d, bool fat_possible
             if (q3dec_fits(fa.T, fa.E, fa.k, fa.H)) return launch_q3dec_gate_up(fa, d.cus, s);
             q3_xprep_kernel<<<d.cus, 256, 0, s>>>(fa);
         }
-        ffn_thin_q3_kernel<PHASE><<<d.cus * d.thin_blocks[1][PHASE - 1][0], THIN_THREADS, 0, s>>>(fa);
+        if constexpr (PHASE == 2) {
+            // decode batches: every tile has at most T rows; its activation
+            // rows (and a zero row) in LDS when they fit
+            const int xr = fa.T <= 4 ? 4 : (fa.T <= 8 ? 8 : (fa.T <= 16 ? 16 : 0));
+            const size_t xb = (size_t)(xr + 1) * fa.I * 2;
+            if (xr > 0 && d.q3x_ok && xb <= Q3X_LDS_MAX) {
+                // blocks per CU as the LDS allows (the 16 KB partial tiles included), at most 4
+                const int per_cu = (int)std::min<size_t>(4, (160 * 1024) / (xb + 16 * 1024 + 1024));
+                const unsigned grid = (unsigned)(d.cus * std::max(per_cu, 1));
+                if (xr == 4) ffn_thin_q3_kernel<2, 4><<<grid, THIN_THREADS, xb, s>>>(fa);
+                else if (xr == 8) ffn_thin_q3_kernel<2, 8><<<grid, THIN_THREADS, xb, s>>>(fa);
+                else ffn_thin_q3_kernel<2, 16><<<grid, THIN_THREADS, xb, s>>>(fa);
+                return hipGetLastError();
+            }
+        }
+        ffn_thin_q3_kernel<PHASE, 0><<<d.cus * d.thin_blocks[1][PHASE - 1][0], THIN_THREADS, 0, s>>>(fa);
     } else {
         // weights through LDS in whole lines (stream.hip) when each wave's
         // quarter of K is a multiple of 64; else straight into registers
