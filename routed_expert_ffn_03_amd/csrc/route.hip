@@ -119,9 +119,11 @@ constexpr int R_THREADS = 256;
 constexpr uint32_t R_ROW = 128;           // bytes of one row per 64-k slot
 
 __host__ __device__ constexpr uint32_t router_stage_bytes(int E) { return (uint32_t)(RB + E) * R_ROW; }
+// staged logits [RB][E + 4] fp32, then the three partial top-8 lists of
+// waves 1-3 ([3][8][RB] keys and experts)
+__host__ __device__ constexpr uint32_t router_gate_bytes(int E) { return (uint32_t)RB * (E + 4) * 4 + 3 * 8 * RB * 8; }
 __host__ __device__ constexpr uint32_t router_lds_bytes(int E) {
-    return router_stage_bytes(E) * 2 > (uint32_t)RB * (E + 8) * 4 ? router_stage_bytes(E) * 2
-                                                                  : (uint32_t)RB * (E + 8) * 4;
+    return router_stage_bytes(E) * 2 > router_gate_bytes(E) ? router_stage_bytes(E) * 2 : router_gate_bytes(E);
 }
 
 template <int CT>
@@ -133,7 +135,9 @@ void router_topk_kernel(const uint16_t* __restrict__ x, const uint16_t* __restri
     constexpr int NO = (RB + E) / 8;                     // 8-row octets per slot
     constexpr int LW = (NO + 3) / 4;                     // load instructions per wave per slot (at most)
     constexpr uint32_t SB = router_stage_bytes(E);
-    constexpr int LD = E + 8;                            // staged logit row (floats): conflict-free stores
+    // staged logit row (floats): E + 4 = 4 (mod 64), so 16 lanes reading 16 B
+    // of 16 different rows hit distinct banks
+    constexpr int LD = E + 4;
     extern __shared__ u32x4 smem[];
     __shared__ int hist[E];
     const int tid = threadIdx.x, lane = tid & 63;
@@ -255,41 +259,118 @@ void router_topk_kernel(const uint16_t* __restrict__ x, const uint16_t* __restri
                 make_float4(src[0], src[1], src[2], src[3]);
         }
     }
-    // top-k per token, one wave per token: the selection of route_topk_kernel,
-    // four tokens at a time (r, r + 4, r + 8, r + 12) so that their chains of
-    // k dependent wave reductions interleave (one wave per SIMD here: nothing
-    // else hides their latency); a slot past the block's rows repeats the
-    // last row and stores nothing
-    constexpr int NV = E / 64;
-    constexpr int TS = R_THREADS / 64;
-    constexpr int RQ = 4;
-    for (int r = wave; r < rows; r += RQ * TS) {
-        int rr[RQ];
+    if (k <= 8 && rows > 16) {
+        // Top-k with one token per lane (lane l: row l of the block): wave w
+        // keeps, per token, the 8 largest of experts [w E/4, (w + 1) E/4) as a
+        // sorted list (ordered logit bits, expert), each logit entering by a
+        // branch-free insertion that puts it after equal ones (experts taken
+        // in ascending order, so equal logits stay in ascending expert order);
+        // waves 1-3 hand their lists to wave 0 through LDS, which inserts them
+        // in wave order and so keeps the same order across the four ranges.
+        // The first k entries are route_topk's choice, in its order.  (A block
+        // of at most 16 tokens, e.g. a decode batch, takes the per-wave
+        // selection below instead: four tokens per wave beat 64 lanes of
+        // which a few hold a token.)
+        uint32_t tv[8];
+        int ti[8];
 #pragma unroll
-        for (int q = 0; q < RQ; ++q) rr[q] = min(r + q * TS, rows - 1);
-        uint32_t ord[RQ][NV];
-#pragma unroll
-        for (int q = 0; q < RQ; ++q)
-#pragma unroll
-            for (int i = 0; i < NV; ++i) ord[q][i] = ordered_bits(lg[rr[q] * LD + lane + 64 * i]);
-        int my_e[RQ];
-        float my_v[RQ];
-#pragma unroll
-        for (int q = 0; q < RQ; ++q) {
-            my_e[q] = 0;
-            my_v[q] = 0.0f;
+        for (int j = 0; j < 8; ++j) {
+            tv[j] = 0u;                                            // below every finite logit's pattern
+            ti[j] = 0;
         }
-        wave_topk<NV, RQ>(ord, k, lane, my_e, my_v);
+        auto insert = [&](uint32_t v, int e) {
+            bool c[8];
 #pragma unroll
-        for (int q = 0; q < RQ; ++q) {
-            const float v0 = __shfl(my_v[q], 0, 64);
-            const float z = lane < k ? expf(my_v[q] - v0) : 0.0f;
-            const float sum = wave_sum(z);
-            if (lane < k && r + q * TS < rows) {
-                const size_t t = (size_t)(t0 + rr[q]);
-                topk_ids[t * k + lane] = my_e[q];
-                topk_w[t * k + lane] = z / sum;
-                atomicAdd(&hist[my_e[q]], 1);
+            for (int j = 0; j < 8; ++j) c[j] = v > tv[j];
+#pragma unroll
+            for (int j = 7; j >= 1; --j) {
+                // the list is sorted, so v lands at the first j with c[j]
+                tv[j] = max(min(tv[j - 1], v), tv[j]);
+                ti[j] = c[j - 1] ? ti[j - 1] : (c[j] ? e : ti[j]);
+            }
+            tv[0] = max(tv[0], v);
+            ti[0] = c[0] ? e : ti[0];
+        };
+        const int rl = min(lane, rows - 1);                         // lanes past the rows repeat the last
+        const float* lrow = lg + rl * LD + wave * (E / 4);
+#pragma unroll 4
+        for (int c4 = 0; c4 < E / 16; ++c4) {
+            const float4 q4 = *reinterpret_cast<const float4*>(lrow + 4 * c4);
+            const int e0 = wave * (E / 4) + 4 * c4;
+            insert(ordered_bits(q4.x), e0);
+            insert(ordered_bits(q4.y), e0 + 1);
+            insert(ordered_bits(q4.z), e0 + 2);
+            insert(ordered_bits(q4.w), e0 + 3);
+        }
+        uint32_t* mv = reinterpret_cast<uint32_t*>(lg + RB * LD);  // [3][8][RB] keys, then experts
+        int* mi = reinterpret_cast<int*>(mv + 3 * 8 * RB);
+        if (wave > 0) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                mv[((wave - 1) * 8 + j) * RB + lane] = tv[j];
+                mi[((wave - 1) * 8 + j) * RB + lane] = ti[j];
+            }
+        }
+        __syncthreads();
+        if (wave == 0) {
+            for (int w = 0; w < 3; ++w)
+#pragma unroll
+                for (int j = 0; j < 8; ++j) insert(mv[(w * 8 + j) * RB + lane], mi[(w * 8 + j) * RB + lane]);
+            if (lane < rows) {
+                const float v0 = from_ordered(tv[0]);
+                float z[8];
+#pragma unroll
+                for (int j = 0; j < 8; ++j) z[j] = j < k ? expf(from_ordered(tv[j]) - v0) : 0.0f;
+                // summed in the order of wave_sum's butterfly over lanes j (so
+                // the weights equal route_topk_kernel's bit for bit)
+                const float sum = ((z[0] + z[4]) + (z[2] + z[6])) + ((z[1] + z[5]) + (z[3] + z[7]));
+                const size_t t = (size_t)(t0 + lane);
+#pragma unroll
+                for (int j = 0; j < 8; ++j)
+                    if (j < k) {
+                        topk_ids[t * k + j] = ti[j];
+                        topk_w[t * k + j] = z[j] / sum;
+                        atomicAdd(&hist[ti[j]], 1);
+                    }
+            }
+        }
+    } else {
+        // top-k per token, one wave per token: the selection of route_topk_kernel,
+        // four tokens at a time (r, r + 4, r + 8, r + 12) so that their chains of
+        // k dependent wave reductions interleave (one wave per SIMD here: nothing
+        // else hides their latency); a slot past the block's rows repeats the
+        // last row and stores nothing
+        constexpr int NV = E / 64;
+        constexpr int TS = R_THREADS / 64;
+        constexpr int RQ = 4;
+        for (int r = wave; r < rows; r += RQ * TS) {
+            int rr[RQ];
+    #pragma unroll
+            for (int q = 0; q < RQ; ++q) rr[q] = min(r + q * TS, rows - 1);
+            uint32_t ord[RQ][NV];
+    #pragma unroll
+            for (int q = 0; q < RQ; ++q)
+    #pragma unroll
+                for (int i = 0; i < NV; ++i) ord[q][i] = ordered_bits(lg[rr[q] * LD + lane + 64 * i]);
+            int my_e[RQ];
+            float my_v[RQ];
+    #pragma unroll
+            for (int q = 0; q < RQ; ++q) {
+                my_e[q] = 0;
+                my_v[q] = 0.0f;
+            }
+            wave_topk<NV, RQ>(ord, k, lane, my_e, my_v);
+    #pragma unroll
+            for (int q = 0; q < RQ; ++q) {
+                const float v0 = __shfl(my_v[q], 0, 64);
+                const float z = lane < k ? expf(my_v[q] - v0) : 0.0f;
+                const float sum = wave_sum(z);
+                if (lane < k && r + q * TS < rows) {
+                    const size_t t = (size_t)(t0 + rr[q]);
+                    topk_ids[t * k + lane] = my_e[q];
+                    topk_w[t * k + lane] = z / sum;
+                    atomicAdd(&hist[my_e[q]], 1);
+                }
             }
         }
     }

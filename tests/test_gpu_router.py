@@ -25,9 +25,11 @@ pytestmark = pytest.mark.gpu
 
 # (T, E, H, k): ragged token blocks, every supported expert count, decode and the 16k chunk.  With the logits
 # asked for, T <= 32 splits the GEMM over the experts (512-k batches; a deeper ring of 16 token rows at T <= 16):
-# T = 16 / 17 and 32 / 33 sit on either side of those switches, H = 1056 and 4128 end in a partial batch.
+# T = 16 / 17 and 32 / 33 sit on either side of those switches, H = 1056 and 4128 end in a partial batch;
+# k = 16 and 32 take the per-wave selection, k <= 8 the per-lane one.
 CASES = [(64, 128, 256, 2), (333, 256, 512, 4), (700, 384, 1024, 8), (1, 384, 4096, 8), (4, 512, 4096, 8),
-         (16, 384, 1056, 8), (32, 256, 1056, 4), (17, 128, 4128, 8), (33, 128, 512, 2), (16384, 384, 4096, 8)]
+         (16, 384, 1056, 8), (32, 256, 1056, 4), (17, 128, 4128, 8), (33, 128, 512, 2), (16384, 384, 4096, 8),
+         (100, 256, 512, 16), (70, 512, 256, 32)]
 
 
 def _x(T, H, seed):
