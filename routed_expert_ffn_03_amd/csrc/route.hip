@@ -69,6 +69,102 @@ void route_topk_kernel(const float* __restrict__ logits, int T, int E, int k, in
     }
 }
 
+// route_topk with one token per lane (k <= 8, E a multiple of 16 up to 512):
+// a block takes RL_TOK tokens and stages their logits in LDS with coalesced
+// loads (rows of E + 4 floats: 16 lanes reading 16 B of 16 rows hit distinct
+// banks); wave w keeps, per token, the 8 largest of experts [w E/4, (w + 1)
+// E/4) (Top8); waves 1-3 hand their lists to wave 0, which merges them in
+// wave order.  Choice, order and weights equal route_topk_kernel's bit for
+// bit; hist_mode as there.
+constexpr int RL_TOK = 64;
+__host__ __device__ constexpr uint32_t route_lane_lds_bytes(int E) {
+    return (uint32_t)RL_TOK * (E + 4) * 4 + 3 * 8 * RL_TOK * 8;
+}
+
+__global__ __launch_bounds__(ROUTE_THREADS)
+void route_topk_lane_kernel(const float* __restrict__ logits, int T, int E, int k, int hist_mode,
+                            int32_t* __restrict__ topk_ids, float* __restrict__ topk_w,
+                            int32_t* __restrict__ counts) {
+    extern __shared__ u32x4 lane_smem[];
+    __shared__ int hist[MAX_EXPERTS];
+    float* lgs = reinterpret_cast<float*>(lane_smem);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int LD = E + 4;
+    const int t0 = blockIdx.x * RL_TOK, rows = min(RL_TOK, T - t0);
+    const int c4n = E / 4;                                         // float4 per row
+    const float4* src = reinterpret_cast<const float4*>(logits + (size_t)t0 * E);
+    for (int i = tid; i < rows * c4n; i += ROUTE_THREADS) {
+        const int r = i / c4n;
+        *reinterpret_cast<float4*>(lgs + r * LD + 4 * (i - r * c4n)) = src[i];
+    }
+    if (hist_mode != 2)
+        for (int e = tid; e < E; e += ROUTE_THREADS) hist[e] = 0;
+    __syncthreads();
+
+    Top8 tl;
+    top8_init(tl);
+    const int qe = E / 4;                                          // experts per wave
+    const float* lrow = lgs + min(lane, rows - 1) * LD + wave * qe;   // lanes past the rows repeat the last
+    for (int c = 0; c < qe / 4; ++c) {
+        const float4 v = *reinterpret_cast<const float4*>(lrow + 4 * c);
+        const int e0 = wave * qe + 4 * c;
+        top8_insert(tl, ordered_bits(v.x), e0);
+        top8_insert(tl, ordered_bits(v.y), e0 + 1);
+        top8_insert(tl, ordered_bits(v.z), e0 + 2);
+        top8_insert(tl, ordered_bits(v.w), e0 + 3);
+    }
+    uint32_t* mv = reinterpret_cast<uint32_t*>(lgs + RL_TOK * LD);   // [3][8][RL_TOK] keys, then experts
+    int* mi = reinterpret_cast<int*>(mv + 3 * 8 * RL_TOK);
+    if (wave > 0) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            mv[((wave - 1) * 8 + j) * RL_TOK + lane] = tl.v[j];
+            mi[((wave - 1) * 8 + j) * RL_TOK + lane] = tl.e[j];
+        }
+    }
+    __syncthreads();
+    if (wave == 0) {
+        for (int w = 0; w < 3; ++w)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) top8_insert(tl, mv[(w * 8 + j) * RL_TOK + lane], mi[(w * 8 + j) * RL_TOK + lane]);
+        if (lane < rows) {
+            float wj[8];
+            top8_weights(tl, k, wj);
+            const size_t t = (size_t)(t0 + lane);
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                if (j < k) {
+                    topk_ids[t * k + j] = tl.e[j];
+                    topk_w[t * k + j] = wj[j];
+                    if (hist_mode != 2) atomicAdd(&hist[tl.e[j]], 1);
+                }
+        }
+    }
+    if (hist_mode == 2) return;
+    __syncthreads();
+    for (int e = tid; e < E; e += ROUTE_THREADS) {
+        if (hist_mode == 1) counts[e] = hist[e];
+        else if (hist[e]) atomicAdd(&counts[e], hist[e]);
+    }
+}
+
+std::mutex g_rl_mu;
+bool g_rl_ready[64] = {};
+
+// the per-lane kernel's LDS cap, once per device; false where it cannot be set
+bool route_lane_ready() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return false;
+    std::lock_guard<std::mutex> lock(g_rl_mu);
+    if (!g_rl_ready[dev]) {
+        if (hipFuncSetAttribute((const void*)route_topk_lane_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                (int)route_lane_lds_bytes(512)) != hipSuccess)
+            return false;
+        g_rl_ready[dev] = true;
+    }
+    return true;
+}
+
 __global__ void zero_i32_kernel(int32_t* p, int n) {
     int i = blockIdx.x * blockDim.x + threadIdx.x;
     if (i < n) p[i] = 0;
@@ -90,6 +186,12 @@ void route_launch(const float* logits, int T, int E, int k, int32_t* topk_ids, f
     }
     // (counts == nullptr: no histogram; the global atomics of ~1k blocks on E
     // bins are a third of this launch at 16k tokens)
+    if (k <= 8 && E % 16 == 0 && E <= 512 && ((uintptr_t)logits & 15) == 0 && route_lane_ready()) {
+        if (counts) zero_i32_kernel<<<(E + 255) / 256, 256, 0, s>>>(counts, E);
+        route_topk_lane_kernel<<<(T + RL_TOK - 1) / RL_TOK, ROUTE_THREADS, route_lane_lds_bytes(E), s>>>(
+            logits, T, E, k, counts ? 0 : 2, topk_ids, topk_w, counts);
+        return;
+    }
     const int tpb = 16;
     if (counts) zero_i32_kernel<<<(E + 255) / 256, 256, 0, s>>>(counts, E);
     const int blocks = (T + tpb - 1) / tpb;
@@ -271,66 +373,43 @@ void router_topk_kernel(const uint16_t* __restrict__ x, const uint16_t* __restri
         // of at most 16 tokens, e.g. a decode batch, takes the per-wave
         // selection below instead: four tokens per wave beat 64 lanes of
         // which a few hold a token.)
-        uint32_t tv[8];
-        int ti[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            tv[j] = 0u;                                            // below every finite logit's pattern
-            ti[j] = 0;
-        }
-        auto insert = [&](uint32_t v, int e) {
-            bool c[8];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) c[j] = v > tv[j];
-#pragma unroll
-            for (int j = 7; j >= 1; --j) {
-                // the list is sorted, so v lands at the first j with c[j]
-                tv[j] = max(min(tv[j - 1], v), tv[j]);
-                ti[j] = c[j - 1] ? ti[j - 1] : (c[j] ? e : ti[j]);
-            }
-            tv[0] = max(tv[0], v);
-            ti[0] = c[0] ? e : ti[0];
-        };
+        Top8 tl;
+        top8_init(tl);
         const int rl = min(lane, rows - 1);                         // lanes past the rows repeat the last
         const float* lrow = lg + rl * LD + wave * (E / 4);
 #pragma unroll 4
         for (int c4 = 0; c4 < E / 16; ++c4) {
             const float4 q4 = *reinterpret_cast<const float4*>(lrow + 4 * c4);
             const int e0 = wave * (E / 4) + 4 * c4;
-            insert(ordered_bits(q4.x), e0);
-            insert(ordered_bits(q4.y), e0 + 1);
-            insert(ordered_bits(q4.z), e0 + 2);
-            insert(ordered_bits(q4.w), e0 + 3);
+            top8_insert(tl, ordered_bits(q4.x), e0);
+            top8_insert(tl, ordered_bits(q4.y), e0 + 1);
+            top8_insert(tl, ordered_bits(q4.z), e0 + 2);
+            top8_insert(tl, ordered_bits(q4.w), e0 + 3);
         }
         uint32_t* mv = reinterpret_cast<uint32_t*>(lg + RB * LD);  // [3][8][RB] keys, then experts
         int* mi = reinterpret_cast<int*>(mv + 3 * 8 * RB);
         if (wave > 0) {
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                mv[((wave - 1) * 8 + j) * RB + lane] = tv[j];
-                mi[((wave - 1) * 8 + j) * RB + lane] = ti[j];
+                mv[((wave - 1) * 8 + j) * RB + lane] = tl.v[j];
+                mi[((wave - 1) * 8 + j) * RB + lane] = tl.e[j];
             }
         }
         __syncthreads();
         if (wave == 0) {
             for (int w = 0; w < 3; ++w)
 #pragma unroll
-                for (int j = 0; j < 8; ++j) insert(mv[(w * 8 + j) * RB + lane], mi[(w * 8 + j) * RB + lane]);
+                for (int j = 0; j < 8; ++j) top8_insert(tl, mv[(w * 8 + j) * RB + lane], mi[(w * 8 + j) * RB + lane]);
             if (lane < rows) {
-                const float v0 = from_ordered(tv[0]);
-                float z[8];
-#pragma unroll
-                for (int j = 0; j < 8; ++j) z[j] = j < k ? expf(from_ordered(tv[j]) - v0) : 0.0f;
-                // summed in the order of wave_sum's butterfly over lanes j (so
-                // the weights equal route_topk_kernel's bit for bit)
-                const float sum = ((z[0] + z[4]) + (z[2] + z[6])) + ((z[1] + z[5]) + (z[3] + z[7]));
+                float wj[8];
+                top8_weights(tl, k, wj);
                 const size_t t = (size_t)(t0 + lane);
 #pragma unroll
                 for (int j = 0; j < 8; ++j)
                     if (j < k) {
-                        topk_ids[t * k + j] = ti[j];
-                        topk_w[t * k + j] = z[j] / sum;
-                        atomicAdd(&hist[ti[j]], 1);
+                        topk_ids[t * k + j] = tl.e[j];
+                        topk_w[t * k + j] = wj[j];
+                        atomicAdd(&hist[tl.e[j]], 1);
                     }
             }
         }

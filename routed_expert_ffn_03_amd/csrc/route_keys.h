@@ -79,6 +79,51 @@ __device__ __forceinline__ void wave_topk(uint32_t (&ord)[Q][NV], int k, int lan
     }
 }
 
+// A sorted list of a token's 8 largest logits (ordered bits, expert), kept
+// by one lane: top-k with one token per lane.  A logit enters by a
+// branch-free insertion after the entries it does not exceed, so logits
+// offered in ascending expert order keep equal values in ascending expert
+// order, the order of the selection above.
+struct Top8 {
+    uint32_t v[8];
+    int e[8];
+};
+
+__device__ __forceinline__ void top8_init(Top8& t) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        t.v[j] = 0u;                                       // below every finite logit's pattern
+        t.e[j] = 0;
+    }
+}
+
+__device__ __forceinline__ void top8_insert(Top8& t, uint32_t v, int e) {
+    bool c[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) c[j] = v > t.v[j];
+#pragma unroll
+    for (int j = 7; j >= 1; --j) {
+        // the list is sorted, so v lands at the first j with c[j]
+        t.v[j] = max(min(t.v[j - 1], v), t.v[j]);
+        t.e[j] = c[j - 1] ? t.e[j - 1] : (c[j] ? e : t.e[j]);
+    }
+    t.v[0] = max(t.v[0], v);
+    t.e[0] = c[0] ? e : t.e[0];
+}
+
+// Softmax weights of the first k entries (k <= 8), summed in the order of
+// wave_sum's butterfly over lanes 0..7, so that they equal the per-wave
+// selection's weights bit for bit.
+__device__ __forceinline__ void top8_weights(const Top8& t, int k, float (&w)[8]) {
+    const float v0 = from_ordered(t.v[0]);
+    float z[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) z[j] = j < k ? expf(from_ordered(t.v[j]) - v0) : 0.0f;
+    const float sum = ((z[0] + z[4]) + (z[2] + z[6])) + ((z[1] + z[5]) + (z[3] + z[7]));
+#pragma unroll
+    for (int j = 0; j < 8; ++j) w[j] = z[j] / sum;
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);

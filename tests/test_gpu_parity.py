@@ -111,8 +111,9 @@ def _tie_logits(T, E, seed):
     return lg
 
 
+# (the one-token-per-lane kernel takes T > 64, k <= 8 and E a multiple of 16 up to 512)
 @pytest.mark.parametrize("T,E,k", [(10, 40, 6), (200, 40, 6), (65, 1024, 32), (300, 100, 1), (7, 16, 16),
-                                   (129, 384, 8)])
+                                   (129, 384, 8), (333, 256, 3), (200, 512, 8), (130, 16, 2), (97, 48, 1)])
 def test_route_ties_and_shapes(T, E, k):
     say(f"[route] T={T} E={E} k={k} (ties, signed zeros)")
     lg = _tie_logits(T, E, T + E + k)
