@@ -823,6 +823,80 @@ __device__ __forceinline__ void thin_q3_pairs(const FfnArgs& a, const MTile& t, 
     thin_reduce_store<1>(a, acc, t, nt, red, wave, lane);
 }
 
+// One down item of a decode batch (a tile of at most 16 rows) on pair-slot
+// operands, as thin_q3_pairs: the tile's activation rows are in LDS in slot
+// order (xl: XR + 1 rows of K halves, the last all zeros; xsl: their group
+// sums, an fp16 hi, lo pair per row and group), the codes enter the fp16
+// products as 1024 + u and each pair ends with the -1028 x group-sum step.
+// The 32 output columns are the W_down rows nt*32 + n.
+template <int XR>
+__device__ __forceinline__ void thin_q3_pairs_down(const FfnArgs& a, const MTile& t, int nt, const uint16_t* xl,
+                                                   const uint32_t* xsl, float (&red)[4][16][64], int wave,
+                                                   int lane) {
+    const int m = lane & 31, g = lane >> 5, mm = m & 15;
+    const int K = a.I, NG = K >> 7, NP = (NG + 1) >> 1;
+    const size_t mat_words = (size_t)a.H * NG * Q3_WORDS;
+    const bool act_lane = (m >> 4) == g && mm < t.rows;
+    const int xr = act_lane ? mm : XR;                  // LDS row of this lane's activations
+    const int row = nt * 32 + m;
+    const uint32_t* wrow = reinterpret_cast<const uint32_t*>(a.wd) + (size_t)t.e * mat_words + (size_t)row * NG * Q3_WORDS;
+    const uint16_t* srow = a.sd + ((size_t)t.e * a.H + row) * NG;
+    uint32_t magic;
+    asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(magic));
+
+    struct Pair {
+        uint32_t w[Q3_WORDS];
+        uint16_t s0, s1;
+    };
+    auto load_pair = [&](int p, Pair& q) {
+        const int G = min(2 * p + g, NG - 1);     // past an odd count: a real group whose sums are zero
+        const uint32_t* gw = wrow + G * Q3_WORDS;
+        const u32x4a4 q0 = *reinterpret_cast<const u32x4a4*>(gw);
+        const u32x4a4 q1 = *reinterpret_cast<const u32x4a4*>(gw + 4);
+        const u32x4a4 q2 = *reinterpret_cast<const u32x4a4*>(gw + 8);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            q.w[i] = q0[i];
+            q.w[4 + i] = q1[i];
+            q.w[8 + i] = q2[i];
+        }
+        q.w[12] = gw[12];
+        q.s0 = srow[2 * p];
+        q.s1 = srow[min(2 * p + 1, NG - 1)];
+    };
+
+    float fin[8] = {};
+    Pair cur, nxt;
+    if (wave < NP) load_pair(wave, cur);
+    for (int p = wave; p < NP; p += 4) {
+        if (p + 4 < NP) load_pair(p + 4, nxt);   // next pair's words in flight during this one
+        const int G = 2 * p + g;
+        const u32x4* xa = reinterpret_cast<const u32x4*>(xl + (size_t)(G < NG ? xr : XR) * K) + 16 * min(G, NG - 1);
+        const uint32_t xsum = G < NG ? xsl[xr * NG + G] : 0u;     // (row XR: zeros)
+        f32x16 c = f32x16{};
+        static_for<16>([&](auto j_c) {
+            constexpr int J = decltype(j_c)::value;
+            u32x4 bv;
+            static_for<4>([&](auto q_c) {
+                constexpr int Q = decltype(q_c)::value;
+                bv[Q] = magic_pair<4 * J + Q>(cur.w, magic);
+            });
+            c = mfma_f16(xa[J], bv, c);
+        });
+        // minus 1028 x (group sum, as fp16 hi + lo): exact fp16 weights -1028 in k-slots 0 and 1 of each half
+        c = mfma_f16(u32x4{xsum, 0u, 0u, 0u}, u32x4{0xE404E404u, 0u, 0u, 0u}, c);
+        const float s0 = (float)__builtin_bit_cast(_Float16, cur.s0);
+        const float s1 = 2 * p + 1 < NG ? (float)__builtin_bit_cast(_Float16, cur.s1) : 0.0f;
+#pragma unroll
+        for (int r = 0; r < 8; ++r) fin[r] = fmaf(s1, c[r + 8], fmaf(s0, c[r], fin[r]));
+        cur = nxt;
+    }
+    f32x16 acc = f32x16{};
+#pragma unroll
+    for (int r = 0; r < 8; ++r) acc[r] = fin[r];
+    thin_reduce_store<2>(a, acc, t, nt, red, wave, lane);
+}
+
 // 3-bit thin kernel: the same items, waves and reduction as the bf16 thin
 // kernel, with the reduction index walked a group pair at a time.  For MFMA
 // step j (0..15) of pair p, lane half g holds fields 8j..8j+7 of group 2p+g
@@ -834,17 +908,19 @@ __device__ __forceinline__ void thin_q3_pairs(const FfnArgs& a, const MTile& t, 
 // and one 4-byte load (52-byte groups are 4-byte aligned; a buffer load needs
 // no more), instead of re-reading words per 8 fields.
 //
-// XR > 0 (the down phase of a decode batch, every tile at most XR rows): a
-// block takes a contiguous run of items in tile-major order and keeps the
-// activation rows of its current tile in LDS (XR rows, then a row of zeros
-// that lanes without a row read), so the activation operand of each MFMA
-// step is one LDS read instead of a global load per lane.
+// XR > 0 (the down phase of a decode batch, every tile at most XR <= 16
+// rows): a block takes a contiguous run of items in tile-major order and
+// keeps the activation rows of its current tile in LDS in pair-slot order
+// with their group sums (XR rows, then a row of zeros that lanes without a
+// row read), and runs each item on the pair-slot operands
+// (thin_q3_pairs_down): no per-weight arithmetic, and the activation operand
+// of each MFMA step is one LDS read.
 template <int PHASE, int XR>
 __global__ __launch_bounds__(THIN_THREADS)
 void ffn_thin_q3_kernel(FfnArgs a) {
     static_assert(XR == 0 || PHASE == 2, "activation rows in LDS: down phase only");
     __shared__ float red[4][16][64];
-    extern __shared__ u32x4 xst[];                   // XR > 0: [XR + 1][K / 8] activation chunks
+    extern __shared__ u32x4 xst[];                   // XR > 0: [XR + 1][K] fp16 in slot order, then [XR + 1][K / 128] sums
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform (SGPR)
     const int m = lane & 31, g = lane >> 5;
@@ -876,17 +952,28 @@ void ffn_thin_q3_kernel(FfnArgs a) {
         const int mt = XR > 0 ? item / NT : item % n_mt;
         const MTile t = a.thin[mt];
         if constexpr (XR > 0) {
+            // the tile's activation rows in pair-slot order with their group
+            // sums (rows past the tile, and row XR, all zeros), then the item
+            uint16_t* xl = reinterpret_cast<uint16_t*>(xst);
+            uint32_t* xsl = reinterpret_cast<uint32_t*>(xl + (size_t)(XR + 1) * K);
             if (mt != staged) {
                 __syncthreads();                     // every wave done with the previous rows
-                const int cpr = K / 8;               // 16-byte chunks per row
-                for (int i = threadIdx.x; i < (XR + 1) * cpr; i += THIN_THREADS) {
-                    const int r = i / cpr;
-                    xst[i] = r < t.rows ? ldg16(a.act + (size_t)(t.row0 + r) * K + 8 * (i - r * cpr))
-                                        : u32x4{0, 0, 0, 0};
+                for (int i = threadIdx.x; i < (XR + 1) * NG; i += THIN_THREADS) {
+                    const int r = i / NG, G = i - r * NG;
+                    uint16_t* dst = xl + (size_t)r * K + G * 128;
+                    if (r < t.rows) {
+                        q3_prep_group_f16(a.act + (size_t)(t.row0 + r) * K + G * 128, dst, xsl + i);
+                    } else {
+#pragma unroll
+                        for (int j = 0; j < 16; ++j) reinterpret_cast<u32x4*>(dst)[j] = u32x4{0, 0, 0, 0};
+                        xsl[i] = 0u;
+                    }
                 }
                 __syncthreads();
                 staged = mt;
             }
+            thin_q3_pairs_down<XR>(a, t, nt, xl, xsl, red, wave, lane);
+            continue;
         }
         if constexpr (PHASE == 1) {
             if (t.rows <= 16) {
@@ -940,13 +1027,9 @@ void ffn_thin_q3_kernel(FfnArgs a) {
             const float sc = valid ? (float)__builtin_bit_cast(_Float16, cur.s) : 0.0f;
             const float m4 = -4.0f * sc;
             const uint32_t ao = (has_row && valid) ? aoff + (uint32_t)G * 256u : NOWHERE;
-            // XR > 0: chunk 16 G + J of this lane's row in LDS (the zero row XR without one)
-            const u32x4* xrow = xst + (size_t)((has_row && valid) ? m : XR) * (K / 8) + (valid ? 16 * G : 0);
             static_for<16>([&](auto j_c) {
                 constexpr int J = decltype(j_c)::value;
-                u32x4 av;
-                if constexpr (XR > 0) av = xrow[J];
-                else av = __builtin_amdgcn_raw_buffer_load_b128(asrc, ao, 16 * J, 0);
+                const u32x4 av = __builtin_amdgcn_raw_buffer_load_b128(asrc, ao, 16 * J, 0);
                 u32x4 bv;
                 static_for<4>([&](auto q_c) {
                     constexpr int Q = decltype(q_c)::value;
@@ -1113,7 +1196,7 @@ hipError_t launch_phase_t(const FfnArgs& fa, const DevInfo& d, bool fat_possible
             // decode batches: every tile has at most T rows; its activation
             // rows (and a zero row) in LDS when they fit
             const int xr = fa.T <= 4 ? 4 : (fa.T <= 8 ? 8 : (fa.T <= 16 ? 16 : 0));
-            const size_t xb = (size_t)(xr + 1) * fa.I * 2;
+            const size_t xb = (size_t)(xr + 1) * fa.I * 2 + ((size_t)(xr + 1) * (fa.I / 128) * 4 + 15) / 16 * 16;
             if (xr > 0 && d.q3x_ok && xb <= Q3X_LDS_MAX) {
                 // blocks per CU as the LDS allows (the 16 KB partial tiles included), at most 4
                 const int per_cu = (int)std::min<size_t>(4, (160 * 1024) / (xb + 16 * 1024 + 1024));
