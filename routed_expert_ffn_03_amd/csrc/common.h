@@ -51,6 +51,15 @@ __device__ __forceinline__ f32x16 mfma_f16(u32x4 a, u32x4 b, f32x16 c) {
                                                   __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
 }
 
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+
+// 16x16x32 fp16: lane L holds row (A) or column (B) L % 16, k 8 (L / 16) ..
+// 8 (L / 16) + 7; result element i of lane L is row 4 (L / 16) + i, column L % 16
+__device__ __forceinline__ f32x4 mfma16_f16(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+
 __device__ __forceinline__ u32x4 ldg16(const void* p) {
     return *reinterpret_cast<const u32x4*>(p);
 }

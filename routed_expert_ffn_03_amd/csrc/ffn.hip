@@ -897,6 +897,94 @@ __device__ __forceinline__ void thin_q3_pairs_down(const FfnArgs& a, const MTile
     thin_reduce_store<2>(a, acc, t, nt, red, wave, lane);
 }
 
+// The same item for a tile of at most 4 rows on 16x16x32 products: lane
+// quarter q (L / 16) holds group 4 p + q of its weight row in k-quarter q,
+// and the activation lanes of row 4 q + i hold token i of that group there,
+// so the 16 result rows are 4 groups x 4 tokens (no padding rows: half the
+// MFMA work of the 32-row tiles per weight).  Each group's scale is applied
+// on its own result rows; the four groups of a token are then summed across
+// the lane quarters.  Columns: W_down rows nt*32 + n and nt*32 + 16 + n.
+__device__ __forceinline__ void thin_q3_quads_down(const FfnArgs& a, const MTile& t, int nt, const uint16_t* xl,
+                                                   const uint32_t* xsl, float (&red)[4][16][64], int wave,
+                                                   int lane) {
+    constexpr int XR = 4;
+    const int n = lane & 15, q = lane >> 4;
+    const int K = a.I, NG = K >> 7, NQ = (NG + 3) >> 2;
+    const size_t mat_words = (size_t)a.H * NG * Q3_WORDS;
+    const bool act_lane = (n >> 2) == q && (n & 3) < t.rows;    // A row n = 4 q + token
+    const int xr = act_lane ? (n & 3) : XR;
+    const uint32_t* wr0 = reinterpret_cast<const uint32_t*>(a.wd) + (size_t)t.e * mat_words +
+                          (size_t)(nt * 32 + n) * NG * Q3_WORDS;
+    const uint32_t* wr1 = wr0 + (size_t)16 * NG * Q3_WORDS;
+    const uint16_t* sr0 = a.sd + ((size_t)t.e * a.H + nt * 32 + n) * NG;
+    const uint16_t* sr1 = sr0 + (size_t)16 * NG;
+    uint32_t magic;
+    asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(magic));
+
+    auto load13 = [&](const uint32_t* gw, uint32_t (&w)[Q3_WORDS]) {
+        const u32x4a4 q0 = *reinterpret_cast<const u32x4a4*>(gw);
+        const u32x4a4 q1 = *reinterpret_cast<const u32x4a4*>(gw + 4);
+        const u32x4a4 q2 = *reinterpret_cast<const u32x4a4*>(gw + 8);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            w[i] = q0[i];
+            w[4 + i] = q1[i];
+            w[8 + i] = q2[i];
+        }
+        w[12] = gw[12];
+    };
+
+    float f0[4] = {}, f1[4] = {};
+    for (int p = wave; p < NQ; p += 4) {
+        const int G = 4 * p + q;
+        const int Gc = min(G, NG - 1);            // past the groups: a real one, scaled by 0 below
+        uint32_t w0[Q3_WORDS], w1[Q3_WORDS];
+        load13(wr0 + Gc * Q3_WORDS, w0);
+        load13(wr1 + Gc * Q3_WORDS, w1);
+        const uint16_t s0h = sr0[Gc], s1h = sr1[Gc];
+        const u32x4* xa = reinterpret_cast<const u32x4*>(xl + (size_t)(G < NG ? xr : XR) * K) + 16 * Gc;
+        const uint32_t xsum = G < NG ? xsl[xr * NG + G] : 0u;     // (row XR: zeros)
+        f32x4 c0 = f32x4{}, c1 = f32x4{};
+        static_for<16>([&](auto j_c) {
+            constexpr int J = decltype(j_c)::value;
+            u32x4 b0, b1;
+            static_for<4>([&](auto q_c) {
+                constexpr int Q = decltype(q_c)::value;
+                b0[Q] = magic_pair<4 * J + Q>(w0, magic);
+                b1[Q] = magic_pair<4 * J + Q>(w1, magic);
+            });
+            const u32x4 av = xa[J];
+            c0 = mfma16_f16(av, b0, c0);
+            c1 = mfma16_f16(av, b1, c1);
+        });
+        // minus 1028 x (group sum, as fp16 hi + lo) in k-slots 0 and 1 of each quarter
+        const u32x4 sa = u32x4{xsum, 0u, 0u, 0u}, sb = u32x4{0xE404E404u, 0u, 0u, 0u};
+        c0 = mfma16_f16(sa, sb, c0);
+        c1 = mfma16_f16(sa, sb, c1);
+        // this lane's result rows 4 q + i: token i of group 4 p + q
+        const float s0 = G < NG ? (float)__builtin_bit_cast(_Float16, s0h) : 0.0f;
+        const float s1 = G < NG ? (float)__builtin_bit_cast(_Float16, s1h) : 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            f0[i] = fmaf(s0, c0[i], f0[i]);
+            f1[i] = fmaf(s1, c1[i], f1[i]);
+        }
+    }
+    // sum the four groups of each token across the lane quarters, then the
+    // thin kernels' accumulator layout: lane L < 32 column L, rows 0..3
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f0[i] += __shfl_xor(f0[i], 16, 64);
+        f0[i] += __shfl_xor(f0[i], 32, 64);
+        f1[i] += __shfl_xor(f1[i], 16, 64);
+        f1[i] += __shfl_xor(f1[i], 32, 64);
+    }
+    f32x16 acc = f32x16{};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] = lane < 16 ? f0[i] : (lane < 32 ? f1[i] : 0.0f);
+    thin_reduce_store<2>(a, acc, t, nt, red, wave, lane);
+}
+
 // 3-bit thin kernel: the same items, waves and reduction as the bf16 thin
 // kernel, with the reduction index walked a group pair at a time.  For MFMA
 // step j (0..15) of pair p, lane half g holds fields 8j..8j+7 of group 2p+g
@@ -972,7 +1060,8 @@ void ffn_thin_q3_kernel(FfnArgs a) {
                 __syncthreads();
                 staged = mt;
             }
-            thin_q3_pairs_down<XR>(a, t, nt, xl, xsl, red, wave, lane);
+            if constexpr (XR == 4) thin_q3_quads_down(a, t, nt, xl, xsl, red, wave, lane);
+            else thin_q3_pairs_down<XR>(a, t, nt, xl, xsl, red, wave, lane);
             continue;
         }
         if constexpr (PHASE == 1) {
