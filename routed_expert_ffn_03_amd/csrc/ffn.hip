@@ -1003,8 +1003,9 @@ __device__ __forceinline__ void thin_q3_quads_down(const FfnArgs& a, const MTile
 // row read), and runs each item on the pair-slot operands
 // (thin_q3_pairs_down): no per-weight arithmetic, and the activation operand
 // of each MFMA step is one LDS read.
+// (XR > 0: four blocks per CU, one per SIMD each, as the launch assumes)
 template <int PHASE, int XR>
-__global__ __launch_bounds__(THIN_THREADS)
+__global__ __launch_bounds__(THIN_THREADS, XR > 0 ? 4 : 1)
 void ffn_thin_q3_kernel(FfnArgs a) {
     static_assert(XR == 0 || PHASE == 2, "activation rows in LDS: down phase only");
     __shared__ float red[4][16][64];

@@ -237,34 +237,28 @@ __device__ __forceinline__ void q3_prep_group(const uint16_t* src16, uint16_t* d
 
 // The same for an fp16 row (the activations of the down phase): the slots
 // for the fp16 products with the codes as the exact fp16 numbers 1024 + u
-// (bits 0x6400 | u), and the group sum as an fp16 hi, lo pair.
+// (bits 0x6400 | u), and the group sum as an fp16 hi, lo pair.  Each field
+// is read where it lies, one 16-bit load per field in slot order, so no
+// 128-value group is held in registers; the fp64 sum of 128 fp16 values is
+// exact, so the order of the additions does not matter.
 __device__ __forceinline__ void q3_prep_group_f16(const uint16_t* src16, uint16_t* dst16, uint32_t* sum_dst) {
-    const u32x4* src = reinterpret_cast<const u32x4*>(src16);
     u32x4* dst = reinterpret_cast<u32x4*>(dst16);
-    uint32_t v[64];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-        const u32x4 q = src[i];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) v[4 * i + j] = q[j];
-    }
-    auto half = [&](int f) -> uint32_t { return (v[f >> 1] >> (16 * (f & 1))) & 0xFFFFu; };
     double sum = 0.0;
-#pragma unroll
-    for (int f = 0; f < 128; ++f) sum += (double)(float)__builtin_bit_cast(_Float16, (uint16_t)half(f));
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
         u32x4 o;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int d = 4 * i + j;
-            o[j] = half(pair_field(2 * d)) | (half(pair_field(2 * d + 1)) << 16);
+            const uint16_t lo = src16[pair_field(2 * d)], hi = src16[pair_field(2 * d + 1)];
+            sum += (double)(float)__builtin_bit_cast(_Float16, lo) + (double)(float)__builtin_bit_cast(_Float16, hi);
+            o[j] = (uint32_t)lo | ((uint32_t)hi << 16);
         }
         dst[i] = o;
     }
-    const _Float16 hi = (_Float16)(float)sum;
-    const _Float16 lo = (_Float16)(float)(sum - (double)hi);
-    *sum_dst = (uint32_t)__builtin_bit_cast(uint16_t, hi) | ((uint32_t)__builtin_bit_cast(uint16_t, lo) << 16);
+    const _Float16 h = (_Float16)(float)sum;
+    const _Float16 l = (_Float16)(float)(sum - (double)h);
+    *sum_dst = (uint32_t)__builtin_bit_cast(uint16_t, h) | ((uint32_t)__builtin_bit_cast(uint16_t, l) << 16);
 }
 
 // Where the FFN part of a workspace keeps its header and tile lists.
