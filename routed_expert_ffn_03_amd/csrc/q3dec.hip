@@ -58,7 +58,16 @@ struct QdItem {
     int rr;                         // the tile's first sorted row << 6 | its row count
 };
 
-template <int NRED>
+// QUAD (at most 4 tokens): 16x16x32 products instead.  Waves 0-7 take the
+// item's 16 gate rows, waves 8-15 its 16 up rows, wave w & 7 a quad of
+// groups (4 (w & 7) ..); lane quarter q (L / 16) holds group 4 (w & 7) + q of
+// its weight row (column L % 16) in k-quarter q, and the activation lanes of
+// row 4 q + i hold token i of that group there, so the 16 result rows are 4
+// groups x 4 tokens with no padding rows (half the MFMA work of the 32-row
+// tiles); each group's scale is applied on its own rows, the four groups are
+// summed across the lane quarters, and 64 threads sum the 8 waves of each half
+// and apply SwiGLU.
+template <int NRED, bool QUAD>
 __global__ __launch_bounds__(QD_THREADS, 1)
 void ffn_q3_decode_kernel(FfnArgs a) {
     extern __shared__ u32x4 smem[];
@@ -87,10 +96,13 @@ void ffn_q3_decode_kernel(FfnArgs a) {
     __syncthreads();
 
     const int n_items = n_mt * NT;
+    // QUAD: this wave's half (gate / up) and quad, this lane's column and quarter
+    const int NQ = (NG + 3) >> 2;
+    const int half = wave >> 3, pq = wave & 7, qn = lane & 15, qq = lane >> 4;
     const int p = wave;                                    // this wave's group pair
-    const bool active = p < NP;
-    const int Gl = 2 * p + g;                              // this lane half's group
-    const int Gw = min(Gl, NG - 1);                        // (NG is even: always Gl)
+    const bool active = QUAD ? pq < NQ : p < NP;
+    const int Gl = QUAD ? 4 * pq + qq : 2 * p + g;         // this lane's group
+    const int Gw = min(Gl, NG - 1);
     uint32_t magic;
     asm volatile("v_mov_b32 %0, 0x43004300" : "=v"(magic));
 
@@ -101,13 +113,30 @@ void ffn_q3_decode_kernel(FfnArgs a) {
     // before an item's first use are exact and never drain the loads of the
     // items after it.
     const int pl = min(p, NP - 1);
-    const int Gld = min(2 * pl + g, NG - 1);
+    const int Gld = QUAD ? min(4 * min(pq, NQ - 1) + qq, NG - 1) : min(2 * pl + g, NG - 1);
     auto load_item = [&](int item, QdItem& q) {
         const int ic = min(item, n_items - 1);
         const int nt = ic / n_mt, mt = ic - nt * n_mt;
         const int2 t = tl[mt];
         q.rr = t.y;
         const int rows = t.y & 63, row0 = t.y >> 6;
+        if constexpr (QUAD) {
+            const size_t row = (size_t)t.x * I + nt * 16 + qn;   // gate (waves 0-7) or up (8-15) row of column qn
+            const uint32_t* gw = reinterpret_cast<const uint32_t*>(half ? a.wu : a.wg) + (row * NG + Gld) * Q3_WORDS;
+            const u32x4w q0 = *reinterpret_cast<const u32x4w*>(gw);
+            const u32x4w q1 = *reinterpret_cast<const u32x4w*>(gw + 4);
+            const u32x4w q2 = *reinterpret_cast<const u32x4w*>(gw + 8);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                q.w[i] = q0[i];
+                q.w[4 + i] = q1[i];
+                q.w[8 + i] = q2[i];
+            }
+            q.w[12] = gw[12];
+            q.s = (half ? a.su : a.sg)[row * NG + Gld];
+            q.pr = a.sorted_pair[row0 + min(qn & 3, rows - 1)];   // the token of activation row qn
+            return;
+        }
         const size_t row = (size_t)t.x * I + nt * 16 + mm;   // gate rows (m < 16), then the matching up rows
         const uint32_t* gw = reinterpret_cast<const uint32_t*>(m < 16 ? a.wg : a.wu) + (row * NG + Gld) * Q3_WORDS;
         const u32x4w q0 = *reinterpret_cast<const u32x4w*>(gw);
@@ -128,6 +157,58 @@ void ffn_q3_decode_kernel(FfnArgs a) {
     auto run_item = [&](int item, const QdItem& q, int buf) {
         const int nt = item / n_mt;
         float* red = red0 + buf * (QD_RED / 4);
+        if constexpr (QUAD) {
+            if (active) {
+                const bool act = (qn >> 2) == qq && (qn & 3) < (q.rr & 63) && Gl < NG;
+                const int xr = act ? q.pr / k : T;             // LDS row of the token (T: zeros)
+                const uint16_t* xa = xl + (size_t)xr * H + Gw * 128;
+                f32x4 c = f32x4{};
+                static_for<16>([&](auto j_c) {
+                    constexpr int J = decltype(j_c)::value;
+                    const u32x4 av = *reinterpret_cast<const u32x4*>(xa + 8 * J);
+                    u32x4 bv;
+                    static_for<4>([&](auto q_c) {
+                        constexpr int Q = decltype(q_c)::value;
+                        bv[Q] = magic_pair<4 * J + Q>(q.w, magic);
+                    });
+                    c = mfma16_bf16(av, bv, c);
+                });
+                // minus 132 x (group sum, bf16 hi + lo) in k-slots 0 and 1 of each quarter
+                const uint32_t xs = xr < T ? xsl[xr * NG + Gl] : 0u;
+                c = mfma16_bf16(u32x4{xs, 0u, 0u, 0u}, u32x4{0xC304C304u, 0u, 0u, 0u}, c);
+                // result rows 4 qq + i: token i of group Gl; scaled, then the quad's four groups summed
+                const uint16_t sh = (uint16_t)q.s;
+                const float sc = Gl < NG ? (float)__builtin_bit_cast(_Float16, sh) : 0.0f;
+                float f[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    f[i] = sc * c[i];
+                    f[i] += __shfl_xor(f[i], 16, 64);
+                    f[i] += __shfl_xor(f[i], 32, 64);
+                }
+                if (qq == 0) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) red[(wave * 4 + i) * 16 + qn] = f[i];
+                }
+            }
+            __syncthreads();
+            // token i, column n: the 8 gate waves' and the 8 up waves' partials
+            if (tid < 64) {
+                const int i = tid >> 4, n = tid & 15;
+                float gs = 0.0f, us = 0.0f;
+#pragma unroll
+                for (int w = 0; w < 8; ++w) {
+                    if (w < NQ) {
+                        gs += red[(w * 4 + i) * 16 + n];
+                        us += red[((8 + w) * 4 + i) * 16 + n];
+                    }
+                }
+                const int rows = q.rr & 63, row0 = q.rr >> 6;
+                if (i < rows) a.act[(size_t)(row0 + i) * I + nt * 16 + n] = f32_to_f16_bits(silu_mul(gs, us));
+            }
+            if (NRED == 1) __syncthreads();
+            return;
+        }
         if (active) {
             const bool act = (m >> 4) == g && mm < (q.rr & 63) && Gl < NG;
             const int xr = act ? q.pr / k : T;                 // LDS row of the token (T: zeros)
@@ -216,19 +297,25 @@ hipError_t launch_q3dec_gate_up(const FfnArgs& fa, int cus, hipStream_t s) {
     {
         std::lock_guard<std::mutex> lock(g_qd_mu);
         if (!g_qd_ready[dev]) {
-            err = hipFuncSetAttribute((const void*)ffn_q3_decode_kernel<1>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                      160 * 1024);
-            if (err == hipSuccess)
-                err = hipFuncSetAttribute((const void*)ffn_q3_decode_kernel<2>,
-                                          hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+            const void* kern[4] = {(const void*)ffn_q3_decode_kernel<1, false>, (const void*)ffn_q3_decode_kernel<2, false>,
+                                   (const void*)ffn_q3_decode_kernel<1, true>, (const void*)ffn_q3_decode_kernel<2, true>};
+            for (int i = 0; i < 4 && err == hipSuccess; ++i)
+                err = hipFuncSetAttribute(kern[i], hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
             if (err != hipSuccess) return err;
             g_qd_ready[dev] = true;
         }
     }
-    if (qd_lds_bytes(fa.T, fa.H, fa.E, fa.k, 2) <= 160u * 1024u)
-        ffn_q3_decode_kernel<2><<<cus, QD_THREADS, qd_lds_bytes(fa.T, fa.H, fa.E, fa.k, 2), s>>>(fa);
-    else
-        ffn_q3_decode_kernel<1><<<cus, QD_THREADS, qd_lds_bytes(fa.T, fa.H, fa.E, fa.k, 1), s>>>(fa);
+    // at most 4 tokens (so every tile at most 4 rows): the 16x16x32 form
+    const bool quad = fa.T <= 4;
+    const bool two = qd_lds_bytes(fa.T, fa.H, fa.E, fa.k, 2) <= 160u * 1024u;
+    const uint32_t lds = qd_lds_bytes(fa.T, fa.H, fa.E, fa.k, two ? 2 : 1);
+    if (quad) {
+        if (two) ffn_q3_decode_kernel<2, true><<<cus, QD_THREADS, lds, s>>>(fa);
+        else ffn_q3_decode_kernel<1, true><<<cus, QD_THREADS, lds, s>>>(fa);
+    } else {
+        if (two) ffn_q3_decode_kernel<2, false><<<cus, QD_THREADS, lds, s>>>(fa);
+        else ffn_q3_decode_kernel<1, false><<<cus, QD_THREADS, lds, s>>>(fa);
+    }
     return hipGetLastError();
 }
 
