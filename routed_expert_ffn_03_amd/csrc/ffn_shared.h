@@ -235,6 +235,37 @@ __device__ __forceinline__ void q3_prep_group(const uint16_t* src16, uint16_t* d
     *sum_dst = (uint32_t)__builtin_bit_cast(uint16_t, hi) | ((uint32_t)__builtin_bit_cast(uint16_t, lo) << 16);
 }
 
+// Part `part` of `parts` (a power of two up to 16) of q3_prep_group for a
+// bf16 row already in LDS: the slot chunks 16 part / parts .. of one group,
+// and the fp64 sum of those chunks' fields, returned for the caller to add
+// across the parts (exact, so in any order, while a group's magnitudes span
+// less than about 2^38; beyond that the order of the partial sums decides
+// the rounding of the group sum).
+__device__ __forceinline__ double q3_prep_part_lds(const uint16_t* src16, uint16_t* dst16, int part, int parts) {
+    u32x4* dst = reinterpret_cast<u32x4*>(dst16);
+    const int per = 16 / parts, i0 = part * per;
+    double sum = 0.0;
+    for (int i = i0; i < i0 + per; ++i) {
+        u32x4 o;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int d = 4 * i + j;
+            const uint32_t lo = src16[pair_field(2 * d)], hi = src16[pair_field(2 * d + 1)];
+            sum += (double)__uint_as_float(lo << 16) + (double)__uint_as_float(hi << 16);
+            o[j] = lo | (hi << 16);
+        }
+        dst[i] = o;
+    }
+    return sum;
+}
+
+// A bf16 group sum as the (hi, lo) pair of q3_prep_group
+__device__ __forceinline__ uint32_t q3_sum_pair_bf16(double sum) {
+    const __bf16 h = (__bf16)(float)sum;
+    const __bf16 l = (__bf16)(float)(sum - (double)(float)h);
+    return (uint32_t)__builtin_bit_cast(uint16_t, h) | ((uint32_t)__builtin_bit_cast(uint16_t, l) << 16);
+}
+
 // The same for an fp16 row (the activations of the down phase): the slots
 // for the fp16 products with the codes as the exact fp16 numbers 1024 + u
 // (bits 0x6400 | u), and the group sum as an fp16 hi, lo pair.  Each field

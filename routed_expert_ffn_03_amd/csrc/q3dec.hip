@@ -81,10 +81,32 @@ void ffn_q3_decode_kernel(FfnArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int m = lane & 31, g = lane >> 5, mm = m & 15;
 
-    // 1. x rows in pair-slot order and group sums; row T all zeros
-    for (int task = tid; task < T * NG; task += QD_THREADS) {
-        const int tok = task / NG, G = task - tok * NG;
-        q3_prep_group(a.x + (size_t)tok * H + G * 128, xl + (size_t)tok * H + G * 128, xsl + tok * NG + G);
+    // 1. x rows in pair-slot order and group sums; row T all zeros.  QUAD:
+    //    the rows first go as they are into the first reduction buffer
+    //    (unused until the first item; T <= 4 and H <= 16 x 256 bound them
+    //    to its 32 KB), in whole 16-byte pieces, and
+    //    are reordered from there by eight threads per token and group (two
+    //    of its 16 slot chunks each; their partial sums meet by xor shuffles
+    //    in a fixed order)
+    if constexpr (QUAD) {
+        uint16_t* xraw = reinterpret_cast<uint16_t*>(red0);
+        for (int i = tid; i < T * H / 8; i += QD_THREADS)
+            reinterpret_cast<u32x4*>(xraw)[i] = ldg16(a.x + 8 * (size_t)i);
+        __syncthreads();
+        for (int u = tid; u < T * NG * 8; u += QD_THREADS) {
+            const int task = u >> 3, part = u & 7;
+            const int tok = task / NG, G = task - tok * NG;
+            double sum = q3_prep_part_lds(xraw + (size_t)tok * H + G * 128, xl + (size_t)tok * H + G * 128, part, 8);
+            sum += __shfl_xor(sum, 1, 64);
+            sum += __shfl_xor(sum, 2, 64);
+            sum += __shfl_xor(sum, 4, 64);
+            if (part == 0) xsl[tok * NG + G] = q3_sum_pair_bf16(sum);
+        }
+    } else {
+        for (int task = tid; task < T * NG; task += QD_THREADS) {
+            const int tok = task / NG, G = task - tok * NG;
+            q3_prep_group(a.x + (size_t)tok * H + G * 128, xl + (size_t)tok * H + G * 128, xsl + tok * NG + G);
+        }
     }
     for (int i = tid; i < H / 8; i += QD_THREADS) reinterpret_cast<u32x4*>(xl + (size_t)T * H)[i] = u32x4{0, 0, 0, 0};
     const int n_mt = a.hdr->n_thin, NT = I / 16;
