@@ -897,6 +897,42 @@ __device__ __forceinline__ void thin_q3_pairs_down(const FfnArgs& a, const MTile
     thin_reduce_store<2>(a, acc, t, nt, red, wave, lane);
 }
 
+// One lane's 13 packed words of a 52-byte group: three 16-byte loads and one
+// 4-byte load (groups are 4-byte aligned)
+__device__ __forceinline__ void load_q3_group(const uint32_t* gw, uint32_t (&w)[Q3_WORDS]) {
+    const u32x4a4 q0 = *reinterpret_cast<const u32x4a4*>(gw);
+    const u32x4a4 q1 = *reinterpret_cast<const u32x4a4*>(gw + 4);
+    const u32x4a4 q2 = *reinterpret_cast<const u32x4a4*>(gw + 8);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        w[i] = q0[i];
+        w[4 + i] = q1[i];
+        w[8 + i] = q2[i];
+    }
+    w[12] = gw[12];
+}
+
+// What one lane of thin_q3_quads_down reads of expert e's W_down for one quad
+// p of groups: rows nt*32 + n and nt*32 + 16 + n (n = L % 16), group 4 p + q
+// (q = L / 16; past the last group, the last group, which the item scales by 0)
+struct QuadW {
+    uint32_t w0[Q3_WORDS], w1[Q3_WORDS];
+    uint16_t s0, s1;
+};
+
+__device__ __forceinline__ void quad_load(const FfnArgs& a, int e, int nt, int p, int lane, QuadW& o) {
+    const int n = lane & 15, q = lane >> 4;
+    const int NG = a.I >> 7;
+    const int Gc = min(4 * p + q, NG - 1);
+    const size_t row0 = (size_t)e * a.H + nt * 32 + n;
+    const uint32_t* wr0 = reinterpret_cast<const uint32_t*>(a.wd) + (row0 * NG + Gc) * Q3_WORDS;
+    load_q3_group(wr0, o.w0);
+    load_q3_group(wr0 + (size_t)16 * NG * Q3_WORDS, o.w1);
+    const uint16_t* sr0 = a.sd + row0 * NG + Gc;
+    o.s0 = sr0[0];
+    o.s1 = sr0[(size_t)16 * NG];
+}
+
 // The same item for a tile of at most 4 rows on 16x16x32 products: lane
 // quarter q (L / 16) holds group 4 p + q of its weight row in k-quarter q,
 // and the activation lanes of row 4 q + i hold token i of that group there,
@@ -904,44 +940,25 @@ __device__ __forceinline__ void thin_q3_pairs_down(const FfnArgs& a, const MTile
 // MFMA work of the 32-row tiles per weight).  Each group's scale is applied
 // on its own result rows; the four groups of a token are then summed across
 // the lane quarters.  Columns: W_down rows nt*32 + n and nt*32 + 16 + n.
+// The wave's first quad comes in `pf`, loaded ahead by the caller; once the
+// item's products are issued, `pf` is loaded with the first quad of the next
+// item (expert next_e, column tile next_nt; none if next_e < 0), so those
+// loads are in flight over this item's reduction.
 __device__ __forceinline__ void thin_q3_quads_down(const FfnArgs& a, const MTile& t, int nt, const uint16_t* xl,
                                                    const uint32_t* xsl, float (&red)[4][16][64], int wave,
-                                                   int lane) {
+                                                   int lane, QuadW& pf, int next_e, int next_nt) {
     constexpr int XR = 4;
     const int n = lane & 15, q = lane >> 4;
     const int K = a.I, NG = K >> 7, NQ = (NG + 3) >> 2;
-    const size_t mat_words = (size_t)a.H * NG * Q3_WORDS;
     const bool act_lane = (n >> 2) == q && (n & 3) < t.rows;    // A row n = 4 q + token
     const int xr = act_lane ? (n & 3) : XR;
-    const uint32_t* wr0 = reinterpret_cast<const uint32_t*>(a.wd) + (size_t)t.e * mat_words +
-                          (size_t)(nt * 32 + n) * NG * Q3_WORDS;
-    const uint32_t* wr1 = wr0 + (size_t)16 * NG * Q3_WORDS;
-    const uint16_t* sr0 = a.sd + ((size_t)t.e * a.H + nt * 32 + n) * NG;
-    const uint16_t* sr1 = sr0 + (size_t)16 * NG;
     uint32_t magic;
     asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(magic));
 
-    auto load13 = [&](const uint32_t* gw, uint32_t (&w)[Q3_WORDS]) {
-        const u32x4a4 q0 = *reinterpret_cast<const u32x4a4*>(gw);
-        const u32x4a4 q1 = *reinterpret_cast<const u32x4a4*>(gw + 4);
-        const u32x4a4 q2 = *reinterpret_cast<const u32x4a4*>(gw + 8);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            w[i] = q0[i];
-            w[4 + i] = q1[i];
-            w[8 + i] = q2[i];
-        }
-        w[12] = gw[12];
-    };
-
     float f0[4] = {}, f1[4] = {};
-    for (int p = wave; p < NQ; p += 4) {
+    auto run = [&](const QuadW& w, int p) {
         const int G = 4 * p + q;
-        const int Gc = min(G, NG - 1);            // past the groups: a real one, scaled by 0 below
-        uint32_t w0[Q3_WORDS], w1[Q3_WORDS];
-        load13(wr0 + Gc * Q3_WORDS, w0);
-        load13(wr1 + Gc * Q3_WORDS, w1);
-        const uint16_t s0h = sr0[Gc], s1h = sr1[Gc];
+        const int Gc = min(G, NG - 1);
         const u32x4* xa = reinterpret_cast<const u32x4*>(xl + (size_t)(G < NG ? xr : XR) * K) + 16 * Gc;
         const uint32_t xsum = G < NG ? xsl[xr * NG + G] : 0u;     // (row XR: zeros)
         f32x4 c0 = f32x4{}, c1 = f32x4{};
@@ -950,8 +967,8 @@ __device__ __forceinline__ void thin_q3_quads_down(const FfnArgs& a, const MTile
             u32x4 b0, b1;
             static_for<4>([&](auto q_c) {
                 constexpr int Q = decltype(q_c)::value;
-                b0[Q] = magic_pair<4 * J + Q>(w0, magic);
-                b1[Q] = magic_pair<4 * J + Q>(w1, magic);
+                b0[Q] = magic_pair<4 * J + Q>(w.w0, magic);
+                b1[Q] = magic_pair<4 * J + Q>(w.w1, magic);
             });
             const u32x4 av = xa[J];
             c0 = mfma16_f16(av, b0, c0);
@@ -962,16 +979,28 @@ __device__ __forceinline__ void thin_q3_quads_down(const FfnArgs& a, const MTile
         c0 = mfma16_f16(sa, sb, c0);
         c1 = mfma16_f16(sa, sb, c1);
         // this lane's result rows 4 q + i: token i of group 4 p + q
-        const float s0 = G < NG ? (float)__builtin_bit_cast(_Float16, s0h) : 0.0f;
-        const float s1 = G < NG ? (float)__builtin_bit_cast(_Float16, s1h) : 0.0f;
+        const float s0 = G < NG ? (float)__builtin_bit_cast(_Float16, w.s0) : 0.0f;
+        const float s1 = G < NG ? (float)__builtin_bit_cast(_Float16, w.s1) : 0.0f;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             f0[i] = fmaf(s0, c0[i], f0[i]);
             f1[i] = fmaf(s1, c1[i], f1[i]);
         }
+    };
+    if (wave < NQ) run(pf, wave);
+    for (int p = wave + 4; p < NQ; p += 4) {
+        QuadW w;
+        quad_load(a, t.e, nt, p, lane, w);
+        run(w, p);
     }
-    // sum the four groups of each token across the lane quarters, then the
-    // thin kernels' accumulator layout: lane L < 32 column L, rows 0..3
+    // (not above the products: the next quad's words would need registers
+    // of their own while this one's are still read)
+    __builtin_amdgcn_sched_barrier(0);
+    if (next_e >= 0 && wave < NQ) quad_load(a, next_e, next_nt, wave, lane, pf);
+    // sum the four groups of each token across the lane quarters; lane L < 32
+    // then holds column L (W_down row nt*32 + L) of the tile's rows 0..3, and
+    // the four waves' 4 x 32 partials meet in LDS (the barriers wait for LDS
+    // traffic only: the loads issued above stay in flight); wave 0 stores
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         f0[i] += __shfl_xor(f0[i], 16, 64);
@@ -979,10 +1008,19 @@ __device__ __forceinline__ void thin_q3_quads_down(const FfnArgs& a, const MTile
         f1[i] += __shfl_xor(f1[i], 16, 64);
         f1[i] += __shfl_xor(f1[i], 32, 64);
     }
-    f32x16 acc = f32x16{};
+    if (lane < 32) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) acc[i] = lane < 16 ? f0[i] : (lane < 32 ? f1[i] : 0.0f);
-    thin_reduce_store<2>(a, acc, t, nt, red, wave, lane);
+        for (int i = 0; i < 4; ++i) red[wave][i][lane] = lane < 16 ? f0[i] : f1[i];
+    }
+    lds_barrier();
+    if (wave == 0 && lane < 32) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float v = red[0][i][lane] + red[1][i][lane] + red[2][i][lane] + red[3][i][lane];
+            if (i < t.rows) a.y[(size_t)(t.row0 + i) * a.H + nt * 32 + lane] = f32_to_f16_bits(v);
+        }
+    }
+    lds_barrier();
 }
 
 // 3-bit thin kernel: the same items, waves and reduction as the bf16 thin
@@ -1036,6 +1074,7 @@ void ffn_thin_q3_kernel(FfnArgs a) {
     const int i_end = XR > 0 ? min(n_items, i_first + chunk) : n_items;
     const int i_step = XR > 0 ? 1 : (int)gridDim.x;
     int staged = -1;                                 // XR > 0: the tile whose rows are in LDS
+    [[maybe_unused]] QuadW pf;                       // XR == 4: the wave's first quad of its current item
     for (int item = i_first; item < i_end; item += i_step) {
         const int nt = XR > 0 ? item % NT : item / n_mt;
         const int mt = XR > 0 ? item / NT : item % n_mt;
@@ -1060,9 +1099,19 @@ void ffn_thin_q3_kernel(FfnArgs a) {
                 }
                 __syncthreads();
                 staged = mt;
+                // a tile's first item loads its own weights (for every wave: a
+                // wave past the last quad reads the last group; this keeps the
+                // words of an earlier item dead over the staging)
+                if constexpr (XR == 4) quad_load(a, t.e, nt, wave, lane, pf);
             }
-            if constexpr (XR == 4) thin_q3_quads_down(a, t, nt, xl, xsl, red, wave, lane);
-            else thin_q3_pairs_down<XR>(a, t, nt, xl, xsl, red, wave, lane);
+            if constexpr (XR == 4) {
+                // the next item's words are loaded ahead only within the tile
+                const int nx = item + 1;
+                const bool ahead = nx < i_end && nx / NT == mt;
+                thin_q3_quads_down(a, t, nt, xl, xsl, red, wave, lane, pf, ahead ? t.e : -1, nx % NT);
+            } else {
+                thin_q3_pairs_down<XR>(a, t, nt, xl, xsl, red, wave, lane);
+            }
             continue;
         }
         if constexpr (PHASE == 1) {

@@ -10,6 +10,9 @@ cross-compiles, nothing runs on a GPU).
 3. The streaming kernel's chunk loop never waits for all of its loads
    (``s_waitcnt vmcnt(0)``): the next chunk's weights stay in flight while
    the current one is multiplied, across items too.
+4. The 3-bit down kernels of decode batches (activation rows in LDS, four
+   blocks per CU under a 128-register bound) spill nothing anywhere: a
+   spilled register is a memory round trip in every item.
 
 The checker itself is pinned on hand-written snippets with and without such
 a hazard.
@@ -146,6 +149,15 @@ def test_fat_k_loops_do_not_spill(ffn_asm):
             spills = [x.strip() for x in body if "scratch_" in x]
             assert not spills, (name, lab, spills[:3])
     assert checked > 0
+
+
+def test_decode_down_kernels_do_not_spill(ffn_asm):
+    kernels = {k: v for k, v in kernel_bodies(ffn_asm).items()
+               if re.search(r"ffn_thin_q3_kernelILi2ELi(4|8|16)E", k)}
+    assert len(kernels) == 3, sorted(kernels)
+    for name, lines in kernels.items():
+        spills = [x.strip() for x in lines if "scratch_" in x]
+        assert not spills, (name, spills[:3])
 
 
 def _loop_blocks(lines):
