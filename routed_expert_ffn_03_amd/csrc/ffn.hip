@@ -823,53 +823,65 @@ __device__ __forceinline__ void thin_q3_pairs(const FfnArgs& a, const MTile& t, 
     thin_reduce_store<1>(a, acc, t, nt, red, wave, lane);
 }
 
+// One lane's 13 packed words of a 52-byte group: three 16-byte loads and one
+// 4-byte load (groups are 4-byte aligned)
+__device__ __forceinline__ void load_q3_group(const uint32_t* gw, uint32_t (&w)[Q3_WORDS]) {
+    const u32x4a4 q0 = *reinterpret_cast<const u32x4a4*>(gw);
+    const u32x4a4 q1 = *reinterpret_cast<const u32x4a4*>(gw + 4);
+    const u32x4a4 q2 = *reinterpret_cast<const u32x4a4*>(gw + 8);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        w[i] = q0[i];
+        w[4 + i] = q1[i];
+        w[8 + i] = q2[i];
+    }
+    w[12] = gw[12];
+}
+
+// What one lane of thin_q3_pairs_down reads of expert e's W_down for one
+// group pair p: row nt*32 + L % 32, group 2 p + L / 32 and the pair's two
+// scales (indexes clamped to the row's last group: a pair past the end loads
+// real words, which the item does not use or scales by 0)
+struct PairW {
+    uint32_t w[Q3_WORDS];
+    uint16_t s0, s1;
+};
+
+__device__ __forceinline__ void pair_load(const FfnArgs& a, int e, int nt, int p, int lane, PairW& o) {
+    const int m = lane & 31, g = lane >> 5;
+    const int NG = a.I >> 7;
+    const size_t row = (size_t)e * a.H + nt * 32 + m;
+    load_q3_group(reinterpret_cast<const uint32_t*>(a.wd) + (row * NG + min(2 * p + g, NG - 1)) * Q3_WORDS, o.w);
+    const uint16_t* srow = a.sd + row * NG;
+    o.s0 = srow[min(2 * p, NG - 1)];
+    o.s1 = srow[min(2 * p + 1, NG - 1)];
+}
+
 // One down item of a decode batch (a tile of at most 16 rows) on pair-slot
 // operands, as thin_q3_pairs: the tile's activation rows are in LDS in slot
 // order (xl: XR + 1 rows of K halves, the last all zeros; xsl: their group
 // sums, an fp16 hi, lo pair per row and group), the codes enter the fp16
 // products as 1024 + u and each pair ends with the -1028 x group-sum step.
-// The 32 output columns are the W_down rows nt*32 + n.
+// The 32 output columns are the W_down rows nt*32 + n.  The wave's first
+// pair comes in `pf`, loaded ahead by the caller; with the item's last
+// products issued, `pf` is loaded with the first pair of the next item
+// (expert next_e, column tile next_nt; none if next_e < 0), in flight over
+// this item's reduction.
 template <int XR>
 __device__ __forceinline__ void thin_q3_pairs_down(const FfnArgs& a, const MTile& t, int nt, const uint16_t* xl,
                                                    const uint32_t* xsl, float (&red)[4][16][64], int wave,
-                                                   int lane) {
+                                                   int lane, PairW& pf, int next_e, int next_nt) {
     const int m = lane & 31, g = lane >> 5, mm = m & 15;
     const int K = a.I, NG = K >> 7, NP = (NG + 1) >> 1;
-    const size_t mat_words = (size_t)a.H * NG * Q3_WORDS;
     const bool act_lane = (m >> 4) == g && mm < t.rows;
     const int xr = act_lane ? mm : XR;                  // LDS row of this lane's activations
-    const int row = nt * 32 + m;
-    const uint32_t* wrow = reinterpret_cast<const uint32_t*>(a.wd) + (size_t)t.e * mat_words + (size_t)row * NG * Q3_WORDS;
-    const uint16_t* srow = a.sd + ((size_t)t.e * a.H + row) * NG;
     uint32_t magic;
     asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(magic));
 
-    struct Pair {
-        uint32_t w[Q3_WORDS];
-        uint16_t s0, s1;
-    };
-    auto load_pair = [&](int p, Pair& q) {
-        const int G = min(2 * p + g, NG - 1);     // past an odd count: a real group whose sums are zero
-        const uint32_t* gw = wrow + G * Q3_WORDS;
-        const u32x4a4 q0 = *reinterpret_cast<const u32x4a4*>(gw);
-        const u32x4a4 q1 = *reinterpret_cast<const u32x4a4*>(gw + 4);
-        const u32x4a4 q2 = *reinterpret_cast<const u32x4a4*>(gw + 8);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            q.w[i] = q0[i];
-            q.w[4 + i] = q1[i];
-            q.w[8 + i] = q2[i];
-        }
-        q.w[12] = gw[12];
-        q.s0 = srow[2 * p];
-        q.s1 = srow[min(2 * p + 1, NG - 1)];
-    };
-
     float fin[8] = {};
-    Pair cur, nxt;
-    if (wave < NP) load_pair(wave, cur);
+    PairW cur = pf, nxt;
     for (int p = wave; p < NP; p += 4) {
-        if (p + 4 < NP) load_pair(p + 4, nxt);   // next pair's words in flight during this one
+        if (p + 4 < NP) pair_load(a, t.e, nt, p + 4, lane, nxt);   // next pair's words in flight during this one
         const int G = 2 * p + g;
         const u32x4* xa = reinterpret_cast<const u32x4*>(xl + (size_t)(G < NG ? xr : XR) * K) + 16 * min(G, NG - 1);
         const uint32_t xsum = G < NG ? xsl[xr * NG + G] : 0u;     // (row XR: zeros)
@@ -891,25 +903,25 @@ __device__ __forceinline__ void thin_q3_pairs_down(const FfnArgs& a, const MTile
         for (int r = 0; r < 8; ++r) fin[r] = fmaf(s1, c[r + 8], fmaf(s0, c[r], fin[r]));
         cur = nxt;
     }
-    f32x16 acc = f32x16{};
+    // (not above the products: the next pair's words would need registers of
+    // their own while this one's are still read)
+    __builtin_amdgcn_sched_barrier(0);
+    if (next_e >= 0 && wave < NP) pair_load(a, next_e, next_nt, wave, lane, pf);
+    // the four waves' partials meet in LDS: lane (m, g) holds column m of
+    // rows 4 g + r and 8 + 4 g + r (r < 4); the barriers wait for LDS traffic
+    // only, so the loads issued above stay in flight; wave 0 stores
 #pragma unroll
-    for (int r = 0; r < 8; ++r) acc[r] = fin[r];
-    thin_reduce_store<2>(a, acc, t, nt, red, wave, lane);
-}
-
-// One lane's 13 packed words of a 52-byte group: three 16-byte loads and one
-// 4-byte load (groups are 4-byte aligned)
-__device__ __forceinline__ void load_q3_group(const uint32_t* gw, uint32_t (&w)[Q3_WORDS]) {
-    const u32x4a4 q0 = *reinterpret_cast<const u32x4a4*>(gw);
-    const u32x4a4 q1 = *reinterpret_cast<const u32x4a4*>(gw + 4);
-    const u32x4a4 q2 = *reinterpret_cast<const u32x4a4*>(gw + 8);
+    for (int r = 0; r < 8; ++r) red[wave][r][lane] = fin[r];
+    lds_barrier();
+    if (wave == 0) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        w[i] = q0[i];
-        w[4 + i] = q1[i];
-        w[8 + i] = q2[i];
+        for (int r = 0; r < 8; ++r) {
+            const float v = red[0][r][lane] + red[1][r][lane] + red[2][r][lane] + red[3][r][lane];
+            const int row = 8 * (r >> 2) + 4 * g + (r & 3);
+            if (row < t.rows) a.y[(size_t)(t.row0 + row) * a.H + nt * 32 + m] = f32_to_f16_bits(v);
+        }
     }
-    w[12] = gw[12];
+    lds_barrier();
 }
 
 // What one lane of thin_q3_quads_down reads of expert e's W_down for one quad
@@ -1075,6 +1087,7 @@ void ffn_thin_q3_kernel(FfnArgs a) {
     const int i_step = XR > 0 ? 1 : (int)gridDim.x;
     int staged = -1;                                 // XR > 0: the tile whose rows are in LDS
     [[maybe_unused]] QuadW pf;                       // XR == 4: the wave's first quad of its current item
+    [[maybe_unused]] PairW pp;                       // other XR > 0: its first group pair
     for (int item = i_first; item < i_end; item += i_step) {
         const int nt = XR > 0 ? item % NT : item / n_mt;
         const int mt = XR > 0 ? item / NT : item % n_mt;
@@ -1100,9 +1113,10 @@ void ffn_thin_q3_kernel(FfnArgs a) {
                 __syncthreads();
                 staged = mt;
                 // a tile's first item loads its own weights (for every wave: a
-                // wave past the last quad reads the last group; this keeps the
+                // wave past the last quad or pair reads the last group; this keeps the
                 // words of an earlier item dead over the staging)
                 if constexpr (XR == 4) quad_load(a, t.e, nt, wave, lane, pf);
+                else pair_load(a, t.e, nt, wave, lane, pp);
             }
             if constexpr (XR == 4) {
                 // the next item's words are loaded ahead only within the tile
@@ -1110,7 +1124,9 @@ void ffn_thin_q3_kernel(FfnArgs a) {
                 const bool ahead = nx < i_end && nx / NT == mt;
                 thin_q3_quads_down(a, t, nt, xl, xsl, red, wave, lane, pf, ahead ? t.e : -1, nx % NT);
             } else {
-                thin_q3_pairs_down<XR>(a, t, nt, xl, xsl, red, wave, lane);
+                const int nx = item + 1;
+                const bool ahead = nx < i_end && nx / NT == mt;
+                thin_q3_pairs_down<XR>(a, t, nt, xl, xsl, red, wave, lane, pp, ahead ? t.e : -1, nx % NT);
             }
             continue;
         }
