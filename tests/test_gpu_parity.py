@@ -296,9 +296,11 @@ def test_route_permute_plan(T, E, k, wfmt):
 
 # The 3-bit gate/up kernel for decode batches keeps every token's x row in
 # LDS (up to 14 tokens at hidden 4096); larger batches take the streaming
-# kernel.  Both sides of that limit, every output compared.
+# kernel.  Both sides of that limit, and of the down kernel's row bounds
+# (4, 8 and 16 activation rows in LDS: 5, 8 and 16 tokens), every output
+# compared.
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("T", [1, 2, 7, 14, 15])
+@pytest.mark.parametrize("T", [1, 2, 5, 7, 8, 14, 15, 16])
 def test_decode_q3_batch_sizes(T):
     base = SHAPES["decode_q3"]
     shape = LayerShape(f"decode_q3_T{T}", T, base.H, base.I, base.E, base.k, base.router, base.wfmt)
