@@ -306,3 +306,14 @@ def test_decode_q3_batch_sizes(T):
     shape = LayerShape(f"decode_q3_T{T}", T, base.H, base.I, base.E, base.k, base.router, base.wfmt)
     say(f"[full layer] {shape.name} T={T} wfmt=q3")
     full_layer_case(shape, 0, T)
+
+
+# The same decode kernels at an odd number of 128-groups per row (I = 384:
+# three groups, so the down items' second group pair and last quad run past
+# the row's end, and three of the four waves own no quad), every output
+# compared.
+@pytest.mark.parametrize("T", [3, 6, 12])
+def test_decode_q3_odd_groups(T):
+    shape = LayerShape(f"decode_q3_odd_T{T}", T, 512, 384, 64, 8, "zipf", "q3")
+    say(f"[full layer] {shape.name} T={T} wfmt=q3")
+    full_layer_case(shape, 0, T)
